@@ -1,0 +1,147 @@
+// Device helpers shared by the kvq kernels (gfx950 only).
+//
+// e4m3 here is the OCP "e4m3fn" format the pages store the cache in: sign, 4
+// exponent bits (bias 7), 3 mantissa bits, max 448, NaN 0x7F/0xFF, no infinity.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kPage = 16;
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// float32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Round-to-nearest-even, saturating float32 -> e4m3 encoder on the bit pattern.
+// NaN -> 0x7F | sign; |x| >= 448 (and inf) -> 0x7E | sign; sign of zero kept.
+// (Also built for the host so the bit logic can be checked exhaustively on a CPU.)
+__host__ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a > 0x7F800000u) {
+    code = 0x7Fu;
+  } else if (a >= 0x43E00000u) {          // 448.0f
+    code = 0x7Eu;
+  } else if (a >= 0x3C800000u) {          // 2^-6: normal e4m3 range
+    // keep 3 of 23 fraction bits, ties to even, carry may bump the exponent;
+    // e4m3 exponent = float32 exponent - 120
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  } else {                                // subnormal grid n * 2^-9, n = 0..8
+    const uint32_t e = a >> 23;
+    const uint32_t mf = (a & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+    const int sh = 141 - (int)(e ? e : 1u);   // value * 2^9 = mf * 2^-sh
+    if (sh >= 25) {
+      code = 0u;
+    } else {
+      const uint32_t q = mf >> sh;
+      const uint32_t rem = mf & ((1u << sh) - 1u);
+      const uint32_t half = 1u << (sh - 1);
+      code = q + ((rem > half) || (rem == half && (q & 1u)) ? 1u : 0u);
+    }
+  }
+  return code | sign;
+}
+
+// Code of x at scale s: encode(fl32(x / s)) with IEEE division; a NaN quotient
+// takes the sign of x (the sign of a NaN produced by division is not fixed).
+__host__ __device__ __forceinline__ uint32_t e4m3_quantize(float x, float s) {
+  const float q = x / s;
+  if (q != q) return 0x7Fu | ((__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u);
+  return e4m3_encode(q);
+}
+
+// |x| maximum that propagates NaN (integer max of the magnitude bit patterns).
+__device__ __forceinline__ uint32_t abs_bits(float x) {
+  return __float_as_uint(x) & 0x7FFFFFFFu;
+}
+
+// Per-token-head scale from the magnitude bits of the row maximum.
+__device__ __forceinline__ float scale_from_amax_bits(uint32_t amax_bits) {
+  if (amax_bits == 0u) return 1.0f;
+  return __uint_as_float(amax_bits) / 448.0f;
+}
+
+// Two e4m3 codes (bytes 0,1 or 2,3 of w) -> two exact bf16 values.
+template <bool kHigh>
+__device__ __forceinline__ bf16x2_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh);
+}
+
+// Two e4m3 codes (bytes 0,1 or 2,3 of w) -> two exact float32 values.
+template <bool kHigh>
+__device__ __forceinline__ float2_t e4m3x2_to_f32x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHigh);
+}
+
+__device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(bf16x2_t, w);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return float_to_bf16_bits(lo) | (float_to_bf16_bits(hi) << 16);
+}
+
+// ---- cross-lane moves inside a 16-lane row (DPP) --------------------------------
+// dpp_ctrl values of the gfx9 encoding.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside 8 (i ^ 7)
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside 16 (i ^ 15)
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF,
+                                                    0xF, false));
+}
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_mov_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, false);
+}
+
+// Partner masks for lane bits 0..3 inside a row: bit b uses xor kXorOfBit[b].
+// The pairing for bit b may also flip lower bits; the butterfly below only relies
+// on it flipping bit b and leaving higher bits alone.
+template <int kBit>
+__device__ __forceinline__ float dpp_partner(float x) {
+  if constexpr (kBit == 0) return dpp_mov<kDppXor1>(x);
+  else if constexpr (kBit == 1) return dpp_mov<kDppXor2>(x);
+  else if constexpr (kBit == 2) return dpp_mov<kDppHalfMirror>(x);
+  else return dpp_mov<kDppMirror>(x);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+}  // namespace kvq

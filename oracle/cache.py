@@ -52,7 +52,12 @@ def quantize(x, scale) -> np.ndarray:
     s = np.asarray(scale, dtype=np.float32)
     with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
         qt = (x / s).astype(np.float32)
-    codes = e4m3.encode(qt)
+    flat = qt.reshape(-1)
+    codes = np.empty(flat.shape, np.uint8)
+    step = 1 << 16   # cache-sized temporaries; the arithmetic is elementwise
+    for i in range(0, flat.size, step):
+        codes[i:i + step] = e4m3.encode(flat[i:i + step])
+    codes = codes.reshape(qt.shape)
     nan_q = np.isnan(qt)
     nan_code = np.where(np.signbit(x), 0xFF, 0x7F).astype(np.uint8)
     return np.where(nan_q, nan_code, codes).astype(np.uint8)

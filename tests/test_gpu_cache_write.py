@@ -1,0 +1,154 @@
+"""GPU parity: e4m3 quantiser and quantising cache write, bit-exact to the oracle."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import cache as ocache
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp8_quantized_paged_amd as k
+    return k
+
+
+from gpu_common import dev, dev_bf16, log, oracle_pools, read_pools, write_cache  # noqa: E402
+
+
+def all_bf16():
+    return (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.5, 0.0123, 3.0 / 448.0, 7.5, 1e-3, 448.0])
+def test_quantize_exhaustive_bf16(kvq, scale):
+    x = all_bf16()
+    log(f"quantize exhaustive scale={scale}")
+    got = kvq.quantize_fp8(dev_bf16(x), scale).cpu().numpy()
+    want = ocache.quantize(x, np.float32(scale))
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(hex(int(i) << 16), hex(got[i]), hex(want[i])) for i in bad[:8]]
+
+
+def test_quantize_ragged_tail(kvq):
+    rng = np.random.default_rng(3)
+    for n in (1, 7, 9, 1000, 4097):
+        x = workloads.bf16_round(rng.standard_normal(n).astype(np.float32) * 30)
+        got = kvq.quantize_fp8(dev_bf16(x), 0.25).cpu().numpy()
+        assert np.array_equal(got, ocache.quantize(x, np.float32(0.25))), n
+
+
+def _check_pools(got, want, rows_slots):
+    page, off = rows_slots // 16, rows_slots % 16
+    for name in ("k_codes", "v_codes"):
+        g, w = got[name][page, :, off], want[name][page, :, off]
+        assert np.array_equal(g, w), (name, int((g != w).sum()))
+    if "k_scales" in got:
+        for name in ("k_scales", "v_scales"):
+            g, w = got[name][page, :, off], want[name][page, :, off]
+            assert np.array_equal(g.view(np.uint32), w.view(np.uint32)), name
+
+
+@pytest.mark.parametrize("mode", ["per_tensor", "per_token_head"])
+def test_cache_write_tiny_decode(kvq, mode):
+    case = workloads.tiny_decode()
+    log(f"cache_write tiny {mode}")
+    c = write_cache(kvq, case, "fp8", mode)
+    _check_pools(read_pools(c), oracle_pools(case, mode), case.slots)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_cache_write_ragged_perm(kvq, D):
+    case = workloads.make_decode_case(21 + D, [1, 17, 0, 40, 16], 8, 4, D, table="perm",
+                                      outliers=4, extra_pages=5)
+    for mode, ks, vs in (("per_token_head", 1.0, 1.0), ("per_tensor", 0.37, 2.5)):
+        log(f"cache_write ragged D={D} {mode}")
+        c = write_cache(kvq, case, "fp8", mode, ks, vs)
+        _check_pools(read_pools(c), oracle_pools(case, mode, ks, vs), case.slots)
+
+
+def test_cache_write_skips_negative_slots_and_strided_rows(kvq):
+    case = workloads.make_decode_case(31, [33], 4, 2, 128, table="perm", extra_pages=2)
+    c = kvq.PagedCache(case.num_pages, 2, 128, "fp8", "per_token_head")
+    slots = case.slots.copy()
+    slots[::3] = -1
+    # rows embedded in a wider [T][3*H*D] buffer (as K/V come out of a fused QKV)
+    T = len(slots)
+    wide_k = np.zeros((T, 3, 2, 128), np.float32)
+    wide_v = np.zeros_like(wide_k)
+    wide_k[:, 1] = case.k
+    wide_v[:, 2] = case.v
+    kt = dev_bf16(wide_k)
+    vt = dev_bf16(wide_v)
+    kvq.cache_write(c, kt[:, 1], vt[:, 2], dev(slots), token_stride=3 * 2 * 128)
+    got = read_pools(c)
+    keep = slots >= 0
+    want = ocache.new_pools(case.num_pages, 2, 128)
+    ocache.cache_write(want, case.k, case.v, slots, "per_token_head")
+    _check_pools(got, want, slots[keep])
+    skipped = case.slots[~keep]
+    page, off = skipped // 16, skipped % 16
+    assert not got["k_codes"][page, :, off].any()
+    assert not got["k_scales"][page, :, off].any()
+
+
+def test_cache_write_edge_values(kvq):
+    """Zero rows, NaN/inf entries, tiny values, values above 448 and exact-grid rows."""
+    D, H = 64, 2
+    rows = np.zeros((8, H, D), np.float32)
+    rows[1, 0, 3] = np.nan
+    rows[2, 1, :] = np.inf
+    rows[2, 1, 5] = -np.inf
+    rows[3] = 1e-30
+    rows[4] = workloads.bf16_round(np.linspace(-1000, 1000, D, dtype=np.float32))
+    rows[5, :, ::2] = -0.0
+    rows[6] = workloads.bf16_round(np.float32(2.0) ** np.arange(-20, 44, dtype=np.float32))
+    rows[7] = 448.0
+    rows = workloads.bf16_round(rows)
+    slots = np.arange(8, dtype=np.int64) * 3
+    case = workloads.DecodeCase("edge", np.zeros((1, H, D), np.float32), rows, rows[::-1].copy(),
+                                np.zeros(8, np.int64), np.arange(8), slots,
+                                np.arange(2, dtype=np.int32)[None], np.array([8], np.int32),
+                                2, H, D)
+    for mode, ks in (("per_token_head", 1.0), ("per_tensor", 1.0), ("per_tensor", 0.001)):
+        log(f"cache_write edges {mode} {ks}")
+        c = write_cache(kvq, case, "fp8", mode, ks, ks)
+        got = read_pools(c)
+        want = oracle_pools(case, mode, ks, ks)
+        page, off = slots // 16, slots % 16
+        for name in ("k_codes", "v_codes"):
+            assert np.array_equal(got[name][page, :, off], want[name][page, :, off]), name
+        if mode == "per_token_head":
+            for name in ("k_scales", "v_scales"):
+                g, w = got[name][page, :, off], want[name][page, :, off]
+                both_nan = np.isnan(g) & np.isnan(w)
+                assert np.array_equal(g[~both_nan].view(np.uint32),
+                                      w[~both_nan].view(np.uint32)), name
+                assert np.array_equal(np.isnan(g), np.isnan(w)), name
+
+
+def test_cache_write_bf16_copy(kvq):
+    case = workloads.make_decode_case(41, [20, 3], 8, 2, 64, table="perm")
+    c = write_cache(kvq, case, "bf16")
+    got = read_pools(c)
+    page, off = case.slots // 16, case.slots % 16
+    assert np.array_equal(got["k"][page, :, off], case.k)
+    assert np.array_equal(got["v"][page, :, off], case.v)
+
+
+def test_cache_write_llama8b_sampled(kvq):
+    """Full Llama-3.1-8B-shaped cache (8 x 20,000 tokens, outlier channels), written
+    in the bulk configuration; codes and scales compared on sampled tokens."""
+    case = workloads.llama8b_decode()
+    log("cache_write llama8b full")
+    c = write_cache(kvq, case, "fp8", "per_token_head", chunk=1 << 24)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(len(case.k), size=4000, replace=False))
+    want = oracle_pools(case, "per_token_head", rows=rows)
+    _check_pools(read_pools(c), want, case.slots[rows])
