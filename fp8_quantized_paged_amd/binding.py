@@ -234,6 +234,17 @@ def decode_workspace_bytes(cache: PagedCache, num_seqs: int, num_q_heads: int,
     return n.value
 
 
+def decode_workspace(cache: PagedCache, num_seqs: int, num_q_heads: int,
+                     max_seq_len: int, window: int = 0, pages_per_split: int = 0,
+                     device="cuda"):
+    """A zero-filled workspace of the size kvq_decode_workspace_bytes asks for (its
+    completion counters must start at zero; calls leave them zero)."""
+    torch = _torch()
+    nb = decode_workspace_bytes(cache, num_seqs, num_q_heads, max_seq_len, window,
+                                pages_per_split)
+    return torch.zeros(max(nb, 256), dtype=torch.uint8, device=device)
+
+
 def decode_attention(cache: PagedCache, q, block_table, seq_lens, max_seq_len: int,
                      scales: Scales | None = None, window: int = 0,
                      softmax_scale: float = 0.0, pages_per_split: int = 0,
@@ -247,8 +258,8 @@ def decode_attention(cache: PagedCache, q, block_table, seq_lens, max_seq_len: i
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16 if out_dtype == "bf16"
                           else torch.float32, device=q.device)
     if workspace is None:
-        nb = decode_workspace_bytes(cache, B, Hq, max_seq_len, window, pages_per_split)
-        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(cache, B, Hq, max_seq_len, window, pages_per_split,
+                                     q.device)
     d = cache.desc()
     _check(_lib.kvq_decode_attention(
         ctypes.byref(d), _ptr(q), B, Hq, _ptr(block_table), block_table.shape[1],

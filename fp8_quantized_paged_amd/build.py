@@ -24,6 +24,10 @@ COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # Keep the decode kernel's unrolled page ring: without this, SimplifyCFG sinks
+    # the identical per-page code of the three buffers back into one block, which
+    # removes the prefetch of the next pages.
+    "-mllvm", "-simplifycfg-sink-common=false",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

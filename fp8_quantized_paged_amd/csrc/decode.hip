@@ -74,6 +74,21 @@ __device__ __forceinline__ SplitRange visible_range(int L, int window) {
   return r;
 }
 
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_out(void* out, int32_t out_f32, int64_t i, float v) {
+  if (out_f32)
+    static_cast<float*>(out)[i] = v;
+  else
+    static_cast<uint16_t*>(out)[i] = (uint16_t)float_to_bf16_bits(v);
+}
+
 // Butterfly over lane bits [LOG_LPT-1 .. LOG_LPT-NB] then all-reduce over the rest.
 template <int NV, int LOG_LPT, int NB, int STEP>
 __device__ __forceinline__ void butterfly(float (&v)[NV], int c) {
@@ -110,7 +125,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const uint8_t* __restrict__ k_pages, const uint8_t* __restrict__ v_pages,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales,
     float q_scale, float k_scale, float v_scale, float sm_log2, int32_t window,
-    float* __restrict__ o_part, float* __restrict__ ml_part) {
+    float* __restrict__ o_part, float* __restrict__ ml_part, int32_t* __restrict__ counters,
+    void* __restrict__ out, int32_t out_f32) {
   using S = DecodeShape<D, G, kFp8>;
   __shared__ uint32_t lds_all[kWavesPerBlock][S::LDS_WORDS];
 
@@ -125,9 +141,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const SplitRange vr = visible_range(L, window);
   const int pb = vr.pfirst + s * pps;
   const int pe = min(pb + pps, vr.pend);
-  if (L <= 0 || pb >= pe) return;
-
+  const int ns = L > 0 ? (vr.pend - vr.pfirst + pps - 1) / pps : 0;  // splits of (b, g)
   const int num_q_heads = num_kv_heads * G;
+  if (s >= ns) {
+    if (s == 0) {  // empty sequence: zero output rows
+      for (int e = lane; e < G * D; e += kWave)
+        store_out(out, out_f32, ((int64_t)b * num_q_heads + g * G) * D + e, 0.0f);
+    }
+    return;
+  }
+
   uint32_t* lds = lds_all[wave];
   uint32_t* p_lds = lds + (kFp8 ? S::Q_WORDS : 0);
   const int tg = lane / S::LPT;   // token group (QK layout)
@@ -137,14 +160,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const uint16_t* qg = q + ((int64_t)b * num_q_heads + (int64_t)g * G) * D;
   uint32_t qv[G][8];  // bf16 pairs of channels 16c .. 16c+15, per head
   if constexpr (kFp8) {
+    const bool unit_q = q_scale == 1.0f;
     for (int e = lane * 8; e < G * D; e += kWave * 8) {
       const uint4 x = *reinterpret_cast<const uint4*>(qg + e);
       const uint32_t xx[4] = {x.x, x.y, x.z, x.w};
       uint32_t out[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t c0 = e4m3_quantize(bf16_bits_to_float(xx[i] & 0xFFFFu), q_scale);
-        const uint32_t c1 = e4m3_quantize(bf16_bits_to_float(xx[i] >> 16), q_scale);
+        // x / 1.0 == x exactly, so the division is skipped for a unit scale
+        const float x0 = bf16_bits_to_float(xx[i] & 0xFFFFu);
+        const float x1 = bf16_bits_to_float(xx[i] >> 16);
+        const uint32_t c0 = unit_q ? e4m3_encode(x0) : e4m3_quantize(x0, q_scale);
+        const uint32_t c1 = unit_q ? e4m3_encode(x1) : e4m3_quantize(x1, q_scale);
         out[i] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(c0 | (c1 << 8)));
       }
       *reinterpret_cast<uint4*>(lds + e / 2) = make_uint4(out[0], out[1], out[2], out[3]);
@@ -204,12 +231,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int* bt = block_table + (int64_t)b * bt_stride;
   const int bt_lane = (pb + lane < pe) ? bt[pb + lane] : 0;
 
-  for (int i = pb; i < pe; ++i) {
+  // One page's inputs for this lane: K rows of its token slots, V rows of its
+  // channels, and the per-token scales of the scores it will hold.
+  struct PageRegs {
+    uint32_t kr[S::NT][S::KW];
+    uint32_t vrw[S::DPL][S::VW];
+    float ksc[S::NVL], vsc[S::NVL];
+  };
+
+  auto load_page = [&](int i, PageRegs& r) {
     const int page = __builtin_amdgcn_readlane(bt_lane, i - pb);
     const int64_t tile = (int64_t)page * num_kv_heads + g;
-
-    // ---- loads: K rows of this lane's token slots, V rows of its channels ----
-    uint32_t kr[S::NT][S::KW];
 #pragma unroll
     for (int ts = 0; ts < S::NT; ++ts) {
       const int t = tg + ts * S::TPL;
@@ -218,11 +250,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
       for (int j = 0; j < S::KW / 4; ++j) {
         const uint4 x = src[j];
-        kr[ts][4 * j] = x.x; kr[ts][4 * j + 1] = x.y;
-        kr[ts][4 * j + 2] = x.z; kr[ts][4 * j + 3] = x.w;
+        r.kr[ts][4 * j] = x.x; r.kr[ts][4 * j + 1] = x.y;
+        r.kr[ts][4 * j + 2] = x.z; r.kr[ts][4 * j + 3] = x.w;
       }
     }
-    uint32_t vrw[S::DPL][S::VW];
 #pragma unroll
     for (int dd = 0; dd < S::DPL; ++dd) {
       const uint4* src = reinterpret_cast<const uint4*>(
@@ -230,22 +261,23 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
       for (int j = 0; j < S::VW / 4; ++j) {
         const uint4 x = src[j];
-        vrw[dd][4 * j] = x.x; vrw[dd][4 * j + 1] = x.y;
-        vrw[dd][4 * j + 2] = x.z; vrw[dd][4 * j + 3] = x.w;
+        r.vrw[dd][4 * j] = x.x; r.vrw[dd][4 * j + 1] = x.y;
+        r.vrw[dd][4 * j + 2] = x.z; r.vrw[dd][4 * j + 3] = x.w;
       }
     }
-    float ksc[S::NVL], vsc[S::NVL];
 #pragma unroll
     for (int k = 0; k < S::NVL; ++k) {
       if constexpr (kFp8 && kPTH) {
-        ksc[k] = k_scales[tile * kPage + t_of[k]];
-        vsc[k] = v_scales[tile * kPage + t_of[k]];
+        r.ksc[k] = k_scales[tile * kPage + t_of[k]];
+        r.vsc[k] = v_scales[tile * kPage + t_of[k]];
       } else {
-        ksc[k] = 1.0f;
-        vsc[k] = kFp8 ? v_scale : 1.0f;
+        r.ksc[k] = 1.0f;
+        r.vsc[k] = kFp8 ? v_scale : 1.0f;
       }
     }
+  };
 
+  auto compute_page = [&](int i, const PageRegs& r) {
     // ---- QK partial dots -----------------------------------------------------
     float part[S::NV];
 #pragma unroll
@@ -254,10 +286,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if constexpr (kFp8) {
-          kp[j] = (j & 1) ? e4m3x2_to_bf16x2<true>(kr[ts][j / 2])
-                          : e4m3x2_to_bf16x2<false>(kr[ts][j / 2]);
+          kp[j] = (j & 1) ? e4m3x2_to_bf16x2<true>(r.kr[ts][j / 2])
+                          : e4m3x2_to_bf16x2<false>(r.kr[ts][j / 2]);
         } else {
-          kp[j] = as_bf16x2(kr[ts][j]);
+          kp[j] = as_bf16x2(r.kr[ts][j]);
         }
       }
 #pragma unroll
@@ -279,7 +311,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
     for (int k = 0; k < S::NVL; ++k) {
       const int pos = i * kPage + t_of[k];
-      sc[k] = (pos >= vr.lo && pos < L) ? sc[k] * (qk_base * ksc[k]) : -INFINITY;
+      sc[k] = (pos >= vr.lo && pos < L) ? sc[k] * (qk_base * r.ksc[k]) : -INFINITY;
       over |= sc[k] > m_mine[k] + kRescaleSlack;
     }
     if (__builtin_amdgcn_ballot_w64(over) != 0) {
@@ -318,7 +350,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       const float p = __builtin_amdgcn_exp2f(sc[k] - m_mine[k]);
       if (owner) {
         l_mine[k] += p;
-        pf[hh_of[k] * kPage + t_of[k]] = p * vsc[k];
+        pf[hh_of[k] * kPage + t_of[k]] = p * r.vsc[k];
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -332,13 +364,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
       for (int j = 0; j < kPage / 2; ++j) {
         if constexpr (kFp8) {
-          const float2_t f = (j & 1) ? e4m3x2_to_f32x2<true>(vrw[dd][j / 2])
-                                     : e4m3x2_to_f32x2<false>(vrw[dd][j / 2]);
+          const float2_t f = (j & 1) ? e4m3x2_to_f32x2<true>(r.vrw[dd][j / 2])
+                                     : e4m3x2_to_f32x2<false>(r.vrw[dd][j / 2]);
           vf[dd][2 * j] = f.x;
           vf[dd][2 * j + 1] = f.y;
         } else {
-          vf[dd][2 * j] = bf16_bits_to_float(vrw[dd][j] & 0xFFFFu);
-          vf[dd][2 * j + 1] = bf16_bits_to_float(vrw[dd][j] >> 16);
+          vf[dd][2 * j] = bf16_bits_to_float(r.vrw[dd][j] & 0xFFFFu);
+          vf[dd][2 * j + 1] = bf16_bits_to_float(r.vrw[dd][j] >> 16);
         }
       }
 #pragma unroll
@@ -357,65 +389,131 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         acc[hh][dd] = x;
       }
     }
+  };
+
+  // Ring of three page buffers, written out so every buffer is a named register
+  // set: two pages are in flight while the third is computed.
+  PageRegs ra, rb, rc;
+  load_page(pb, ra);
+  if (pb + 1 < pe) load_page(pb + 1, rb);
+  for (int i = pb; i < pe; i += 3) {
+    if (i + 2 < pe) load_page(i + 2, rc);
+    compute_page(i, ra);
+    if (i + 1 >= pe) break;
+    if (i + 3 < pe) load_page(i + 3, ra);
+    compute_page(i + 1, rb);
+    if (i + 2 >= pe) break;
+    if (i + 4 < pe) load_page(i + 4, rb);
+    compute_page(i + 2, rc);
   }
 
-  // ---- split partials: o (unnormalised), m (log2 domain), l ----------------------
+  // ---- split results --------------------------------------------------------------
+  float lh[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     float x = 0.0f;
 #pragma unroll
     for (int k = 0; k < S::NVL; ++k) x += (owner && hh_of[k] == hh) ? l_mine[k] : 0.0f;
-    const float lh = wave_sum(x);
-    const int64_t row = ((int64_t)b * num_q_heads + g * G + hh) * splits + s;
+    lh[hh] = wave_sum(x);
+  }
+  const int64_t out_row0 = (int64_t)b * num_q_heads + g * G;
+  if (ns == 1) {  // the only split: normalise and store directly
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float inv = lh[hh] > 0.0f ? 1.0f / lh[hh] : 0.0f;
+#pragma unroll
+      for (int dd = 0; dd < S::DPL; ++dd)
+        store_out(out, out_f32, (out_row0 + hh) * D + lane + kWave * dd, acc[hh][dd] * inv);
+    }
+    return;
+  }
+  // partials: o (unnormalised), m (log2 domain), l.  Stored as agent-scope atomics,
+  // i.e. written through to the device coherence point (the L2 of each XCD is not
+  // coherent with the others), so no L2 write-back is needed to publish them.
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const int64_t row = (out_row0 + hh) * splits + s;
     if (lane == 0) {
-      ml_part[row * 2] = m_all[hh];
-      ml_part[row * 2 + 1] = lh;
+      store_agent(&ml_part[row * 2], m_all[hh]);
+      store_agent(&ml_part[row * 2 + 1], lh[hh]);
     }
 #pragma unroll
-    for (int dd = 0; dd < S::DPL; ++dd) o_part[row * D + lane + kWave * dd] = acc[hh][dd];
+    for (int dd = 0; dd < S::DPL; ++dd)  // lane-major: this lane's channels adjacent
+      store_agent(&o_part[row * D + lane * S::DPL + dd], acc[hh][dd]);
   }
-}
-
-template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(
-    int32_t num_q_heads, int32_t splits, int32_t pps, const int32_t* __restrict__ seq_lens,
-    int32_t window, const float* __restrict__ o_part, const float* __restrict__ ml_part,
-    void* __restrict__ out, int32_t out_f32) {
-  const int b = blockIdx.x / num_q_heads;
-  const int h = blockIdx.x % num_q_heads;
-  const int lane = threadIdx.x;
-  const int L = seq_lens[b];
-  int ns = 0;
-  if (L > 0) {
-    const SplitRange vr = visible_range(L, window);
-    ns = (vr.pend - vr.pfirst + pps - 1) / pps;
-  }
-  const int64_t row0 = ((int64_t)b * num_q_heads + h) * splits;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml_part[(row0 + s) * 2]);
-  float lsum = 0.0f;
-  float o[D / kWave];
+  // The last split of (b, g) to finish merges all of them (level 3 of the float32
+  // accumulation): wait until this wave's partials are performed, then count; the
+  // wave that completes the count reads the partials back with agent-scope loads
+  // and resets the counter for the next call.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // s_waitcnt vmcnt(0)
+  int done = 0;
+  if (lane == 0)
+    done = __hip_atomic_fetch_add(&counters[(int64_t)b * num_kv_heads + g], 1,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  done = __builtin_amdgcn_readfirstlane(done);
+  if (done != ns - 1) return;
+  // Merge with many loads in flight: weights of up to 64 splits sit one per lane;
+  // partial rows are fetched kMergeBatch splits x G heads at a time.
+  constexpr int kMergeBatch = (G * S::DPL) >= 64 ? 1 : 64 / (G * S::DPL);
+  float M[G], lpart[G], o[G][S::DPL];
 #pragma unroll
-  for (int dd = 0; dd < D / kWave; ++dd) o[dd] = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float m = ml_part[(row0 + s) * 2];
-    if (m == -INFINITY) continue;
-    const float wgt = __builtin_amdgcn_exp2f(m - M);
-    lsum += ml_part[(row0 + s) * 2 + 1] * wgt;
+  for (int hh = 0; hh < G; ++hh) {
+    const int64_t row0 = (out_row0 + hh) * splits;
+    float mj = -INFINITY;
+    for (int j = lane; j < ns; j += kWave) mj = fmaxf(mj, load_agent(&ml_part[(row0 + j) * 2]));
+    M[hh] = wave_max(mj);
+    lpart[hh] = 0.0f;
 #pragma unroll
-    for (int dd = 0; dd < D / kWave; ++dd)
-      o[dd] += o_part[(row0 + s) * D + lane + kWave * dd] * wgt;
+    for (int dd = 0; dd < S::DPL; ++dd) o[hh][dd] = 0.0f;
   }
-  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-  const int64_t base = ((int64_t)b * num_q_heads + h) * D;
+  for (int j0 = 0; j0 < ns; j0 += kWave) {
+    float w[G];  // lane x: weight of split j0 + x
 #pragma unroll
-  for (int dd = 0; dd < D / kWave; ++dd) {
-    const float r = o[dd] * inv;
-    if (out_f32)
-      static_cast<float*>(out)[base + lane + kWave * dd] = r;
-    else
-      static_cast<uint16_t*>(out)[base + lane + kWave * dd] = (uint16_t)float_to_bf16_bits(r);
+    for (int hh = 0; hh < G; ++hh) {
+      const int64_t row = (out_row0 + hh) * splits + j0 + lane;
+      w[hh] = 0.0f;
+      if (j0 + lane < ns) {
+        const float m = load_agent(&ml_part[row * 2]);
+        w[hh] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M[hh]);
+        lpart[hh] += load_agent(&ml_part[row * 2 + 1]) * w[hh];
+      }
+    }
+    const int cnt = min(kWave, ns - j0);
+    for (int x0 = 0; x0 < cnt; x0 += kMergeBatch) {
+      float v[G][kMergeBatch][S::DPL];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+          const int x = min(x0 + u, cnt - 1);  // clamped rows get weight 0 below
+          const int64_t row = (out_row0 + hh) * splits + j0 + x;
+#pragma unroll
+          for (int dd = 0; dd < S::DPL; ++dd)
+            v[hh][u][dd] = load_agent(&o_part[row * D + lane * S::DPL + dd]);
+        }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+          const float wx = x0 + u < cnt ? __int_as_float(__builtin_amdgcn_readlane(
+                                              __float_as_int(w[hh]), x0 + u))
+                                        : 0.0f;
+#pragma unroll
+          for (int dd = 0; dd < S::DPL; ++dd) o[hh][dd] += v[hh][u][dd] * wx;
+        }
+    }
   }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const float lsum = wave_sum(lpart[hh]);
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+#pragma unroll
+    for (int dd = 0; dd < S::DPL; ++dd)
+      store_out(out, out_f32, (out_row0 + hh) * D + lane * S::DPL + dd, o[hh][dd] * inv);
+  }
+  if (lane == 0)
+    __hip_atomic_store(&counters[(int64_t)b * num_kv_heads + g], 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- host side ----------------------------------------------------------------------
@@ -444,8 +542,14 @@ static int auto_pages_per_split(int32_t num_seqs, int32_t num_kv_heads, int max_
 struct DecodePlan {
   int pps;
   int splits;
+  size_t counter_bytes;  // completion counters, int32 [B][Hkv], 256-byte padded
   size_t bytes;
 };
+
+static size_t counter_area_bytes(int32_t num_seqs, int32_t num_kv_heads) {
+  const size_t n = (size_t)num_seqs * num_kv_heads * sizeof(int32_t);
+  return (n + 255) / 256 * 256;
+}
 
 static kvq_status plan_decode(const kvq_cache_desc* cache, int32_t num_seqs,
                               int32_t num_q_heads, int32_t max_seq_len, int32_t window,
@@ -466,9 +570,11 @@ static kvq_status plan_decode(const kvq_cache_desc* cache, int32_t num_seqs,
   const int mp = max_visible_pages(max_seq_len, window);
   plan->pps = pages_per_split ? pages_per_split
                               : auto_pages_per_split(num_seqs, cache->num_kv_heads, mp);
-  plan->splits = (mp + plan->pps - 1) / plan->pps;
-  plan->bytes = (size_t)num_seqs * num_q_heads * plan->splits * (cache->head_dim + 2) *
-                sizeof(float);
+  // at least one split: an all-empty batch still needs its zero output rows
+  plan->splits = mp > 0 ? (mp + plan->pps - 1) / plan->pps : 1;
+  plan->counter_bytes = counter_area_bytes(num_seqs, cache->num_kv_heads);
+  plan->bytes = plan->counter_bytes + (size_t)num_seqs * num_q_heads * plan->splits *
+                                          (cache->head_dim + 2) * sizeof(float);
   return KVQ_OK;
 }
 
@@ -476,40 +582,43 @@ template <int D, int G, bool kFp8, bool kPTH>
 static void launch_split(const kvq_cache_desc* c, const void* q, int32_t B,
                          const DecodePlan& pl, const int32_t* bt, int32_t bts,
                          const int32_t* sl, const kvq_scales* sc, float sm_log2,
-                         int32_t window, float* o_part, float* ml_part, hipStream_t st) {
+                         int32_t window, float* o_part, float* ml_part, int32_t* counters,
+                         void* out, int32_t out_f32, hipStream_t st) {
   const int64_t waves = (int64_t)B * c->num_kv_heads * pl.splits;
   const unsigned blocks = (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
   decode_split_kernel<D, G, kFp8, kPTH><<<blocks, 256, 0, st>>>(
       static_cast<const uint16_t*>(q), B, c->num_kv_heads, pl.splits, pl.pps, bt, bts, sl,
       static_cast<const uint8_t*>(c->k_pages), static_cast<const uint8_t*>(c->v_pages),
       c->k_scales, c->v_scales, sc ? sc->q_scale : 1.f, sc ? sc->k_scale : 1.f,
-      sc ? sc->v_scale : 1.f, sm_log2, window, o_part, ml_part);
+      sc ? sc->v_scale : 1.f, sm_log2, window, o_part, ml_part, counters, out, out_f32);
 }
 
 template <int D, int G>
 static void dispatch_dtype(const kvq_cache_desc* c, const void* q, int32_t B,
                            const DecodePlan& pl, const int32_t* bt, int32_t bts,
                            const int32_t* sl, const kvq_scales* sc, float sm_log2,
-                           int32_t window, float* o, float* ml, hipStream_t st) {
+                           int32_t window, float* o, float* ml, int32_t* cnt, void* out,
+                           int32_t f32, hipStream_t st) {
   if (c->dtype == KVQ_BF16)
-    launch_split<D, G, false, false>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, st);
+    launch_split<D, G, false, false>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st);
   else if (c->mode == KVQ_SCALE_PER_TOKEN_HEAD)
-    launch_split<D, G, true, true>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, st);
+    launch_split<D, G, true, true>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st);
   else
-    launch_split<D, G, true, false>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, st);
+    launch_split<D, G, true, false>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st);
 }
 
 template <int D>
 static void dispatch_group(int G, const kvq_cache_desc* c, const void* q, int32_t B,
                            const DecodePlan& pl, const int32_t* bt, int32_t bts,
                            const int32_t* sl, const kvq_scales* sc, float sm_log2,
-                           int32_t window, float* o, float* ml, hipStream_t st) {
+                           int32_t window, float* o, float* ml, int32_t* cnt, void* out,
+                           int32_t f32, hipStream_t st) {
   switch (G) {
-    case 1: dispatch_dtype<D, 1>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, st); break;
-    case 2: dispatch_dtype<D, 2>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, st); break;
-    case 4: dispatch_dtype<D, 4>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, st); break;
-    case 8: dispatch_dtype<D, 8>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, st); break;
-    case 16: dispatch_dtype<D, 16>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, st); break;
+    case 1: dispatch_dtype<D, 1>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st); break;
+    case 2: dispatch_dtype<D, 2>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st); break;
+    case 4: dispatch_dtype<D, 4>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st); break;
+    case 8: dispatch_dtype<D, 8>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st); break;
+    case 16: dispatch_dtype<D, 16>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st); break;
   }
 }
 
@@ -569,22 +678,15 @@ extern "C" kvq_status kvq_decode_attention(
   const int G = num_q_heads / cache->num_kv_heads;
   const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)D);
   const float sm_log2 = sm * kLog2e;
-  float* o_part = static_cast<float*>(workspace);
+  int32_t* counters = static_cast<int32_t*>(workspace);
+  float* o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.counter_bytes);
   float* ml_part = o_part + (size_t)num_seqs * num_q_heads * pl.splits * D;
-  auto st = static_cast<hipStream_t>(stream);
-  if (pl.splits > 0) {
-    switch (D) {
-      case 64: dispatch_group<64>(G, cache, q, num_seqs, pl, block_table, block_table_stride, seq_lens, scales, sm_log2, window, o_part, ml_part, st); break;
-      case 128: dispatch_group<128>(G, cache, q, num_seqs, pl, block_table, block_table_stride, seq_lens, scales, sm_log2, window, o_part, ml_part, st); break;
-      case 256: dispatch_group<256>(G, cache, q, num_seqs, pl, block_table, block_table_stride, seq_lens, scales, sm_log2, window, o_part, ml_part, st); break;
-    }
-  }
-  const unsigned mblocks = (unsigned)((int64_t)num_seqs * num_q_heads);
   const int f32 = out_dtype == KVQ_F32;
+  auto st = static_cast<hipStream_t>(stream);
   switch (D) {
-    case 64: decode_merge_kernel<64><<<mblocks, 64, 0, st>>>(num_q_heads, pl.splits, pl.pps, seq_lens, window, o_part, ml_part, out, f32); break;
-    case 128: decode_merge_kernel<128><<<mblocks, 64, 0, st>>>(num_q_heads, pl.splits, pl.pps, seq_lens, window, o_part, ml_part, out, f32); break;
-    case 256: decode_merge_kernel<256><<<mblocks, 64, 0, st>>>(num_q_heads, pl.splits, pl.pps, seq_lens, window, o_part, ml_part, out, f32); break;
+    case 64: dispatch_group<64>(G, cache, q, num_seqs, pl, block_table, block_table_stride, seq_lens, scales, sm_log2, window, o_part, ml_part, counters, out, f32, st); break;
+    case 128: dispatch_group<128>(G, cache, q, num_seqs, pl, block_table, block_table_stride, seq_lens, scales, sm_log2, window, o_part, ml_part, counters, out, f32, st); break;
+    case 256: dispatch_group<256>(G, cache, q, num_seqs, pl, block_table, block_table_stride, seq_lens, scales, sm_log2, window, o_part, ml_part, counters, out, f32, st); break;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch: %s", hipGetErrorString(e));

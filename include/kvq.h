@@ -179,9 +179,10 @@ kvq_status kvq_quantize_fp8(const void* x, int64_t n, float scale, uint8_t* code
                             void* stream);
 
 /*
- * Workspace bytes needed by kvq_decode_attention for these arguments (split-K
- * partial results).  pages_per_split = 0 selects the library's choice, which
- * depends only on the arguments given here.  bytes [host].
+ * Workspace bytes needed by kvq_decode_attention for these arguments: completion
+ * counters (int32 per (sequence, KV head), 256-byte padded) followed by the split-K
+ * partial results.  pages_per_split = 0 selects the library's choice, which depends
+ * only on the arguments given here.  bytes [host].
  */
 kvq_status kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t max_seq_len,
@@ -204,7 +205,8 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t num_s
  * probability weights p_j * v_scale_j enter the P.V dot products rounded to bf16;
  * partial results of each split are merged in float32 (the pages' two-level
  * accumulation: level 1 inside a page, level 2 in the split's fp32 registers,
- * level 3 across splits).
+ * level 3 across splits, done by the last split of each (sequence, KV head) to
+ * finish; there is a single kernel launch per call).
  *
  * q [device] bf16 [num_seqs][num_q_heads][D];  out [device] [num_seqs][num_q_heads][D]
  *   of out_dtype (KVQ_BF16 or KVQ_F32).
@@ -216,6 +218,9 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t num_s
  * softmax_scale: 0 selects 1/sqrt(D).
  * pages_per_split: 0 = library choice; must match kvq_decode_workspace_bytes.
  * workspace [device], workspace_bytes: at least kvq_decode_workspace_bytes(...).
+ *   Its counter area must be zero before the first call (allocate it zero-filled);
+ *   every call leaves it zero again.  Calls that share one workspace must not
+ *   overlap in time (same stream, or ordered by events).
  * Supported: D in {64,128,256}; num_q_heads / num_kv_heads in {1,2,4,8,16}.
  */
 kvq_status kvq_decode_attention(const kvq_cache_desc* cache, const void* q,

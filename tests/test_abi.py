@@ -110,14 +110,14 @@ def test_decode_workspace_and_checks():
     L = _lib()
     n = ctypes.c_size_t()
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 32, 20000, 0, 0, ctypes.byref(n)) == 0
-    assert n.value > 0
-    assert n.value % (8 * 32 * (128 + 2) * 4) == 0
+    assert n.value > 256
+    assert (n.value - 256) % (8 * 32 * (128 + 2) * 4) == 0   # 256: counters for 8 x 8
     # explicit pages_per_split: splits = ceil(1250 / 10) = 125
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 32, 20000, 0, 10, ctypes.byref(n)) == 0
-    assert n.value == 8 * 32 * 125 * 130 * 4
+    assert n.value == 256 + 8 * 32 * 125 * 130 * 4
     # a window bounds the visible pages: 128 keys span at most 9 pages
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 32, 20000, 128, 4, ctypes.byref(n)) == 0
-    assert n.value == 8 * 32 * 3 * 130 * 4
+    assert n.value == 256 + 8 * 32 * 3 * 130 * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 24, 20000, 0, 0, ctypes.byref(n)) == kvq.binding.ERR_UNSUPPORTED
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 33, 20000, 0, 0, ctypes.byref(n)) == kvq.binding.ERR_INVALID_ARG
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 32, 20000, 0, 65, ctypes.byref(n)) == kvq.binding.ERR_INVALID_ARG
@@ -125,7 +125,7 @@ def test_decode_workspace_and_checks():
     args = lambda ws, wsb, outdt=kvq.BF16, q=4096, scales=ctypes.byref(sc): (
         ctypes.byref(d), q, 8, 32, 4096, 1250, 4096, 20000, scales, 0, 0.0, 10, 4096,
         outdt, ws, wsb, None)
-    need = 8 * 32 * 125 * 130 * 4
+    need = 256 + 8 * 32 * 125 * 130 * 4
     assert L.kvq_decode_attention(*args(None, 0)) == kvq.binding.ERR_WORKSPACE
     assert L.kvq_decode_attention(*args(4096, need - 1)) == kvq.binding.ERR_WORKSPACE
     assert L.kvq_decode_attention(*args(4096, need, outdt=kvq.FP8_E4M3)) == kvq.binding.ERR_UNSUPPORTED

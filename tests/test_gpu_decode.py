@@ -111,6 +111,30 @@ def test_split_count_invariance_and_determinism(kvq):
         assert np.array_equal(a, again[0])
 
 
+def test_workspace_reuse_across_calls(kvq):
+    """One workspace serves consecutive calls with different inputs and split counts:
+    every call must leave its completion counters at zero and must not read another
+    call's partial results."""
+    a = workloads.make_decode_case(63, [3000, 900, 0, 40], 32, 8, 128, table="perm")
+    b = workloads.make_decode_case(64, [2500, 17, 1300, 4000], 32, 8, 128, table="perm")
+    ca = write_cache(kvq, a, "fp8", "per_token_head")
+    cb = write_cache(kvq, b, "fp8", "per_token_head")
+    ws = kvq.decode_workspace(ca, 4, 32, 4000, 0, 4)
+    sc = kvq.Scales(1.0, 1.0, 1.0, 1.0)
+
+    def call(c, case):
+        return kvq.decode_attention(c, dev_bf16(case.q), dev(case.block_table),
+                                    dev(case.seq_lens), int(case.seq_lens.max()), sc,
+                                    pages_per_split=4, out_dtype="f32",
+                                    workspace=ws).cpu().numpy()
+    want_a = oracle_decode(a, "per_token_head")
+    want_b = oracle_decode(b, "per_token_head")
+    for _ in range(3):
+        assert_close_to_oracle(call(ca, a), want_a, "reuse a")
+        assert_close_to_oracle(call(cb, b), want_b, "reuse b")
+    assert not ws[:256].any()   # counters back at zero
+
+
 def test_llama8b_decode_sampled(kvq):
     """Llama-3.1-8B-shaped decode layer at full size (8 x 20,000 tokens, seeded
     permutation block table, outliers, per-token-head scales), in the launch
