@@ -509,7 +509,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
     for (int dd = 0; dd < S::DPL; ++dd)
-      store_out(out, out_f32, (out_row0 + hh) * D + lane * S::DPL + dd, o[hh][dd] * inv);
+      store_out(out, out_f32, (out_row0 + hh) * D + lane + kWave * dd, o[hh][dd] * inv);
   }
   if (lane == 0)
     __hip_atomic_store(&counters[(int64_t)b * num_kv_heads + g], 0, __ATOMIC_RELAXED,
