@@ -1,4 +1,5 @@
-// Split-K paged GQA decode attention over an FP8 (or bf16) cache, and the merge.
+// Split-K paged GQA decode attention over an FP8 (or bf16) cache, with the split
+// merge fused into the same launch.
 //
 // Method: "vLLM FP8 KV-Cache and Attention Quantization Update" (agentlenshq.com):
 // FP8 e4m3 storage halves the bytes each decode step reads (section "Performance
@@ -7,9 +8,10 @@
 // keep a bf16 cache (section "Hybrid attention and layer skipping"); the query is
 // quantised inside the attention op (section "Kernel and fusion optimizations").
 //
-// Work split.  One wavefront owns one (sequence b, KV head g, split s) and serves
-// all G query heads of the group.  A split is a run of at most 64 cache pages of
-// the sequence's visible key range; a workgroup holds four independent waves.
+// Work split.  A workgroup of four waves owns one (sequence b, KV head g, split s);
+// a split is a run of at most 256 cache pages of the sequence's visible key range,
+// dealt to the waves round-robin (wave w takes pages w, w+4, ...).  Each wave serves
+// all G query heads of the group, so every cache byte is loaded and converted once.
 //
 // Per page (16 tokens) a wave does:
 //   QK  - "token layout": D/16 lanes share one token row, each lane holding 16
@@ -22,22 +24,51 @@
 //         reference maximum: the wave rescales only when some score exceeds the
 //         reference by more than 2^8, so the common page costs one ballot.
 //   PV  - "channel layout": lane l owns channels l + 64*i and reads their 16-token
-//         rows of the dim-major V tile (one 16-byte load per channel), converted
-//         to float32.  The float32 weights p * v_scale are broadcast through LDS
-//         and accumulated with float32 FMAs (weights are not rounded below
-//         float32: with outlier channels the sum cancels large terms).
-// Accumulation levels: one page inside the dot2 chains / FMA chains, the split in
-// float32 registers, splits merged in float32 by the merge kernel.
+//         rows of the dim-major V tile (one 16-byte load per channel).
+//         fp8 cache: codes become exact f16 values and the weights, rounded to
+//         f16 (relative error <= 2^-11; the weights never exceed 2^8), enter
+//         v_dot2_f32_f16 with float32 accumulation straight into the running
+//         output.  Per-token V scales are folded into the weight's exponent
+//         (w = 2^(score + log2 v_scale - m_v)) against a second lazily moved
+//         reference m_v, so the f16 weights stay in range whatever the scales.
+//         bf16 cache: float32 weights and float32 FMAs.
+//   Weights travel from the score lanes to the channel lanes through LDS.
+// Accumulation levels: within a page in the dot2/FMA chains, the split in float32
+// registers, the four waves of a workgroup through LDS, and the splits of a
+// (sequence, KV head) by the last workgroup to finish (float32, fixed order).
 #include "kvq_device.h"
 #include "kvq_host.h"
 
 namespace kvq {
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
 constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: weights stay <= 256
-constexpr int kMaxPagesPerSplit = 64;
-constexpr int kWavesPerBlock = 4;
+constexpr int kWaves = 4;              // waves per workgroup
+constexpr int kThreads = kWaves * kWave;
+constexpr int kMaxPagesPerWave = 64;   // one block-table entry per lane
+constexpr int kMaxPagesPerSplit = kWaves * kMaxPagesPerWave;
+// Workgroups the automatic split size aims for: two per CU on 256 CUs, all of
+// them resident at once.
+constexpr int kTargetWorkgroups = 512;
+// s_waitcnt immediate (gfx9 encoding) that waits for every vector memory operation
+// and leaves the LDS/export counters free.
+constexpr int kWaitVmcnt0 = 0x0F70;
+// Page buffers per wave (pages in flight + the one being computed).
+constexpr int kDecodeRing = 3;
+// Cache pages are read once per call: load them non-temporally (they bypass the
+// caches' normal retention instead of evicting the block table, scales and query).
+constexpr bool kStreamLoads = true;
+constexpr bool kSplitMajor = false;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4_t stream_load(const u32x4_t* p) {
+  if constexpr (kStreamLoads) return __builtin_nontemporal_load(p);
+  else return *p;
+}
 
 template <int D, int G, bool kFp8>
 struct DecodeShape {
@@ -54,25 +85,28 @@ struct DecodeShape {
   static constexpr int KW = kFp8 ? 4 : 8;           // K dwords per lane per token slot
   static constexpr int VW = kFp8 ? 4 : 8;           // V dwords per channel row
   static constexpr int EB = kFp8 ? 1 : 2;           // element bytes
-  static constexpr int Q_WORDS = G * D / 2;         // query (bf16) in LDS
-  static constexpr int P_WORDS = G * kPage;         // weights (float32) in LDS
-  static constexpr int LDS_WORDS = (kFp8 ? Q_WORDS : 0) + P_WORDS;
+  // PV weights of one page in LDS: f16 [G][16] (fp8) or float [G][16] (bf16)
+  static constexpr int W_WORDS = kFp8 ? G * kPage / 2 : G * kPage;
 };
 
-// Number of pages a split covers and the visible page range of a sequence.
-struct SplitRange {
-  int lo;      // first visible key
-  int pfirst;  // first visible page
-  int pend;    // one past the last page
+struct DecodeArgs {
+  const uint16_t* q;
+  int32_t num_kv_heads, splits, pps;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  const uint8_t* k_pages;
+  const uint8_t* v_pages;
+  const float* k_scales;
+  const float* v_scales;
+  float q_scale, k_scale, v_scale, sm_log2;
+  int32_t window;
+  float* o_part;      // [B*Hkv][splits][G][D]
+  float* ml_part;     // [B*Hkv][splits][G][2]: reference max (log2), weight sum
+  int32_t* counters;  // [B*Hkv] finished splits; zero between calls
+  void* out;
+  int32_t out_f32;
 };
-
-__device__ __forceinline__ SplitRange visible_range(int L, int window) {
-  SplitRange r;
-  r.lo = window > 0 ? max(0, L - window) : 0;
-  r.pfirst = r.lo / kPage;
-  r.pend = (L + kPage - 1) / kPage;
-  return r;
-}
 
 __device__ __forceinline__ void store_agent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -89,7 +123,12 @@ __device__ __forceinline__ void store_out(void* out, int32_t out_f32, int64_t i,
     static_cast<uint16_t*>(out)[i] = (uint16_t)float_to_bf16_bits(v);
 }
 
-// Butterfly over lane bits [LOG_LPT-1 .. LOG_LPT-NB] then all-reduce over the rest.
+__device__ __forceinline__ float exp2_or_zero(float x) {
+  return x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x);
+}
+
+// Butterfly over lane bits [LOG_LPT-1 .. LOG_LPT-NB]: each step halves the values a
+// lane keeps and adds its partner's other half.
 template <int NV, int LOG_LPT, int NB, int STEP>
 __device__ __forceinline__ void butterfly(float (&v)[NV], int c) {
   if constexpr (STEP < NB) {
@@ -107,6 +146,7 @@ __device__ __forceinline__ void butterfly(float (&v)[NV], int c) {
   }
 }
 
+// Plain all-reduce over the remaining low lane bits (group sizes below 4).
 template <int NVL, int STEP, int NAR>
 __device__ __forceinline__ void allreduce_low_bits(float (&v)[NVL]) {
   if constexpr (STEP < NAR) {
@@ -117,87 +157,68 @@ __device__ __forceinline__ void allreduce_low_bits(float (&v)[NVL]) {
   }
 }
 
-template <int D, int G, bool kFp8, bool kPTH>
-__global__ __launch_bounds__(256) void decode_split_kernel(
-    const uint16_t* __restrict__ q, int32_t num_seqs, int32_t num_kv_heads,
-    int32_t splits, int32_t pps, const int32_t* __restrict__ block_table,
-    int32_t bt_stride, const int32_t* __restrict__ seq_lens,
-    const uint8_t* __restrict__ k_pages, const uint8_t* __restrict__ v_pages,
-    const float* __restrict__ k_scales, const float* __restrict__ v_scales,
-    float q_scale, float k_scale, float v_scale, float sm_log2, int32_t window,
-    float* __restrict__ o_part, float* __restrict__ ml_part, int32_t* __restrict__ counters,
-    void* __restrict__ out, int32_t out_f32) {
+template <int D, int G, bool kFp8, bool kPTH, int kRing>
+__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
   using S = DecodeShape<D, G, kFp8>;
-  __shared__ uint32_t lds_all[kWavesPerBlock][S::LDS_WORDS];
+  constexpr int QW = G * D / 2;                  // query as bf16 pairs
+  constexpr int MERGE = (kWaves / 2) * G * D;    // wave-merge slots (floats)
+  __shared__ uint32_t q_lds_all[kWaves][QW];
+  __shared__ uint32_t w_lds_all[kWaves][S::W_WORDS];
+  __shared__ float ml_lds[kWaves][G][2];
+  __shared__ float merge_lds[MERGE];
+  __shared__ int last_lds;
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
-  const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-  if (w >= (int64_t)num_seqs * num_kv_heads * splits) return;
-  const int s = (int)(w % splits);
-  const int g = (int)((w / splits) % num_kv_heads);
-  const int b = (int)(w / ((int64_t)splits * num_kv_heads));
-  const int L = seq_lens[b];
-  const SplitRange vr = visible_range(L, window);
-  const int pb = vr.pfirst + s * pps;
-  const int pe = min(pb + pps, vr.pend);
-  const int ns = L > 0 ? (vr.pend - vr.pfirst + pps - 1) / pps : 0;  // splits of (b, g)
-  const int num_q_heads = num_kv_heads * G;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  // Workgroup order: split-major (all (b, g) units of split 0, then split 1, ...),
+  // so the workgroups in flight together read neighbouring pages of the pools.
+  const int nunits = (int)(gridDim.x / (unsigned)a.splits);
+  const int s = kSplitMajor ? (int)(blockIdx.x / (unsigned)nunits)
+                            : (int)(blockIdx.x % (unsigned)a.splits);
+  const int ug = kSplitMajor ? (int)(blockIdx.x % (unsigned)nunits)
+                             : (int)(blockIdx.x / (unsigned)a.splits);  // b * Hkv + g
+  const int g = ug % a.num_kv_heads;
+  const int b = ug / a.num_kv_heads;
+  const int* bt = a.block_table + (int64_t)b * a.bt_stride;
+  const int64_t row0 = (int64_t)ug * G;  // first output row: b * Hq + g * G
+  // Issued before the sequence length is known: the query words of the group and,
+  // for full attention (the split's pages then do not depend on the length), the
+  // split's block-table entries; entries past the sequence are never used.
+  int bt_lane = 0;
+  if (a.window == 0) {
+    const int idx = s * a.pps + wave + kWaves * lane;
+    if (idx < min(s * a.pps + a.pps, a.bt_stride)) bt_lane = bt[idx];
+  }
+  constexpr int QPW = (QW + kWave - 1) / kWave;  // query words per lane
+  uint32_t qraw[QPW];
+  {
+    const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(a.q + row0 * D);
+#pragma unroll
+    for (int u = 0; u < QPW; ++u) {
+      const int e = lane + u * kWave;
+      qraw[u] = e < QW ? qsrc[e] : 0u;
+    }
+  }
+  const int L = a.seq_lens[b];
+  const int lo = a.window > 0 ? max(0, L - a.window) : 0;
+  const int pfirst = lo / kPage;
+  const int pend = (L + kPage - 1) / kPage;
+  const int ns = L > 0 ? (pend - pfirst + a.pps - 1) / a.pps : 0;  // splits of (b, g)
   if (s >= ns) {
     if (s == 0) {  // empty sequence: zero output rows
-      for (int e = lane; e < G * D; e += kWave)
-        store_out(out, out_f32, ((int64_t)b * num_q_heads + g * G) * D + e, 0.0f);
+      for (int e = tid; e < G * D; e += kThreads) store_out(a.out, a.out_f32, row0 * D + e, 0.0f);
     }
     return;
   }
 
-  uint32_t* lds = lds_all[wave];
-  uint32_t* p_lds = lds + (kFp8 ? S::Q_WORDS : 0);
   const int tg = lane / S::LPT;   // token group (QK layout)
   const int c = lane % S::LPT;    // channel chunk: channels 16c .. 16c+15
-
-  // ---- query: fused e4m3 quantisation (fp8) or plain bf16 -----------------------
-  const uint16_t* qg = q + ((int64_t)b * num_q_heads + (int64_t)g * G) * D;
-  uint32_t qv[G][8];  // bf16 pairs of channels 16c .. 16c+15, per head
-  if constexpr (kFp8) {
-    const bool unit_q = q_scale == 1.0f;
-    for (int e = lane * 8; e < G * D; e += kWave * 8) {
-      const uint4 x = *reinterpret_cast<const uint4*>(qg + e);
-      const uint32_t xx[4] = {x.x, x.y, x.z, x.w};
-      uint32_t out[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // x / 1.0 == x exactly, so the division is skipped for a unit scale
-        const float x0 = bf16_bits_to_float(xx[i] & 0xFFFFu);
-        const float x1 = bf16_bits_to_float(xx[i] >> 16);
-        const uint32_t c0 = unit_q ? e4m3_encode(x0) : e4m3_quantize(x0, q_scale);
-        const uint32_t c1 = unit_q ? e4m3_encode(x1) : e4m3_quantize(x1, q_scale);
-        out[i] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(c0 | (c1 << 8)));
-      }
-      *reinterpret_cast<uint4*>(lds + e / 2) = make_uint4(out[0], out[1], out[2], out[3]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const uint4 a = *reinterpret_cast<const uint4*>(lds + (hh * D + c * 16) / 2);
-      const uint4 bq = *reinterpret_cast<const uint4*>(lds + (hh * D + c * 16) / 2 + 4);
-      qv[hh][0] = a.x; qv[hh][1] = a.y; qv[hh][2] = a.z; qv[hh][3] = a.w;
-      qv[hh][4] = bq.x; qv[hh][5] = bq.y; qv[hh][6] = bq.z; qv[hh][7] = bq.w;
-    }
-  } else {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const uint4* src = reinterpret_cast<const uint4*>(qg + hh * D + c * 16);
-      const uint4 a = src[0], bq = src[1];
-      qv[hh][0] = a.x; qv[hh][1] = a.y; qv[hh][2] = a.z; qv[hh][3] = a.w;
-      qv[hh][4] = bq.x; qv[hh][5] = bq.y; qv[hh][6] = bq.z; qv[hh][7] = bq.w;
-    }
-  }
+  uint32_t qv[G][8];              // bf16 pairs of channels 16c .. 16c+15, per head;
+                                  // filled once the query is in LDS
 
   // score multiplier (log2 domain); per-token K scales multiply in per page
-  const float qk_base = kFp8 ? q_scale * sm_log2 * (kPTH ? 1.0f : k_scale) : sm_log2;
+  const float qk_base = kFp8 ? a.q_scale * a.sm_log2 * (kPTH ? 1.0f : a.k_scale) : a.sm_log2;
 
   // indices of the scores this lane holds after the butterfly
   int idx0 = 0;
@@ -213,71 +234,80 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     t_of[k] = tg + (n / G) * S::TPL;
   }
 
-  float m_all[G];
-  float m_mine[S::NVL], l_mine[S::NVL];
+  // Running state.  m_all: per-head reference maximum of the scores (wave-uniform);
+  // mv_all: reference of the V-weighted exponents (per-token-head scales only).
+  float m_all[G], mv_all[G];
+  float m_mine[S::NVL], mv_mine[S::NVL], l_mine[S::NVL];
   float acc[G][S::DPL];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     m_all[hh] = -INFINITY;
+    mv_all[hh] = -INFINITY;
 #pragma unroll
     for (int dd = 0; dd < S::DPL; ++dd) acc[hh][dd] = 0.0f;
   }
 #pragma unroll
   for (int k = 0; k < S::NVL; ++k) {
     m_mine[k] = -INFINITY;
+    mv_mine[k] = -INFINITY;
     l_mine[k] = 0.0f;
   }
 
-  const int* bt = block_table + (int64_t)b * bt_stride;
-  const int bt_lane = (pb + lane < pe) ? bt[pb + lane] : 0;
+  // this wave's pages of the split: pb + wave + kWaves * i, i < nwp
+  const int pb = pfirst + s * a.pps;
+  const int pe = min(pb + a.pps, pend);
+  const int nwp = pe - pb > wave ? (pe - pb - wave + kWaves - 1) / kWaves : 0;
+  if (a.window > 0) bt_lane = lane < nwp ? bt[pb + wave + kWaves * lane] : 0;
+  uint32_t* w_lds = w_lds_all[wave];
 
   // One page's inputs for this lane: K rows of its token slots, V rows of its
   // channels, and the per-token scales of the scores it will hold.
   struct PageRegs {
     uint32_t kr[S::NT][S::KW];
-    uint32_t vrw[S::DPL][S::VW];
+    uint32_t vr[S::DPL][S::VW];
     float ksc[S::NVL], vsc[S::NVL];
   };
 
   auto load_page = [&](int i, PageRegs& r) {
-    const int page = __builtin_amdgcn_readlane(bt_lane, i - pb);
-    const int64_t tile = (int64_t)page * num_kv_heads + g;
+    const int page = __builtin_amdgcn_readlane(bt_lane, i);
+    const int64_t tile = (int64_t)page * a.num_kv_heads + g;
 #pragma unroll
     for (int ts = 0; ts < S::NT; ++ts) {
       const int t = tg + ts * S::TPL;
-      const uint4* src = reinterpret_cast<const uint4*>(
-          k_pages + ((tile * kPage + t) * D + c * 16) * S::EB);
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+          a.k_pages + ((tile * kPage + t) * D + c * 16) * S::EB);
 #pragma unroll
       for (int j = 0; j < S::KW / 4; ++j) {
-        const uint4 x = src[j];
+        const u32x4_t x = stream_load(src + j);
         r.kr[ts][4 * j] = x.x; r.kr[ts][4 * j + 1] = x.y;
         r.kr[ts][4 * j + 2] = x.z; r.kr[ts][4 * j + 3] = x.w;
       }
     }
 #pragma unroll
     for (int dd = 0; dd < S::DPL; ++dd) {
-      const uint4* src = reinterpret_cast<const uint4*>(
-          v_pages + ((tile * D + lane + kWave * dd) * kPage) * S::EB);
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+          a.v_pages + ((tile * D + lane + kWave * dd) * kPage) * S::EB);
 #pragma unroll
       for (int j = 0; j < S::VW / 4; ++j) {
-        const uint4 x = src[j];
-        r.vrw[dd][4 * j] = x.x; r.vrw[dd][4 * j + 1] = x.y;
-        r.vrw[dd][4 * j + 2] = x.z; r.vrw[dd][4 * j + 3] = x.w;
+        const u32x4_t x = stream_load(src + j);
+        r.vr[dd][4 * j] = x.x; r.vr[dd][4 * j + 1] = x.y;
+        r.vr[dd][4 * j + 2] = x.z; r.vr[dd][4 * j + 3] = x.w;
       }
     }
 #pragma unroll
     for (int k = 0; k < S::NVL; ++k) {
       if constexpr (kFp8 && kPTH) {
-        r.ksc[k] = k_scales[tile * kPage + t_of[k]];
-        r.vsc[k] = v_scales[tile * kPage + t_of[k]];
+        r.ksc[k] = a.k_scales[tile * kPage + t_of[k]];
+        r.vsc[k] = a.v_scales[tile * kPage + t_of[k]];
       } else {
         r.ksc[k] = 1.0f;
-        r.vsc[k] = kFp8 ? v_scale : 1.0f;
+        r.vsc[k] = 1.0f;
       }
     }
   };
 
   auto compute_page = [&](int i, const PageRegs& r) {
+    const int lpage = pb + wave + kWaves * i;  // logical page
     // ---- QK partial dots -----------------------------------------------------
     float part[S::NV];
 #pragma unroll
@@ -294,14 +324,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        float a = 0.0f;
+        float x = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) a = dot2_bf16(as_bf16x2(qv[hh][j]), kp[j], a);
-        part[ts * G + hh] = a;
+        for (int j = 0; j < 8; ++j) x = dot2_bf16(as_bf16x2(qv[hh][j]), kp[j], x);
+        part[ts * G + hh] = x;
       }
     }
     butterfly<S::NV, S::LOG_LPT, S::NB, 0>(part, c);
-    float sc[S::NVL];
+    float sc[S::NVL], sv[S::NVL];
 #pragma unroll
     for (int k = 0; k < S::NVL; ++k) sc[k] = part[k];
     allreduce_low_bits<S::NVL, 0, S::NAR>(sc);
@@ -310,47 +340,59 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     bool over = false;
 #pragma unroll
     for (int k = 0; k < S::NVL; ++k) {
-      const int pos = i * kPage + t_of[k];
-      sc[k] = (pos >= vr.lo && pos < L) ? sc[k] * (qk_base * r.ksc[k]) : -INFINITY;
+      const int pos = lpage * kPage + t_of[k];
+      sc[k] = (pos >= lo && pos < L) ? sc[k] * (qk_base * r.ksc[k]) : -INFINITY;
       over |= sc[k] > m_mine[k] + kRescaleSlack;
+      if constexpr (kFp8 && kPTH) {
+        sv[k] = sc[k] + log2f(r.vsc[k]);
+        over |= sv[k] > mv_mine[k] + kRescaleSlack;
+      }
     }
     if (__builtin_amdgcn_ballot_w64(over) != 0) {
-      float alpha[G];
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        float x = -INFINITY;
+        float x = -INFINITY, y = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < S::NVL; ++k) x = hh_of[k] == hh ? fmaxf(x, sc[k]) : x;
-        const float mx = wave_max(x);
-        const float mn = fmaxf(m_all[hh], mx);
-        alpha[hh] = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_all[hh] - mn);
-        m_all[hh] = mn;
-#pragma unroll
-        for (int dd = 0; dd < S::DPL; ++dd) acc[hh][dd] *= alpha[hh];
-      }
-#pragma unroll
-      for (int k = 0; k < S::NVL; ++k) {
-        float a = alpha[0], m = m_all[0];
-#pragma unroll
-        for (int hh = 1; hh < G; ++hh) {
-          a = hh_of[k] == hh ? alpha[hh] : a;
-          m = hh_of[k] == hh ? m_all[hh] : m;
+        for (int k = 0; k < S::NVL; ++k) {
+          x = hh_of[k] == hh ? fmaxf(x, sc[k]) : x;
+          if constexpr (kFp8 && kPTH) y = hh_of[k] == hh ? fmaxf(y, sv[k]) : y;
         }
-        l_mine[k] *= a;
-        m_mine[k] = m;
+        const float mn = fmaxf(m_all[hh], wave_max(x));
+        const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_all[hh] - mn);
+        m_all[hh] = mn;
+        float beta = alpha;
+        if constexpr (kFp8 && kPTH) {
+          const float mvn = fmaxf(mv_all[hh], wave_max(y));
+          beta = mvn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mv_all[hh] - mvn);
+          mv_all[hh] = mvn;
+        }
+#pragma unroll
+        for (int dd = 0; dd < S::DPL; ++dd) acc[hh][dd] *= beta;
+#pragma unroll
+        for (int k = 0; k < S::NVL; ++k) {
+          if (hh_of[k] == hh) {
+            l_mine[k] *= alpha;
+            m_mine[k] = mn;
+            if constexpr (kFp8 && kPTH) mv_mine[k] = mv_all[hh];
+          }
+        }
       }
     }
 
     // ---- weights -> LDS --------------------------------------------------------
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    float* pf = reinterpret_cast<float*>(p_lds);
 #pragma unroll
     for (int k = 0; k < S::NVL; ++k) {
       const float p = __builtin_amdgcn_exp2f(sc[k] - m_mine[k]);
+      float w = p;
+      if constexpr (kFp8 && kPTH) w = __builtin_amdgcn_exp2f(sv[k] - mv_mine[k]);
       if (owner) {
         l_mine[k] += p;
-        pf[hh_of[k] * kPage + t_of[k]] = p * r.vsc[k];
+        if constexpr (kFp8)
+          reinterpret_cast<_Float16*>(w_lds)[hh_of[k] * kPage + t_of[k]] = (_Float16)w;
+        else
+          reinterpret_cast<float*>(w_lds)[hh_of[k] * kPage + t_of[k]] = w;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -358,162 +400,268 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- PV ----------------------------------------------------------------------
-    float vf[S::DPL][kPage];
+    if constexpr (kFp8) {
+      half2_t vh[S::DPL][kPage / 2];
 #pragma unroll
-    for (int dd = 0; dd < S::DPL; ++dd)
+      for (int dd = 0; dd < S::DPL; ++dd)
 #pragma unroll
-      for (int j = 0; j < kPage / 2; ++j) {
-        if constexpr (kFp8) {
-          const float2_t f = (j & 1) ? e4m3x2_to_f32x2<true>(r.vrw[dd][j / 2])
-                                     : e4m3x2_to_f32x2<false>(r.vrw[dd][j / 2]);
-          vf[dd][2 * j] = f.x;
-          vf[dd][2 * j + 1] = f.y;
-        } else {
-          vf[dd][2 * j] = bf16_bits_to_float(r.vrw[dd][j] & 0xFFFFu);
-          vf[dd][2 * j + 1] = bf16_bits_to_float(r.vrw[dd][j] >> 16);
+        for (int j = 0; j < kPage / 2; ++j)
+          vh[dd][j] = (j & 1)
+              ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.vr[dd][j / 2], 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.vr[dd][j / 2], 1.0f, false);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        half2_t wv[kPage / 2];
+        const uint4 w0 = *reinterpret_cast<const uint4*>(w_lds + hh * (kPage / 2));
+        const uint4 w1 = *reinterpret_cast<const uint4*>(w_lds + hh * (kPage / 2) + 4);
+        wv[0] = __builtin_bit_cast(half2_t, w0.x); wv[1] = __builtin_bit_cast(half2_t, w0.y);
+        wv[2] = __builtin_bit_cast(half2_t, w0.z); wv[3] = __builtin_bit_cast(half2_t, w0.w);
+        wv[4] = __builtin_bit_cast(half2_t, w1.x); wv[5] = __builtin_bit_cast(half2_t, w1.y);
+        wv[6] = __builtin_bit_cast(half2_t, w1.z); wv[7] = __builtin_bit_cast(half2_t, w1.w);
+#pragma unroll
+        for (int dd = 0; dd < S::DPL; ++dd) {
+          float x = acc[hh][dd];
+#pragma unroll
+          for (int j = 0; j < kPage / 2; ++j) x = __builtin_amdgcn_fdot2(wv[j], vh[dd][j], x, false);
+          acc[hh][dd] = x;
         }
       }
+    } else {
+      float vf[S::DPL][kPage];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float pw[kPage];
+      for (int dd = 0; dd < S::DPL; ++dd)
 #pragma unroll
-      for (int j = 0; j < kPage / 4; ++j) {
-        const float4 a = *reinterpret_cast<const float4*>(p_lds + hh * kPage + 4 * j);
-        pw[4 * j] = a.x; pw[4 * j + 1] = a.y; pw[4 * j + 2] = a.z; pw[4 * j + 3] = a.w;
-      }
+        for (int j = 0; j < kPage / 2; ++j) {
+          vf[dd][2 * j] = bf16_bits_to_float(r.vr[dd][j] & 0xFFFFu);
+          vf[dd][2 * j + 1] = bf16_bits_to_float(r.vr[dd][j] >> 16);
+        }
 #pragma unroll
-      for (int dd = 0; dd < S::DPL; ++dd) {
-        float x = acc[hh][dd];
+      for (int hh = 0; hh < G; ++hh) {
+        float pw[kPage];
 #pragma unroll
-        for (int t = 0; t < kPage; ++t) x = fmaf(pw[t], vf[dd][t], x);
-        acc[hh][dd] = x;
+        for (int j = 0; j < kPage / 4; ++j) {
+          const float4 x = *reinterpret_cast<const float4*>(w_lds + hh * kPage + 4 * j);
+          pw[4 * j] = x.x; pw[4 * j + 1] = x.y; pw[4 * j + 2] = x.z; pw[4 * j + 3] = x.w;
+        }
+#pragma unroll
+        for (int dd = 0; dd < S::DPL; ++dd) {
+          float x = acc[hh][dd];
+#pragma unroll
+          for (int t = 0; t < kPage; ++t) x = fmaf(pw[t], vf[dd][t], x);
+          acc[hh][dd] = x;
+        }
       }
     }
   };
 
-  // Ring of three page buffers, written out so every buffer is a named register
-  // set: two pages are in flight while the third is computed.
-  PageRegs ra, rb, rc;
-  load_page(pb, ra);
-  if (pb + 1 < pe) load_page(pb + 1, rb);
-  for (int i = pb; i < pe; i += 3) {
-    if (i + 2 < pe) load_page(i + 2, rc);
-    compute_page(i, ra);
-    if (i + 1 >= pe) break;
-    if (i + 3 < pe) load_page(i + 3, ra);
-    compute_page(i + 1, rb);
-    if (i + 2 >= pe) break;
-    if (i + 4 < pe) load_page(i + 4, rb);
-    compute_page(i + 2, rc);
+  // Ring of kRing page buffers, fully unrolled so every buffer is a named register
+  // set: kRing - 1 pages are in flight while one is computed.  The first loads go
+  // out before the query is quantised.
+  PageRegs ring[kRing];
+#pragma unroll
+  for (int r = 0; r < kRing - 1; ++r)
+    if (r < nwp) load_page(r, ring[r]);
+
+  // ---- query of the group: fused e4m3 quantisation (fp8) or plain bf16 ----------
+  // Every wave quantises the whole group into its own LDS copy, so only a wave-level
+  // barrier separates the writes from the reads (a workgroup barrier would also wait
+  // for the page loads already in flight).
+  {
+    uint32_t* q_lds = q_lds_all[wave];
+    const bool unit_q = a.q_scale == 1.0f;
+#pragma unroll
+    for (int u = 0; u < QPW; ++u) {
+      const int e = lane + u * kWave;
+      uint32_t val = qraw[u];
+      if constexpr (kFp8) {
+        // x / 1.0 == x exactly, so the division is skipped for a unit scale
+        const float x0 = bf16_bits_to_float(val & 0xFFFFu);
+        const float x1 = bf16_bits_to_float(val >> 16);
+        const uint32_t c0 = unit_q ? e4m3_encode(x0) : e4m3_quantize(x0, a.q_scale);
+        const uint32_t c1 = unit_q ? e4m3_encode(x1) : e4m3_quantize(x1, a.q_scale);
+        val = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16x2<false>(c0 | (c1 << 8)));
+      }
+      if (e < QW) q_lds[e] = val;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(q_lds + (hh * D + c * 16) / 2);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(q_lds + (hh * D + c * 16) / 2 + 4);
+      qv[hh][0] = x0.x; qv[hh][1] = x0.y; qv[hh][2] = x0.z; qv[hh][3] = x0.w;
+      qv[hh][4] = x1.x; qv[hh][5] = x1.y; qv[hh][6] = x1.z; qv[hh][7] = x1.w;
+    }
   }
 
-  // ---- split results --------------------------------------------------------------
-  float lh[G];
+  // Full steps: every step issues one page load (the index is clamped to the
+  // wave's last page, so the final steps re-read it instead of branching) and
+  // computes one page, so the loop body has no data-dependent branch around its
+  // loads and the wait counts stay exact.
+  int i0 = 0;
+  for (; i0 + kRing <= nwp; i0 += kRing) {
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+      load_page(min(i0 + r + kRing - 1, nwp - 1), ring[(r + kRing - 1) % kRing]);
+      compute_page(i0 + r, ring[r]);
+    }
+  }
+  // Remainder: fewer than kRing pages, all already loaded into slots 0 .. kRing-2.
+#pragma unroll
+  for (int r = 0; r < kRing - 1; ++r)
+    if (i0 + r < nwp) compute_page(i0 + r, ring[r]);
+
+  // ---- this wave's result relative to m_all: o = acc * f, l ------------------------
+  float lw[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     float x = 0.0f;
 #pragma unroll
     for (int k = 0; k < S::NVL; ++k) x += (owner && hh_of[k] == hh) ? l_mine[k] : 0.0f;
-    lh[hh] = wave_sum(x);
+    lw[hh] = wave_sum(x);
+    float f = kFp8 && !kPTH ? a.v_scale : 1.0f;
+    if constexpr (kFp8 && kPTH)
+      f = m_all[hh] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv_all[hh] - m_all[hh]);
+#pragma unroll
+    for (int dd = 0; dd < S::DPL; ++dd) acc[hh][dd] *= f;
   }
-  const int64_t out_row0 = (int64_t)b * num_q_heads + g * G;
-  if (ns == 1) {  // the only split: normalise and store directly
+
+  // ---- merge the four waves (level 3, fixed order) --------------------------------
+  if (lane == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float inv = lh[hh] > 0.0f ? 1.0f / lh[hh] : 0.0f;
+      ml_lds[wave][hh][0] = m_all[hh];
+      ml_lds[wave][hh][1] = lw[hh];
+    }
+  }
+  __syncthreads();
+  float M[G], Lsum[G];
 #pragma unroll
-      for (int dd = 0; dd < S::DPL; ++dd)
-        store_out(out, out_f32, (out_row0 + hh) * D + lane + kWave * dd, acc[hh][dd] * inv);
+  for (int hh = 0; hh < G; ++hh) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, ml_lds[w][hh][0]);
+    M[hh] = mx;
+    float ls = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      ls += ml_lds[w][hh][1] * exp2_or_zero(ml_lds[w][hh][0] == -INFINITY
+                                                ? -INFINITY : ml_lds[w][hh][0] - mx);
+    Lsum[hh] = ls;
+    const float f = m_all[hh] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_all[hh] - mx);
+#pragma unroll
+    for (int dd = 0; dd < S::DPL; ++dd) acc[hh][dd] *= f;
+  }
+  // tree: waves [h, 2h) hand their sums to waves [0, h)
+#pragma unroll
+  for (int half = kWaves / 2; half >= 1; half /= 2) {
+    if (wave >= half && wave < 2 * half) {
+      float* slot = merge_lds + (wave - half) * G * D;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int dd = 0; dd < S::DPL; ++dd) slot[hh * D + lane + kWave * dd] = acc[hh][dd];
+    }
+    __syncthreads();
+    if (wave < half) {
+      const float* slot = merge_lds + wave * G * D;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int dd = 0; dd < S::DPL; ++dd) acc[hh][dd] += slot[hh * D + lane + kWave * dd];
+    }
+    __syncthreads();
+  }
+
+  if (ns == 1) {  // the only split: normalise and store directly
+    if (wave == 0) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float inv = Lsum[hh] > 0.0f ? 1.0f / Lsum[hh] : 0.0f;
+#pragma unroll
+        for (int dd = 0; dd < S::DPL; ++dd)
+          store_out(a.out, a.out_f32, (row0 + hh) * D + lane + kWave * dd, acc[hh][dd] * inv);
+      }
     }
     return;
   }
-  // partials: o (unnormalised), m (log2 domain), l.  Stored as agent-scope atomics,
-  // i.e. written through to the device coherence point (the L2 of each XCD is not
-  // coherent with the others), so no L2 write-back is needed to publish them.
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const int64_t row = (out_row0 + hh) * splits + s;
-    if (lane == 0) {
-      store_agent(&ml_part[row * 2], m_all[hh]);
-      store_agent(&ml_part[row * 2 + 1], lh[hh]);
-    }
-#pragma unroll
-    for (int dd = 0; dd < S::DPL; ++dd)  // lane-major: this lane's channels adjacent
-      store_agent(&o_part[row * D + lane * S::DPL + dd], acc[hh][dd]);
-  }
-  // The last split of (b, g) to finish merges all of them (level 3 of the float32
-  // accumulation): wait until this wave's partials are performed, then count; the
-  // wave that completes the count reads the partials back with agent-scope loads
-  // and resets the counter for the next call.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // s_waitcnt vmcnt(0)
-  int done = 0;
-  if (lane == 0)
-    done = __hip_atomic_fetch_add(&counters[(int64_t)b * num_kv_heads + g], 1,
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  done = __builtin_amdgcn_readfirstlane(done);
-  if (done != ns - 1) return;
-  // Merge with many loads in flight: weights of up to 64 splits sit one per lane;
-  // partial rows are fetched kMergeBatch splits x G heads at a time.
-  constexpr int kMergeBatch = (G * S::DPL) >= 64 ? 1 : 64 / (G * S::DPL);
-  float M[G], lpart[G], o[G][S::DPL];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const int64_t row0 = (out_row0 + hh) * splits;
-    float mj = -INFINITY;
-    for (int j = lane; j < ns; j += kWave) mj = fmaxf(mj, load_agent(&ml_part[(row0 + j) * 2]));
-    M[hh] = wave_max(mj);
-    lpart[hh] = 0.0f;
-#pragma unroll
-    for (int dd = 0; dd < S::DPL; ++dd) o[hh][dd] = 0.0f;
-  }
-  for (int j0 = 0; j0 < ns; j0 += kWave) {
-    float w[G];  // lane x: weight of split j0 + x
+
+  // ---- split partial -> workspace; the last split of (b, g) merges them all ---------
+  // Partials are stored as agent-scope atomics, i.e. written through to the device
+  // coherence point (the L2 of each XCD is not coherent with the others); the wave
+  // then waits until they are performed before it counts itself done, and the last
+  // workgroup reads them back with agent-scope loads.
+  const int64_t prow = (int64_t)ug * a.splits;  // partial rows of (b, g)
+  if (wave == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const int64_t row = (out_row0 + hh) * splits + j0 + lane;
-      w[hh] = 0.0f;
-      if (j0 + lane < ns) {
-        const float m = load_agent(&ml_part[row * 2]);
-        w[hh] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M[hh]);
-        lpart[hh] += load_agent(&ml_part[row * 2 + 1]) * w[hh];
+      float* o = a.o_part + ((prow + s) * G + hh) * D;
+#pragma unroll
+      for (int dd = 0; dd < S::DPL; ++dd) store_agent(o + lane + kWave * dd, acc[hh][dd]);
+      if (lane == 0) {
+        store_agent(a.ml_part + ((prow + s) * G + hh) * 2, M[hh]);
+        store_agent(a.ml_part + ((prow + s) * G + hh) * 2 + 1, Lsum[hh]);
       }
     }
-    const int cnt = min(kWave, ns - j0);
-    for (int x0 = 0; x0 < cnt; x0 += kMergeBatch) {
-      float v[G][kMergeBatch][S::DPL];
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    int done = 0;
+    if (lane == 0)
+      done = __hip_atomic_fetch_add(&a.counters[ug], 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    done = __builtin_amdgcn_readfirstlane(done);
+    if (lane == 0) last_lds = done == ns - 1;
+  }
+  __syncthreads();
+  if (!last_lds) return;
+
+  // Level-3 merge over the ns splits, in split order, by all threads of the
+  // workgroup: thread t handles output elements t, t + 256, ...; every batch of
+  // splits is fetched with all its loads in flight at once.
+  constexpr int kEPT = (G * D + kThreads - 1) / kThreads;
+  constexpr int kBatch = 32 / kEPT > 2 ? 32 / kEPT : 2;
+  float Mx[kEPT], lsum[kEPT], osum[kEPT];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh)
+  for (int x = 0; x < kEPT; ++x) {
+    Mx[x] = -INFINITY;
+    lsum[x] = 0.0f;
+    osum[x] = 0.0f;
+  }
+  for (int j0 = 0; j0 < ns; j0 += kBatch) {
+    float mv[kEPT][kBatch], lv[kEPT][kBatch], ov[kEPT][kBatch];
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) {
-          const int x = min(x0 + u, cnt - 1);  // clamped rows get weight 0 below
-          const int64_t row = (out_row0 + hh) * splits + j0 + x;
+    for (int x = 0; x < kEPT; ++x) {
+      const int e = min(tid + x * kThreads, G * D - 1);
+      const int hh = e / D;
 #pragma unroll
-          for (int dd = 0; dd < S::DPL; ++dd)
-            v[hh][u][dd] = load_agent(&o_part[row * D + lane * S::DPL + dd]);
-        }
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) {
-          const float wx = x0 + u < cnt ? __int_as_float(__builtin_amdgcn_readlane(
-                                              __float_as_int(w[hh]), x0 + u))
-                                        : 0.0f;
-#pragma unroll
-          for (int dd = 0; dd < S::DPL; ++dd) o[hh][dd] += v[hh][u][dd] * wx;
-        }
+      for (int u = 0; u < kBatch; ++u) {
+        const int j = min(j0 + u, ns - 1);
+        mv[x][u] = load_agent(a.ml_part + ((prow + j) * G + hh) * 2);
+        lv[x][u] = load_agent(a.ml_part + ((prow + j) * G + hh) * 2 + 1);
+        ov[x][u] = load_agent(a.o_part + (prow + j) * G * D + e);
+      }
     }
+#pragma unroll
+    for (int x = 0; x < kEPT; ++x)
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (j0 + u >= ns || mv[x][u] == -INFINITY) continue;
+        const float mn = fmaxf(Mx[x], mv[x][u]);
+        const float fa = exp2_or_zero(Mx[x] == -INFINITY ? -INFINITY : Mx[x] - mn);
+        const float fb = __builtin_amdgcn_exp2f(mv[x][u] - mn);
+        osum[x] = osum[x] * fa + ov[x][u] * fb;
+        lsum[x] = lsum[x] * fa + lv[x][u] * fb;
+        Mx[x] = mn;
+      }
   }
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const float lsum = wave_sum(lpart[hh]);
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-#pragma unroll
-    for (int dd = 0; dd < S::DPL; ++dd)
-      store_out(out, out_f32, (out_row0 + hh) * D + lane + kWave * dd, o[hh][dd] * inv);
+  for (int x = 0; x < kEPT; ++x) {
+    const int e = tid + x * kThreads;
+    if (e < G * D)
+      store_out(a.out, a.out_f32, row0 * D + e, lsum[x] > 0.0f ? osum[x] / lsum[x] : 0.0f);
   }
-  if (lane == 0)
-    __hip_atomic_store(&counters[(int64_t)b * num_kv_heads + g], 0, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0)
+    __hip_atomic_store(&a.counters[ug], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- host side ----------------------------------------------------------------------
@@ -525,16 +673,15 @@ static int max_visible_pages(int32_t max_seq_len, int32_t window) {
   return all < win ? all : win;
 }
 
-// Pages per split: enough splits to put ~16 waves on each of the 256 CUs, each
-// split between 4 and 64 pages.
+// Pages per split: enough splits that the grid fills the GPU with resident
+// workgroups (kTargetWorkgroups), each wave getting at least two pages.
 static int auto_pages_per_split(int32_t num_seqs, int32_t num_kv_heads, int max_pages) {
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  if (units <= 0 || max_pages <= 0) return 4;
-  const int64_t target_waves = 256 * 16;
-  int64_t splits = (target_waves + units - 1) / units;
+  if (units <= 0 || max_pages <= 0) return 2 * kWaves;
+  int64_t splits = (kTargetWorkgroups + units - 1) / units;
   if (splits < 1) splits = 1;
   int64_t pps = (max_pages + splits - 1) / splits;
-  if (pps < 4) pps = 4;
+  if (pps < 2 * kWaves) pps = 2 * kWaves;
   if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
   return (int)pps;
 }
@@ -573,52 +720,40 @@ static kvq_status plan_decode(const kvq_cache_desc* cache, int32_t num_seqs,
   // at least one split: an all-empty batch still needs its zero output rows
   plan->splits = mp > 0 ? (mp + plan->pps - 1) / plan->pps : 1;
   plan->counter_bytes = counter_area_bytes(num_seqs, cache->num_kv_heads);
-  plan->bytes = plan->counter_bytes + (size_t)num_seqs * num_q_heads * plan->splits *
-                                          (cache->head_dim + 2) * sizeof(float);
+  plan->bytes = plan->splits > 1
+                    ? plan->counter_bytes + (size_t)num_seqs * num_q_heads * plan->splits *
+                                                (cache->head_dim + 2) * sizeof(float)
+                    : 0;
   return KVQ_OK;
 }
 
 template <int D, int G, bool kFp8, bool kPTH>
-static void launch_split(const kvq_cache_desc* c, const void* q, int32_t B,
-                         const DecodePlan& pl, const int32_t* bt, int32_t bts,
-                         const int32_t* sl, const kvq_scales* sc, float sm_log2,
-                         int32_t window, float* o_part, float* ml_part, int32_t* counters,
-                         void* out, int32_t out_f32, hipStream_t st) {
-  const int64_t waves = (int64_t)B * c->num_kv_heads * pl.splits;
-  const unsigned blocks = (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
-  decode_split_kernel<D, G, kFp8, kPTH><<<blocks, 256, 0, st>>>(
-      static_cast<const uint16_t*>(q), B, c->num_kv_heads, pl.splits, pl.pps, bt, bts, sl,
-      static_cast<const uint8_t*>(c->k_pages), static_cast<const uint8_t*>(c->v_pages),
-      c->k_scales, c->v_scales, sc ? sc->q_scale : 1.f, sc ? sc->k_scale : 1.f,
-      sc ? sc->v_scale : 1.f, sm_log2, window, o_part, ml_part, counters, out, out_f32);
+static void launch(const DecodeArgs& args, int32_t B, int32_t Hkv, const DecodePlan& pl,
+                   hipStream_t st) {
+  const unsigned blocks = (unsigned)((int64_t)B * Hkv * pl.splits);
+  decode_kernel<D, G, kFp8, kPTH, kDecodeRing><<<blocks, kThreads, 0, st>>>(args);
 }
 
 template <int D, int G>
-static void dispatch_dtype(const kvq_cache_desc* c, const void* q, int32_t B,
-                           const DecodePlan& pl, const int32_t* bt, int32_t bts,
-                           const int32_t* sl, const kvq_scales* sc, float sm_log2,
-                           int32_t window, float* o, float* ml, int32_t* cnt, void* out,
-                           int32_t f32, hipStream_t st) {
+static void dispatch_dtype(const kvq_cache_desc* c, const DecodeArgs& args, int32_t B,
+                           const DecodePlan& pl, hipStream_t st) {
   if (c->dtype == KVQ_BF16)
-    launch_split<D, G, false, false>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st);
+    launch<D, G, false, false>(args, B, c->num_kv_heads, pl, st);
   else if (c->mode == KVQ_SCALE_PER_TOKEN_HEAD)
-    launch_split<D, G, true, true>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st);
+    launch<D, G, true, true>(args, B, c->num_kv_heads, pl, st);
   else
-    launch_split<D, G, true, false>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st);
+    launch<D, G, true, false>(args, B, c->num_kv_heads, pl, st);
 }
 
 template <int D>
-static void dispatch_group(int G, const kvq_cache_desc* c, const void* q, int32_t B,
-                           const DecodePlan& pl, const int32_t* bt, int32_t bts,
-                           const int32_t* sl, const kvq_scales* sc, float sm_log2,
-                           int32_t window, float* o, float* ml, int32_t* cnt, void* out,
-                           int32_t f32, hipStream_t st) {
+static void dispatch_group(int G, const kvq_cache_desc* c, const DecodeArgs& args, int32_t B,
+                           const DecodePlan& pl, hipStream_t st) {
   switch (G) {
-    case 1: dispatch_dtype<D, 1>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st); break;
-    case 2: dispatch_dtype<D, 2>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st); break;
-    case 4: dispatch_dtype<D, 4>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st); break;
-    case 8: dispatch_dtype<D, 8>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st); break;
-    case 16: dispatch_dtype<D, 16>(c, q, B, pl, bt, bts, sl, sc, sm_log2, window, o, ml, cnt, out, f32, st); break;
+    case 1: dispatch_dtype<D, 1>(c, args, B, pl, st); break;
+    case 2: dispatch_dtype<D, 2>(c, args, B, pl, st); break;
+    case 4: dispatch_dtype<D, 4>(c, args, B, pl, st); break;
+    case 8: dispatch_dtype<D, 8>(c, args, B, pl, st); break;
+    case 16: dispatch_dtype<D, 16>(c, args, B, pl, st); break;
   }
 }
 
@@ -677,16 +812,36 @@ extern "C" kvq_status kvq_decode_attention(
   const int D = cache->head_dim;
   const int G = num_q_heads / cache->num_kv_heads;
   const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)D);
-  const float sm_log2 = sm * kLog2e;
-  int32_t* counters = static_cast<int32_t*>(workspace);
-  float* o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.counter_bytes);
-  float* ml_part = o_part + (size_t)num_seqs * num_q_heads * pl.splits * D;
-  const int f32 = out_dtype == KVQ_F32;
+  DecodeArgs args;
+  args.q = static_cast<const uint16_t*>(q);
+  args.num_kv_heads = cache->num_kv_heads;
+  args.splits = pl.splits;
+  args.pps = pl.pps;
+  args.block_table = block_table;
+  args.bt_stride = block_table_stride;
+  args.seq_lens = seq_lens;
+  args.k_pages = static_cast<const uint8_t*>(cache->k_pages);
+  args.v_pages = static_cast<const uint8_t*>(cache->v_pages);
+  args.k_scales = cache->k_scales;
+  args.v_scales = cache->v_scales;
+  args.q_scale = scales ? scales->q_scale : 1.0f;
+  args.k_scale = scales ? scales->k_scale : 1.0f;
+  args.v_scale = scales ? scales->v_scale : 1.0f;
+  args.sm_log2 = sm * kLog2e;
+  args.window = window;
+  args.counters = pl.bytes ? static_cast<int32_t*>(workspace) : nullptr;
+  args.o_part = pl.bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                    pl.counter_bytes)
+                         : nullptr;
+  args.ml_part = pl.bytes ? args.o_part + (size_t)num_seqs * num_q_heads * pl.splits * D
+                          : nullptr;
+  args.out = out;
+  args.out_f32 = out_dtype == KVQ_F32;
   auto st = static_cast<hipStream_t>(stream);
   switch (D) {
-    case 64: dispatch_group<64>(G, cache, q, num_seqs, pl, block_table, block_table_stride, seq_lens, scales, sm_log2, window, o_part, ml_part, counters, out, f32, st); break;
-    case 128: dispatch_group<128>(G, cache, q, num_seqs, pl, block_table, block_table_stride, seq_lens, scales, sm_log2, window, o_part, ml_part, counters, out, f32, st); break;
-    case 256: dispatch_group<256>(G, cache, q, num_seqs, pl, block_table, block_table_stride, seq_lens, scales, sm_log2, window, o_part, ml_part, counters, out, f32, st); break;
+    case 64: dispatch_group<64>(G, cache, args, num_seqs, pl, st); break;
+    case 128: dispatch_group<128>(G, cache, args, num_seqs, pl, st); break;
+    case 256: dispatch_group<256>(G, cache, args, num_seqs, pl, st); break;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch: %s", hipGetErrorString(e));

@@ -102,10 +102,20 @@ def test_split_count_invariance_and_determinism(kvq):
     case = workloads.make_decode_case(62, [2000, 777], 32, 8, 128, table="perm", outliers=4)
     c = write_cache(kvq, case, "fp8", "per_token_head")
     base = run_decode(kvq, c, case, "per_token_head", pps=4)
+    # Between split counts the float32 summation order changes, and so does each
+    # wave's softmax reference maximum, against which the PV weights are rounded to
+    # f16 (unit roundoff 2^-11).  Two such roundings of the weights of
+    # o = sum_j w_j v_j / sum_j w_j differ by at most 2 * 2^-11 * sum_j w_j |v_j| /
+    # sum_j w_j, i.e. twice the attention output over |v|, which the oracle gives.
+    pools = oracle_pools(case, "per_token_head")
+    _, qh = ocache.quantize_q(case.q, 1.0)
+    abs_out = attention.decode(qh, ocache.dequantized(pools, "k"),
+                               np.abs(ocache.dequantized(pools, "v")), case.block_table,
+                               case.seq_lens)
+    bound = 1e-5 + 1e-5 * np.abs(base) + 2.0 ** -10 * abs_out
     for pps in (1, 7, 16, 64, 0):
         other = run_decode(kvq, c, case, "per_token_head", pps=pps)
-        # only the float32 summation order changes between split counts
-        assert np.all(np.abs(other - base) <= 1e-4 + 1e-5 * np.abs(base)), pps
+        assert np.all(np.abs(other - base) <= bound), pps
     again = [run_decode(kvq, c, case, "per_token_head", pps=16) for _ in range(5)]
     for a in again[1:]:
         assert np.array_equal(a, again[0])
