@@ -181,8 +181,9 @@ kvq_status kvq_quantize_fp8(const void* x, int64_t n, float scale, uint8_t* code
 /*
  * Workspace bytes needed by kvq_decode_attention for these arguments: completion
  * counters (int32 per (sequence, KV head), 256-byte padded) followed by the split-K
- * partial results.  pages_per_split = 0 selects the library's choice, which depends
- * only on the arguments given here.  bytes [host].
+ * partial results; 0 when every sequence fits in one split (then no workspace is
+ * read or written).  pages_per_split = 0 selects the library's choice, which
+ * depends only on the arguments given here; otherwise 1..256.  bytes [host].
  */
 kvq_status kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t max_seq_len,

@@ -120,7 +120,7 @@ def test_decode_workspace_and_checks():
     assert n.value == 256 + 8 * 32 * 3 * 130 * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 24, 20000, 0, 0, ctypes.byref(n)) == kvq.binding.ERR_UNSUPPORTED
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 33, 20000, 0, 0, ctypes.byref(n)) == kvq.binding.ERR_INVALID_ARG
-    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 32, 20000, 0, 65, ctypes.byref(n)) == kvq.binding.ERR_INVALID_ARG
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 32, 20000, 0, 257, ctypes.byref(n)) == kvq.binding.ERR_INVALID_ARG
     sc = kvq.Scales(1.0, 1.0, 1.0, 1.0)
     args = lambda ws, wsb, outdt=kvq.BF16, q=4096, scales=ctypes.byref(sc): (
         ctypes.byref(d), q, 8, 32, 4096, 1250, 4096, 20000, scales, 0, 0.0, 10, 4096,
