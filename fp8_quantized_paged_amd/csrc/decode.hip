@@ -341,10 +341,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < S::NVL; ++k) {
       const int pos = lpage * kPage + t_of[k];
-      sc[k] = (pos >= lo && pos < L) ? sc[k] * (qk_base * r.ksc[k]) : -INFINITY;
+      const bool vis = pos >= lo && pos < L;
+      sc[k] = vis ? sc[k] * (qk_base * r.ksc[k]) : -INFINITY;
       over |= sc[k] > m_mine[k] + kRescaleSlack;
       if constexpr (kFp8 && kPTH) {
-        sv[k] = sc[k] + log2f(r.vsc[k]);
+        // masked slots may hold unwritten scales: never take their logarithm
+        sv[k] = vis ? sc[k] + log2f(r.vsc[k]) : -INFINITY;
         over |= sv[k] > mv_mine[k] + kRescaleSlack;
       }
     }
@@ -400,6 +402,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- PV ----------------------------------------------------------------------
+    // Slots past the sequence end (last page only) were never written: their bytes
+    // may be any code, NaN included, and a zero weight times NaN is NaN.
+    uint32_t vw[S::DPL][S::VW];
+#pragma unroll
+    for (int dd = 0; dd < S::DPL; ++dd)
+#pragma unroll
+      for (int j = 0; j < S::VW; ++j) vw[dd][j] = r.vr[dd][j];
+    const int valid = L - lpage * kPage;  // wave-uniform
+    if (valid < kPage) {
+      constexpr int TPW = 4 / S::EB;  // tokens per V word
+#pragma unroll
+      for (int j = 0; j < S::VW; ++j) {
+        const int keep = min(max(valid - TPW * j, 0), TPW);
+        const uint32_t msk = keep >= TPW ? 0xFFFFFFFFu : ((1u << (8 * S::EB * keep)) - 1u);
+#pragma unroll
+        for (int dd = 0; dd < S::DPL; ++dd) vw[dd][j] &= msk;
+      }
+    }
     if constexpr (kFp8) {
       half2_t vh[S::DPL][kPage / 2];
 #pragma unroll
@@ -407,8 +427,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < kPage / 2; ++j)
           vh[dd][j] = (j & 1)
-              ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.vr[dd][j / 2], 1.0f, true)
-              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.vr[dd][j / 2], 1.0f, false);
+              ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vw[dd][j / 2], 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vw[dd][j / 2], 1.0f, false);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         half2_t wv[kPage / 2];
@@ -432,8 +452,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
       for (int dd = 0; dd < S::DPL; ++dd)
 #pragma unroll
         for (int j = 0; j < kPage / 2; ++j) {
-          vf[dd][2 * j] = bf16_bits_to_float(r.vr[dd][j] & 0xFFFFu);
-          vf[dd][2 * j + 1] = bf16_bits_to_float(r.vr[dd][j] >> 16);
+          vf[dd][2 * j] = bf16_bits_to_float(vw[dd][j] & 0xFFFFu);
+          vf[dd][2 * j + 1] = bf16_bits_to_float(vw[dd][j] >> 16);
         }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {

@@ -41,17 +41,24 @@ def gather(pool, block_table_row, n_tokens: int) -> np.ndarray:
     return pool[pages, :, j % PAGE_SIZE, :]
 
 
-def attend_rows(q, k, v, lo, hi, sm_scale: float) -> np.ndarray:
+def attend_rows(q, k, v, lo, hi, sm_scale: float, spread: bool = False):
     """Softmax attention of query rows q [R][D] over rows k, v [L][D].
 
     Row r sees keys lo[r] .. hi[r] inclusive; an empty range gives zeros.
+
+    With ``spread`` also returns, per row and channel, the attention-weighted mean
+    absolute deviation of V from the output, sum_j w_j |v_j - o|: the amount by
+    which the output moves per unit of relative error in the weights (if every
+    weight w_j becomes w_j (1 + e_j) with |e_j| <= r, renormalised, the output
+    moves by at most r / (1 - r) times this).
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     out = np.zeros((q.shape[0], v.shape[1]), np.float64)
+    dev = np.zeros_like(out)
     if k.shape[0] == 0:
-        return out
+        return (out, dev) if spread else out
     s = (q @ k.T) * sm_scale                      # [R][L]
     j = np.arange(k.shape[0])[None, :]
     vis = (j >= np.asarray(lo)[:, None]) & (j <= np.asarray(hi)[:, None])
@@ -63,7 +70,11 @@ def attend_rows(q, k, v, lo, hi, sm_scale: float) -> np.ndarray:
     l = p.sum(axis=1, keepdims=True)
     o = (p @ v) / np.where(l > 0, l, 1.0)
     out[ok] = o[ok]
-    return out
+    if not spread:
+        return out
+    for r in np.nonzero(ok)[0]:
+        dev[r] = (p[r] @ np.abs(v - o[r])) / l[r, 0]
+    return out, dev
 
 
 def default_sm_scale(head_dim: int) -> float:
@@ -103,12 +114,14 @@ def decode(q, k_pool, v_pool, block_table, seq_lens, window: int = 0,
 
 
 def prefill(q, cu_q_lens, k_pool, v_pool, block_table, seq_lens, causal: bool = True,
-            window: int = 0, sm_scale: float | None = None, rows=None) -> np.ndarray:
+            window: int = 0, sm_scale: float | None = None, rows=None,
+            spread: bool = False):
     """Chunked-prefill attention.  q [Nq][Hq][D] holds the new queries of all
     sequences back to back (sequence b owns rows cu_q_lens[b] .. cu_q_lens[b+1]-1).
 
     Returns float64 [Nq][Hq][D].  ``rows`` optionally restricts the work to a sorted
-    list of query row indices (other rows stay zero).
+    list of query row indices (other rows stay zero).  With ``spread`` also returns
+    attend_rows' weighted mean absolute deviation of V, same shape.
     """
     q = np.asarray(q, np.float64)
     Nq, Hq, D = q.shape
@@ -116,6 +129,7 @@ def prefill(q, cu_q_lens, k_pool, v_pool, block_table, seq_lens, causal: bool = 
     G = Hq // Hkv
     sm = default_sm_scale(D) if sm_scale is None else sm_scale
     out = np.zeros((Nq, Hq, D), np.float64)
+    dev = np.zeros_like(out)
     for b in range(len(seq_lens)):
         r0, r1 = int(cu_q_lens[b]), int(cu_q_lens[b + 1])
         n, L = r1 - r0, int(seq_lens[b])
@@ -133,5 +147,9 @@ def prefill(q, cu_q_lens, k_pool, v_pool, block_table, seq_lens, causal: bool = 
         v = gather(v_pool, block_table[b], L)
         for h in range(Hq):
             g = h // G
-            out[idx, h] = attend_rows(q[idx, h], k[:, g], v[:, g], lo, hi, sm)
-    return out
+            res = attend_rows(q[idx, h], k[:, g], v[:, g], lo, hi, sm, spread)
+            if spread:
+                out[idx, h], dev[idx, h] = res
+            else:
+                out[idx, h] = res
+    return (out, dev) if spread else out

@@ -256,6 +256,32 @@ def test_prefill_brute_force_rows():
                 assert np.allclose(out[i, h], ref, atol=1e-12, rtol=0)
 
 
+def test_spread_brute_force_and_special_cases():
+    """sum_j w_j |v_j - o| against pure-Python loops; one visible key gives 0; equal
+    scores give the plain mean absolute deviation of V about its mean."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((3, 6))
+    k = rng.standard_normal((9, 6))
+    v = rng.standard_normal((9, 6))
+    lo, hi = [0, 2, 4], [8, 5, 4]
+    out, dev = attention.attend_rows(q, k, v, lo, hi, 0.5, spread=True)
+    for r in range(3):
+        js = range(lo[r], hi[r] + 1)
+        s = [0.5 * sum(q[r, d] * k[j, d] for d in range(6)) for j in js]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        tot = sum(w)
+        o = [sum(wi * v[j, d] for wi, j in zip(w, js)) / tot for d in range(6)]
+        ref = [sum(wi * abs(v[j, d] - o[d]) for wi, j in zip(w, js)) / tot
+               for d in range(6)]
+        assert np.allclose(out[r], o, atol=1e-13, rtol=0)
+        assert np.allclose(dev[r], ref, atol=1e-13, rtol=0)
+    assert np.all(dev[2] == 0.0)                     # a single visible key
+    _, dev_eq = attention.attend_rows(np.zeros((1, 6)), k, v, [0], [8], 1.0, spread=True)
+    assert np.allclose(dev_eq[0], np.mean(np.abs(v - v.mean(axis=0)), axis=0),
+                       atol=1e-14, rtol=0)
+
+
 # ---- mutation tests -------------------------------------------------------------
 
 def test_mutants_are_caught():
