@@ -1,23 +1,27 @@
-"""Benchmark: FP8 paged decode attention on the Llama-3.1-8B-shaped decode layer.
+"""Benchmark: FP8 paged attention hot path on one MI355X.
 
-Workload (one "step" = the whole decode hot path for one batch): 8 sequences of
-20,000 tokens, 32 query / 8 KV heads, head_dim 128, page size 16, block table a
-seeded permutation of all 10,000 pages, K/V bf16 N(0,1) with 4 outlier channels per
-KV head scaled x20, fp8 e4m3 cache with per-token-head scales.  Each step writes
-the 8 current tokens through the quantising cache write, then runs the split-K
+Headline (the JSON line's `value`): the Llama-3.1-8B-shaped decode layer — 8
+sequences of 20,000 tokens, 32 query / 8 KV heads, head_dim 128, page size 16, block
+table a seeded permutation of all 10,000 pages, K/V bf16 N(0,1) with 4 outlier
+channels per KV head scaled x20, fp8 e4m3 cache with per-token-head scales.  One step
+writes the 8 current tokens through the quantising cache write, then runs the split-K
 decode (fused query quantisation and split merge) over all 20,000 keys of every
 sequence.  Inputs are resident in HBM before timing starts; steps rotate over four
-independent cache copies (4 x 338 MB) so the 256 MB Infinity Cache cannot serve a
-step from the previous one.
+independent cache copies (4 x 338 MB) so the 256 MB Infinity Cache cannot serve a step
+from the previous one.  `value` = algorithmic bytes of the step / step time (GB/s).
 
-Prints ONE JSON line.  `value` = algorithmic bytes of the step / measured step time
-(GB/s).  `roofline` covers the decode kernel alone (HIP events around each decode
-launch, on the stream it runs on).  `cpu_baseline` times the CPU oracle (float64)
-on a bounded sample of the same step (a subset of the sequences).
+`roofline` covers the decode kernel alone (HIP events around each decode launch, on the
+stream it runs on).  Further legs, each timed the same way, are reported beside it:
+the bf16-cache baseline of the same layer, the tiny decode, the 131,072-token decode,
+the 24-layer gpt-oss-20b-shaped hybrid step (12 fp8 full layers + 12 bf16 window-128
+layers, cache writes included) and the head_dim-256 chunked prefill (FP8 matrix cores,
+`roofline` against the dense FP8 peak).  `cpu_baseline` times the CPU oracle (float64)
+on the headline step's inputs.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -27,9 +31,13 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, AMD published
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, AMD published
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 matrix throughput, AMD published
 METRIC = "fp8 paged decode attention: HBM GB/s (% of peak), µs/step at 8×20k ctx"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_llama8b_traffic.json")
+DECODE_KERNEL = "decode_kernel"
+COPY_BYTES = 1 << 30
+LEGS = ("decode", "bf16", "tiny", "long", "hybrid", "prefill")
 
 
 def parse():
@@ -38,25 +46,49 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rotate", type=int, default=4, help="independent cache copies")
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help=f"comma-separated subset of {LEGS}; 'decode' is the headline")
     ap.add_argument("--cpu-seqs", type=int, default=8,
                     help="sequences in the oracle's timed sample (0 = skip)")
     ap.add_argument("--cpu-reps", type=int, default=2,
                     help="repetitions of the oracle's timed sample")
-    ap.add_argument("--no-bf16", action="store_true", help="skip the bf16-cache leg")
     ap.add_argument("--copy-calib", action="store_true",
-                    help="also run a plain 1 GiB device copy (counter calibration)")
+                    help=f"also run a plain {COPY_BYTES >> 20} MiB device copy (counter "
+                         "calibration for the HBM traffic figures)")
+    ap.add_argument("--traffic-from", default="",
+                    help="FETCH_SIZE,WRITE_SIZE rocprofv3 --pmc output directories (csv): "
+                         "write the decode kernel's measured HBM bytes per launch to "
+                         "profiles/ and exit (no GPU needed)")
     return ap.parse_args()
 
 
-def step_bytes(B, L, Hkv, Hq, D, scale_bytes):
-    """Algorithmic bytes.  decode: per (token, KV head) D K codes + D V codes + K/V
-    scales; plus q and out (bf16) and the block table.  write: per new (token, head)
-    read 2D bf16 values x2 (K, V), write D codes x2 and the scales."""
-    pages = (L + 15) // 16
-    dec = B * L * Hkv * (2 * D + scale_bytes) + 2 * (B * Hq * D * 2) + B * pages * 4
-    wr = B * Hkv * (2 * 2 * D + 2 * D + scale_bytes)
-    return dec, wr
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
 
+
+# ---- algorithmic work -------------------------------------------------------------------
+
+def decode_bytes(B, L, Hkv, Hq, D, elem, scale_bytes, window=0):
+    """Bytes a decode launch must move: per visible (token, KV head) 2D code bytes (or
+    4D for bf16) and the per-token scales, plus q and out (bf16) and the block-table
+    entries of the visible pages."""
+    vis = min(L, window) if window > 0 else L
+    pages = (vis + 15) // 16 + (1 if window > 0 else 0)
+    return (B * vis * Hkv * (2 * D * elem + scale_bytes) + 2 * (B * Hq * D * 2)
+            + B * min(pages, (L + 15) // 16) * 4)
+
+
+def write_bytes(T, Hkv, D, elem, scale_bytes):
+    """Cache write of T new tokens: read K and V (bf16), write the codes and scales."""
+    return T * Hkv * (2 * 2 * D + 2 * D * elem + scale_bytes)
+
+
+def prefill_flops(ctx, new, Hq, D):
+    """4 D flops (QK^T and PV multiply-adds) per (query row, visible key, query head)."""
+    return 4.0 * D * Hq * sum(ctx + i + 1 for i in range(new))
+
+
+# ---- measured traffic (rocprofv3 --pmc) ---------------------------------------------------
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
@@ -66,8 +98,8 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic():
-    """HBM bytes per decode launch from the committed counter profile, if it was
-    taken on the current kernel source; else None."""
+    """HBM bytes per decode launch from the committed counter profile, if it was taken
+    on the current kernel source; else None."""
     try:
         prof = json.load(open(PROFILE_TRAFFIC))
     except (OSError, ValueError):
@@ -76,6 +108,57 @@ def measured_traffic():
         return None
     return prof.get("bytes_per_launch")
 
+
+def _counter_rows(directory):
+    import csv
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
+                          recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no *counter_collection.csv under {directory}")
+    return rows
+
+
+def _per_dispatch(rows, counter, name_part):
+    vals = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter or name_part not in r.get("Kernel_Name", ""):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def write_traffic_profile(fetch_dir, write_dir):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the decode kernel, scaled by what
+    the same counters read for the plain 1 GiB device copy (the runtime's copy kernel),
+    averaged over dispatches."""
+    import statistics
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    dec_f = _per_dispatch(fr, "FETCH_SIZE", DECODE_KERNEL)
+    dec_w = _per_dispatch(wr, "WRITE_SIZE", DECODE_KERNEL)
+    # the calibration copy is the largest copy dispatch (others are small staging copies)
+    cp_f = _per_dispatch(fr, "FETCH_SIZE", "copy")
+    cp_w = _per_dispatch(wr, "WRITE_SIZE", "copy")
+    if not (dec_f and dec_w and cp_f and cp_w):
+        raise SystemExit("decode or copy dispatches missing in the counter files")
+    f_scale = COPY_BYTES / (max(cp_f) * 1024.0)
+    w_scale = COPY_BYTES / (max(cp_w) * 1024.0)
+    fetch = statistics.mean(dec_f) * 1024.0 * f_scale
+    write = statistics.mean(dec_w) * 1024.0 * w_scale
+    prof = {"kernel": DECODE_KERNEL, "kernel_source_hash": kernel_source_hash(),
+            "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+            "bytes_per_launch": round(fetch + write),
+            "fetch_scale_from_copy": f_scale, "write_scale_from_copy": w_scale,
+            "dispatches": [len(dec_f), len(dec_w)]}
+    with open(PROFILE_TRAFFIC, "w") as f:
+        json.dump(prof, f, indent=1)
+    print(json.dumps(prof))
+
+
+# ---- CPU baseline -------------------------------------------------------------------------
 
 def cpu_baseline(case, nseq, reps=1):
     """Time the oracle on the step restricted to ``nseq`` sequences: quantise the new
@@ -108,47 +191,88 @@ def cpu_baseline(case, nseq, reps=1):
             attention.decode(qh, ocache.dequantized(pools, "k"),
                              ocache.dequantized(pools, "v"), bt, np.array([L]))
     dt = (time.perf_counter() - t0) / reps
-    dec, wr = step_bytes(nseq, L, Hkv, case.num_q_heads, D, 8)
+    dec = decode_bytes(nseq, L, Hkv, case.num_q_heads, D, 1, 8)
+    wr = write_bytes(nseq, Hkv, D, 1, 8)
     try:
         from threadpoolctl import threadpool_info
         blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         blas = None
     cores = len(os.sched_getaffinity(0))
-    return {"value": (dec + wr) / dt / 1e9, "unit": "GB/s", "cores": cores,
-            "kind": "oracle", "seconds": dt, "blas_threads": blas,
+    return {"value": round((dec + wr) / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 4), "blas_threads": blas,
             "sample": f"{nseq} of {B} sequences of one decode step (same inputs: new-token "
                       f"cache write, q quantisation, cache read, float64 attention), mean "
                       f"of {reps} runs; value = their algorithmic bytes / oracle seconds"}
 
 
+# ---- GPU legs -------------------------------------------------------------------------------
+
+class Timer:
+    """HIP events on torch's current stream, which is the stream libkvq launches on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in ev]  # µs
+
+
+def stats(us):
+    import numpy as np
+    return {"us_mean": round(float(np.mean(us)), 2), "us_median": round(float(np.median(us)), 2),
+            "us_p10_p90": [round(float(np.percentile(us, 10)), 2),
+                           round(float(np.percentile(us, 90)), 2)]}
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        fetch_dir, write_dir = args.traffic_from.split(",")
+        write_traffic_profile(fetch_dir, write_dir)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build "
               "has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
+    legs = [x for x in args.legs.split(",") if x]
+    for x in legs:
+        if x not in LEGS:
+            sys.exit(f"unknown leg {x!r}; choose from {LEGS}")
     import numpy as np
     import torch
 
     import fp8_quantized_paged_amd as kvq
     import workloads
 
-    def log(*a):
-        print(*a, file=sys.stderr, flush=True)
-
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    case = workloads.llama8b_decode()
-    B, Hq, D = case.q.shape
-    Hkv = case.num_kv_heads
-    L = int(case.seq_lens[0])
-    log(f"bench: workload generated (B={B} L={L} Hq={Hq} Hkv={Hkv} D={D})")
+    timer = Timer(torch)
 
     def to_dev(x):
         bits = workloads.bf16_bits(x).view(np.int16)
         return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).to(dev)
 
+    ones = kvq.Scales(1.0, 1.0, 1.0, 1.0)
+    result = {}
+
+    # ---- headline: Llama-shaped decode layer --------------------------------------------
+    case = workloads.llama8b_decode()
+    B, Hq, D = case.q.shape
+    Hkv = case.num_kv_heads
+    L = int(case.seq_lens[0])
+    log(f"bench: llama-shaped workload generated (B={B} L={L} Hq={Hq} Hkv={Hkv} D={D})")
     last = case.last_token_rows()
     hist = np.setdiff1d(np.arange(len(case.k)), last)
     q = to_dev(case.q)
@@ -156,11 +280,9 @@ def main():
     slots_new = torch.from_numpy(case.slots[last].astype(np.int64)).to(dev)
     bt = torch.from_numpy(case.block_table).to(dev)
     sl = torch.from_numpy(case.seq_lens).to(dev)
-    scales = kvq.Scales(1.0, 1.0, 1.0, 1.0)
 
-    def build_caches(dtype, n):
-        caches = [kvq.PagedCache(case.num_pages, Hkv, D, dtype, "per_token_head")
-                  for _ in range(n)]
+    def build_caches(dtype, n, mode="per_token_head"):
+        caches = [kvq.PagedCache(case.num_pages, Hkv, D, dtype, mode) for _ in range(n)]
         step = 16384
         for i in range(0, len(hist), step):
             sel = hist[i:i + step]
@@ -171,97 +293,221 @@ def main():
         torch.cuda.synchronize()
         return caches
 
-    def run(caches, steps, warmup, events=True):
+    def decode_step_legs(caches, steps, warmup):
         ws = kvq.decode_workspace(caches[0], B, Hq, L, 0, 0, dev)
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
-        for i in range(warmup):
-            c = caches[i % len(caches)]
-            kvq.cache_write(c, k_new, v_new, slots_new)
-            kvq.decode_attention(c, q, bt, sl, L, scales, out=out, workspace=ws)
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)] if events else []
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record()
-        for i in range(steps):
-            c = caches[i % len(caches)]
-            kvq.cache_write(c, k_new, v_new, slots_new)
-            if events:
-                ev[i][0].record()
-            kvq.decode_attention(c, q, bt, sl, L, scales, out=out, workspace=ws)
-            if events:
-                ev[i][1].record()
-        t1.record()
-        torch.cuda.synchronize()
-        step_ms = t0.elapsed_time(t1) / steps
-        dec_ms = [a.elapsed_time(b) for a, b in ev]
-        return step_ms, dec_ms
+        t_dec = []
 
-    fp8_caches = build_caches("fp8", args.rotate)
-    log("bench: fp8 caches filled")
-    step_ms, dec_ms = run(fp8_caches, args.steps, args.warmup)
-    dec_bytes, wr_bytes = step_bytes(B, L, Hkv, Hq, D, 8)
-    dec_us = float(np.mean(dec_ms)) * 1e3
-    achieved = dec_bytes / (dec_us * 1e-6) / 1e9
-    result = {
-        "metric": METRIC,
-        "value": round((dec_bytes + wr_bytes) / (step_ms * 1e-3) / 1e9, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5),
-        "us_per_step": round(step_ms * 1e3, 2),
-        "pct_hbm_peak": round(100 * (dec_bytes + wr_bytes) / (step_ms * 1e-3) / 1e9
-                              / HBM_PEAK_GBS, 2),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8_e4m3",
-        "data": "synthetic",
-        "config": {"workload": "Llama-3.1-8B-shaped decode layer: 8 seqs x 20,000 ctx, "
-                               "32 q / 8 KV heads, head_dim 128, page 16, permuted block "
-                               "table, fp8 e4m3 cache with per-token-head scales; step = "
-                               "cache write of 8 new tokens + split-K decode",
-                   "batch": B, "context": L, "q_heads": Hq, "kv_heads": Hkv,
-                   "head_dim": D, "page_size": 16, "scale_mode": "per_token_head",
-                   "accumulate": "f32", "cache_copies_rotated": args.rotate,
-                   "step_bytes": dec_bytes + wr_bytes, "decode_bytes": dec_bytes},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(), "kernel": "decode_split_kernel",
-                     "kernel_us": round(dec_us, 2),
-                     "kernel_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
-                                           round(float(np.percentile(dec_ms, 90)) * 1e3, 2)]},
-    }
-    del fp8_caches
-    torch.cuda.empty_cache()
-    if not args.no_bf16:
-        bf_caches = build_caches("bf16", 2)
-        bf_ms, bf_dec = run(bf_caches, max(10, args.steps // 2), args.warmup)
-        pages = (L + 15) // 16
-        bdec = B * L * Hkv * 4 * D + 2 * (B * Hq * D * 2) + B * pages * 4  # bf16 K+V
-        result["bf16_cache_baseline"] = {
-            "us_per_step": round(bf_ms * 1e3, 2),
-            "decode_us": round(float(np.mean(bf_dec)) * 1e3, 2),
-            "GB_s": round(bdec / (float(np.mean(bf_dec)) * 1e-3) / 1e9, 1),
-            "fp8_over_bf16_step_time": round(step_ms / bf_ms, 3)}
-        del bf_caches
+        def step(i):
+            c = caches[i % len(caches)]
+            kvq.cache_write(c, k_new, v_new, slots_new)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            kvq.decode_attention(c, q, bt, sl, L, ones, out=out, workspace=ws)
+            e1.record()
+            t_dec.append((e0, e1))
+        t_step = timer.run(step, steps, warmup)
+        dec_us = [a.elapsed_time(b) * 1e3 for a, b in t_dec[warmup:]]
+        return t_step, dec_us
+
+    if "decode" in legs:
+        caches = build_caches("fp8", args.rotate)
+        log("bench: fp8 caches filled")
+        t_step, dec_us = decode_step_legs(caches, args.steps, args.warmup)
+        del caches
         torch.cuda.empty_cache()
+        dec_b = decode_bytes(B, L, Hkv, Hq, D, 1, 8)
+        wr_b = write_bytes(B, Hkv, D, 1, 8)
+        step_us = float(np.mean(t_step))
+        dk_us = float(np.mean(dec_us))
+        achieved = dec_b / (dk_us * 1e-6) / 1e9
+        result.update({
+            "metric": METRIC,
+            "value": round((dec_b + wr_b) / (step_us * 1e-6) / 1e9, 2),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(step_us / 1e3, 5),
+            "us_per_step": round(step_us, 2),
+            "pct_hbm_peak": round(100 * (dec_b + wr_b) / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "fp8_e4m3",
+            "data": "synthetic",
+            "config": {"workload": "Llama-3.1-8B-shaped decode layer: 8 seqs x 20,000 ctx, "
+                                   "32 q / 8 KV heads, head_dim 128, page 16, permuted block "
+                                   "table, fp8 e4m3 cache with per-token-head scales; step = "
+                                   "cache write of 8 new tokens + split-K decode",
+                       "batch": B, "context": L, "q_heads": Hq, "kv_heads": Hkv,
+                       "head_dim": D, "page_size": 16, "scale_mode": "per_token_head",
+                       "accumulate": "f32", "cache_copies_rotated": args.rotate,
+                       "step_bytes": dec_b + wr_b, "decode_bytes": dec_b},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(), "kernel": DECODE_KERNEL,
+                         "kernel_us": round(dk_us, 2), **{k: v for k, v in stats(dec_us).items()
+                                                          if k != "us_mean"}},
+        })
+
+    if "bf16" in legs:
+        caches = build_caches("bf16", 2)
+        t_step, dec_us = decode_step_legs(caches, max(10, args.steps // 2), args.warmup)
+        del caches
+        torch.cuda.empty_cache()
+        bdec = decode_bytes(B, L, Hkv, Hq, D, 2, 0)
+        result["bf16_cache_baseline"] = {
+            "us_per_step": round(float(np.mean(t_step)), 2),
+            "decode_us": round(float(np.mean(dec_us)), 2),
+            "GB_s": round(bdec / (float(np.mean(dec_us)) * 1e-6) / 1e9, 1),
+            "decode_bytes": bdec}
+        if "us_per_step" in result:
+            result["bf16_cache_baseline"]["fp8_over_bf16_step_time"] = round(
+                result["us_per_step"] / float(np.mean(t_step)), 3)
+    del case, q, k_new, v_new
+    torch.cuda.empty_cache()
+
+    if "tiny" in legs:
+        tc = workloads.tiny_decode()
+        c = kvq.PagedCache(tc.num_pages, tc.num_kv_heads, tc.head_dim, "fp8", "per_token_head")
+        kvq.cache_write(c, to_dev(tc.k), to_dev(tc.v),
+                        torch.from_numpy(tc.slots.astype(np.int64)).to(dev))
+        tq, tbt, tsl = to_dev(tc.q), torch.from_numpy(tc.block_table).to(dev), \
+            torch.from_numpy(tc.seq_lens).to(dev)
+        ws = kvq.decode_workspace(c, 1, 4, 256, 0, 0, dev)
+        out = torch.empty((1, 4, 64), dtype=torch.bfloat16, device=dev)
+        us = timer.run(lambda i: kvq.decode_attention(c, tq, tbt, tsl, 256, ones, out=out,
+                                                      workspace=ws), 50, 5)
+        result["tiny_decode"] = {"workload": "1 seq x 256 tokens, 4/1 heads, D 64, "
+                                             "per-token-head", **stats(us)}
+
+    gen = torch.Generator(device=dev)
+
+    def dev_normal(shape, std, seed):
+        gen.manual_seed(seed)
+        return (torch.randn(shape, generator=gen, device=dev) * std).to(torch.bfloat16)
+
+    if "long" in legs:
+        # 131,072-token decode, 32/8 heads, D 128, N(0, 0.5^2), per-tensor scale 1.0,
+        # identity table; two cache copies (2 x 268 MB) rotate
+        Lc, P = 131072, 131072 // 16
+        caches = []
+        for cpy in range(2):
+            c = kvq.PagedCache(P, 8, 128, "fp8", "per_tensor")
+            for t0 in range(0, Lc, 16384):
+                kk = dev_normal((16384, 8, 128), 0.5, 1030 + t0)
+                vv = dev_normal((16384, 8, 128), 0.5, 1031 + t0)
+                kvq.cache_write(c, kk, vv, torch.arange(t0, t0 + 16384, device=dev))
+            caches.append(c)
+        lq = dev_normal((1, 32, 128), 1.0, 1039)
+        lbt = torch.arange(P, dtype=torch.int32, device=dev).reshape(1, -1)
+        lsl = torch.tensor([Lc], dtype=torch.int32, device=dev)
+        ws = kvq.decode_workspace(caches[0], 1, 32, Lc, 0, 0, dev)
+        out = torch.empty((1, 32, 128), dtype=torch.bfloat16, device=dev)
+        us = timer.run(lambda i: kvq.decode_attention(caches[i % 2], lq, lbt, lsl, Lc, ones,
+                                                      out=out, workspace=ws),
+                       max(10, args.steps // 2), args.warmup)
+        nb = decode_bytes(1, Lc, 8, 32, 128, 1, 0)
+        result["long_context_decode"] = {
+            "workload": "1 seq x 131,072 tokens, 32/8 heads, D 128, per-tensor scale",
+            **stats(us), "bytes": nb,
+            "GB_s": round(nb / (float(np.mean(us)) * 1e-6) / 1e9, 1),
+            "frac_hbm": round(nb / (float(np.mean(us)) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del caches
+        torch.cuda.empty_cache()
+
+    if "hybrid" in legs:
+        # 24 layers: even = full attention over an fp8 cache (per-tensor 1.0), odd =
+        # window 128 over a bf16 cache; 8 x 20,000 tokens, 64/8 heads, D 64; a step
+        # writes each layer's 8 new tokens and runs its decode
+        Bh, Lh, Hqh, Hkvh, Dh, W = 8, 20000, 64, 8, 64, 128
+        Ph = Bh * ((Lh + 15) // 16)
+        hbt = torch.arange(Ph, dtype=torch.int32, device=dev).reshape(Bh, -1)
+        hsl = torch.full((Bh,), Lh, dtype=torch.int32, device=dev)
+        fill = torch.tensor([b * (Ph // Bh) * 16 + t for b in range(Bh) for t in range(Lh - 1)],
+                            dtype=torch.int64, device=dev)
+        new_slots = torch.tensor([b * (Ph // Bh) * 16 + Lh - 1 for b in range(Bh)],
+                                 dtype=torch.int64, device=dev)
+        layers = []
+        for layer in range(24):
+            full = layer % 2 == 0
+            c = kvq.PagedCache(Ph, Hkvh, Dh, "fp8" if full else "bf16", "per_tensor")
+            for t0 in range(0, fill.numel(), 32768):
+                sel = fill[t0:t0 + 32768]
+                kk = dev_normal((sel.numel(), Hkvh, Dh), 1.0, 2000 + 100 * layer + t0 // 32768)
+                vv = dev_normal((sel.numel(), Hkvh, Dh), 1.0, 5000 + 100 * layer + t0 // 32768)
+                kvq.cache_write(c, kk, vv, sel)
+            kn = dev_normal((Bh, Hkvh, Dh), 1.0, 9000 + layer)
+            vn = dev_normal((Bh, Hkvh, Dh), 1.0, 9100 + layer)
+            qn = dev_normal((Bh, Hqh, Dh), 1.0, 9200 + layer)
+            win = 0 if full else W
+            ws = kvq.decode_workspace(c, Bh, Hqh, Lh, win, 0, dev)
+            layers.append((c, kn, vn, qn, win, ws))
+        torch.cuda.synchronize()
+        out = torch.empty((Bh, Hqh, Dh), dtype=torch.bfloat16, device=dev)
+
+        def hybrid_step(i):
+            for c, kn, vn, qn, win, ws in layers:
+                kvq.cache_write(c, kn, vn, new_slots)
+                kvq.decode_attention(c, qn, hbt, hsl, Lh, ones, window=win, out=out,
+                                     workspace=ws)
+        us = timer.run(hybrid_step, max(10, args.steps // 4), max(2, args.warmup // 2))
+        nb = 12 * (decode_bytes(Bh, Lh, Hkvh, Hqh, Dh, 1, 0) + write_bytes(Bh, Hkvh, Dh, 1, 0)) \
+            + 12 * (decode_bytes(Bh, Lh, Hkvh, Hqh, Dh, 2, 0, window=W)
+                    + write_bytes(Bh, Hkvh, Dh, 2, 0))
+        result["hybrid_stack_step"] = {
+            "workload": "gpt-oss-20b-shaped 24-layer step: 12 fp8 full layers + 12 bf16 "
+                        "window-128 layers, 8 x 20,000 ctx, 64/8 heads, D 64; cache writes "
+                        "included",
+            **stats(us), "bytes": nb,
+            "GB_s": round(nb / (float(np.mean(us)) * 1e-6) / 1e9, 1),
+            "frac_hbm": round(nb / (float(np.mean(us)) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del layers
+        torch.cuda.empty_cache()
+
+    if "prefill" in legs:
+        pc = workloads.hd256_prefill()
+        log("bench: hd256 prefill workload generated")
+        c = kvq.PagedCache(pc.num_pages, pc.num_kv_heads, pc.head_dim, "fp8", "per_token_head")
+        for t0 in range(0, len(pc.k), 16384):
+            sl_ = slice(t0, t0 + 16384)
+            kvq.cache_write(c, to_dev(pc.k[sl_]), to_dev(pc.v[sl_]),
+                            torch.from_numpy(pc.slots[sl_].astype(np.int64)).to(dev))
+        pq = to_dev(pc.q)
+        pcu = torch.from_numpy(pc.cu_q_lens).to(dev)
+        pbt = torch.from_numpy(pc.block_table).to(dev)
+        psl = torch.from_numpy(pc.seq_lens).to(dev)
+        n_new = int(pc.cu_q_lens[1])
+        out = torch.empty(pc.q.shape, dtype=torch.bfloat16, device=dev)
+        us = timer.run(lambda i: kvq.prefill_attention(c, pq, pcu, pbt, psl, n_new, ones,
+                                                       out=out), 10, 3)
+        fl = prefill_flops(int(pc.seq_lens[0]) - n_new, n_new, pc.q.shape[1], pc.head_dim)
+        tf = fl / (float(np.mean(us)) * 1e-6) / 1e12
+        result["prefill_hd256"] = {
+            "workload": "head_dim-256 chunked prefill: 8,192 new on a 32,768-token fp8 "
+                        "cache, 8/4 heads, causal, per-token-head scales",
+            **stats(us), "flops": fl,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                         "kernel": "prefill_kernel"}}
+        del c
+        torch.cuda.empty_cache()
+
     if args.copy_calib:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        result["copy_calib_bytes"] = n
-    if args.cpu_seqs > 0:
+        result["copy_calib_bytes"] = COPY_BYTES
+
+    if args.cpu_seqs > 0 and "decode" in legs:
         log("bench: timing the CPU oracle sample")
-        result["cpu_baseline"] = cpu_baseline(case, min(args.cpu_seqs, B), args.cpu_reps)
-    else:
+        result["cpu_baseline"] = cpu_baseline(workloads.llama8b_decode(),
+                                              min(args.cpu_seqs, 8), args.cpu_reps)
+    elif "decode" in legs:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
 
