@@ -23,7 +23,7 @@ SOURCES = ["host.cpp", "cache_write.hip", "decode.hip", "prefill.hip"]
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wno-unused-command-line-argument",
+    "-Wno-unused-command-line-argument", "-Wno-inline-asm",
     # Keep the decode kernel's unrolled page ring: without this, SimplifyCFG sinks
     # the identical per-page code of the three buffers back into one block, which
     # removes the prefetch of the next pages.

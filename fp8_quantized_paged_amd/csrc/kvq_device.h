@@ -27,36 +27,23 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
   return u >> 16;
 }
 
-// Round-to-nearest-even, saturating float32 -> e4m3 encoder on the bit pattern.
+// Round-to-nearest-even, saturating float32 -> e4m3 encoder, without branches.
 // NaN -> 0x7F | sign; |x| >= 448 (and inf) -> 0x7E | sign; sign of zero kept.
-// (Also built for the host so the bit logic can be checked exhaustively on a CPU.)
+// Normal range [2^-6, 448): keep 3 of the 23 fraction bits, ties to even (a carry may
+// bump the exponent); e4m3 exponent = float32 exponent - 120.  Below 2^-6 the grid
+// is n * 2^-9, n = 0..8: |x| * 2^9 is exact and rint rounds half to even.
+// (Also built for the host so it can be checked exhaustively on a CPU.)
 __host__ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   const uint32_t sign = (u >> 24) & 0x80u;
   const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a > 0x7F800000u) {
-    code = 0x7Fu;
-  } else if (a >= 0x43E00000u) {          // 448.0f
-    code = 0x7Eu;
-  } else if (a >= 0x3C800000u) {          // 2^-6: normal e4m3 range
-    // keep 3 of 23 fraction bits, ties to even, carry may bump the exponent;
-    // e4m3 exponent = float32 exponent - 120
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    code = (r >> 20) - (120u << 3);
-  } else {                                // subnormal grid n * 2^-9, n = 0..8
-    const uint32_t e = a >> 23;
-    const uint32_t mf = (a & 0x7FFFFFu) | (e ? 0x800000u : 0u);
-    const int sh = 141 - (int)(e ? e : 1u);   // value * 2^9 = mf * 2^-sh
-    if (sh >= 25) {
-      code = 0u;
-    } else {
-      const uint32_t q = mf >> sh;
-      const uint32_t rem = mf & ((1u << sh) - 1u);
-      const uint32_t half = 1u << (sh - 1);
-      code = q + ((rem > half) || (rem == half && (q & 1u)) ? 1u : 0u);
-    }
-  }
+  const uint32_t normal = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  // the clamp keeps the conversion defined for inputs that take another branch
+  const float scaled = __builtin_fminf(__builtin_bit_cast(float, a) * 512.0f, 8.0f);
+  const uint32_t sub = (uint32_t)__builtin_rintf(scaled);
+  uint32_t code = a >= 0x3C800000u ? normal : sub;  // 2^-6
+  code = a >= 0x43E00000u ? 0x7Eu : code;           // 448
+  code = a > 0x7F800000u ? 0x7Fu : code;            // NaN
   return code | sign;
 }
 

@@ -61,28 +61,54 @@ __device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// LDS layout of one tile buffer.
-//   K:  [64 keys][D bytes], the 16-byte chunks of key k stored at chunk (c ^ k % NC)
-//       (XOR swizzle: the 32 lanes reading one chunk column hit distinct banks).
-//   VT: [D dims][80 bytes]: per dim, 2 groups x 32 bytes (the key order of the PV
-//       contraction, see vt_offset) + 16 bytes of padding against bank conflicts.
-//   scales: float c[64] (score multiplier per key), vs[64], inv_vs[64].
+// Key order inside a 64-key tile.  The A operand of S^T = K . Q^T is loaded so that
+// MFMA row i (0..63) holds key kappa(i) = 32 (i / 32) + 16 ((i / 4) % 2) + 4 ((i % 32) / 8)
+// + i % 4.  With the 32x32 result layout (lane l, register r of key block kb holds
+// row i = 32 kb + 8 (r / 4) + 4 (l / 32) + r % 4) this puts, in lane group gg = l / 32,
+// register r of key block kb on key 32 kb + 16 gg + r: page 2 kb + gg, token r.  So
+// the P' bytes a lane packs in register order are whole pages, and the matching V^T
+// operand bytes are whole 16-token rows of the dim-major V tiles, which the loads
+// copy unchanged.
+__device__ __forceinline__ int tile_key(int i) {
+  const int j = i % 32;
+  return 32 * (i / 32) + 16 * ((j / 4) % 2) + 4 * (j / 8) + j % 4;
+}
+
+// LDS layout of one pipeline stage (all regions are arrays of 16-byte chunks written
+// by direct global->LDS loads: instruction u of the workgroup fills chunks
+// 64 u .. 64 u + 63, one per lane, so placement is chosen by the address each lane
+// fetches):
+//   K:  chunk i * NC + (c ^ i % NC) holds bytes 16c .. 16c+15 of the key of MFMA row
+//       i (XOR swizzle: the 16 lanes of one read pass hit distinct bank groups).
+//   VT: chunk 4d + ((2 gg + kb) ^ ((d >> 2) & 3)) holds the 16 tokens of channel d of
+//       page 2 kb + gg (again a swizzle for conflict-free 16-lane passes).
+//   KS, VS: the 64 keys' K and V scales (per-token-head mode).
+//   CF, FV, IF: per-key factors derived by wave 0 from KS/VS: score multiplier
+//       k_scale * q_scale * softmax_scale * log2(e), P' factor v_scale / (v_ref *
+//       prob_scale), and its reciprocal.
 template <int D>
 struct Layout {
   static constexpr int NC = D / 16;
   static constexpr int K_OFF = 0;
-  static constexpr int VT_PITCH = 80;
   static constexpr int VT_OFF = kTile * D;
-  static constexpr int SC_OFF = VT_OFF + D * VT_PITCH;
-  static constexpr int BYTES = SC_OFF + 3 * kTile * 4;
+  static constexpr int KS_OFF = VT_OFF + kTile * D;
+  static constexpr int VS_OFF = KS_OFF + kTile * 4;
+  static constexpr int CF_OFF = VS_OFF + kTile * 4;
+  static constexpr int FV_OFF = CF_OFF + kTile * 4;
+  static constexpr int IF_OFF = FV_OFF + kTile * 4;
+  static constexpr int VREF_OFF = IF_OFF + kTile * 4;
+  static constexpr int BYTES = VREF_OFF + 16;
+  static constexpr int K_INSTR = kTile * NC / kWave;   // 16-byte loads per tile (K)
+  static constexpr int V_INSTR = kTilePages * D / kWave;
 };
 
-// Key order of the PV contraction.  In the 32x32 MFMA result, lane l (group
-// g = l / 32) register r of key block kb holds key 32 kb + 8 (r / 4) + 4 g + r % 4;
-// P' packs those bytes in register order, i.e. byte 16 kb + r of the lane's 32-byte
-// B operand.  V^T row (d, g) is stored in that order: dword 4 kb + a holds keys
-// 32 kb + 8 a + 4 g + 0..3.
-__device__ __forceinline__ int vt_dword(int kb, int a) { return 4 * kb + a; }
+constexpr int kStages = 3;  // tiles resident: one computed, kStages - 1 in flight
+// Block-table entries are fetched into LDS by direct loads, kIdTiles tiles' worth at a
+// time, one chunk ahead of use.  (Reading them with vector loads inside the tile loop
+// would put them in the same in-order completion count as the tile loads and force
+// a wait for every tile in flight.)
+constexpr int kIdTiles = 64;
+static_assert(kIdTiles * kTilePages == kThreads, "one page id per thread per chunk");
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -101,23 +127,53 @@ struct PrefillArgs {
   int32_t out_f32;
 };
 
-template <int D, int G, bool kPTH>
-struct Staging {
-  static constexpr int KCH = kTile * D / 16 / kThreads;  // K chunks per thread
-  static constexpr int VCH = kTilePages * D / kThreads;   // V rows per thread
-  uint4 k[KCH];
-  uint4 v[VCH];
-  float sc;  // threads 0..63: K scale of key tid; 64..127: V scale of key tid - 64
-};
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8).  wait_vmcnt<N>: at most N vector memory operations outstanding, the other
+// counters untouched.  barrier_lds: this wave's LDS operations done, then the
+// workgroup barrier (unlike __syncthreads it does not wait for the direct-to-LDS
+// loads still in flight).
+// Direct global -> LDS loads (each lane's 16 or 4 bytes land at lds_off + lane * size).
+// Written as inline assembly on purpose: the compiler treats its own form of these
+// loads as pending LDS writes and waits for all of them before any LDS read, which
+// would drain the tile pipeline; here the waits are explicit (wait_vmcnt), and
+// unknown vector memory operations can only make the compiler's own waits stricter.
+__device__ __forceinline__ void lds_load16(const void* src, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_off) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(const void* src, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_off) : "memory", "m0");
+}
+template <typename T>
+__device__ __forceinline__ uint32_t lds_offset(T* p) {  // p points into __shared__ memory
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
 
 template <int D, int G, bool kPTH>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) {
   using LY = Layout<D>;
-  using ST = Staging<D, G, kPTH>;
   constexpr int NP = kWgRows / G;  // query positions per workgroup
   constexpr int KS = D / 64;       // 64-dim steps of the QK contraction
   constexpr int DB = D / 32;       // 32-dim blocks of the output
-  __shared__ __align__(16) uint8_t lds[2][LY::BYTES];
+  // direct loads per wave per tile: K and V chunks, plus one scale load (waves 0, 1)
+  constexpr int KW = LY::K_INSTR / kWaves;
+  constexpr int VW = LY::V_INSTR / kWaves;
+  static_assert(KW >= 1 && VW >= 1, "tile shape");
+  __shared__ __align__(16) uint8_t lds[kStages][LY::BYTES];
+  // physical page ids of the workgroup's tiles, kIdTiles tiles per chunk, two chunks
+  __shared__ int ids_lds[2][kIdTiles * kTilePages];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -162,6 +218,64 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
                                 a.window + 1)
                    : 0);
 
+  // ---- lane-constant parts of the direct loads ------------------------------------
+  // K: instruction j of this wave fills chunk s = 64 (wave * KW + j) + lane
+  int k_page[KW], k_off[KW];
+#pragma unroll
+  for (int j = 0; j < KW; ++j) {
+    const int sch = 64 * (wave * KW + j) + lane;
+    const int i = sch / LY::NC;
+    const int c = (sch % LY::NC) ^ (i % LY::NC);
+    const int key = tile_key(i);
+    k_page[j] = key / kPage;
+    k_off[j] = (key % kPage) * D + c * 16;
+  }
+  // V: chunk s = 64 (wave * VW + j) + lane holds channel d of page 2 kb + gg
+  int v_page[VW], v_off[VW];
+#pragma unroll
+  for (int j = 0; j < VW; ++j) {
+    const int sch = 64 * (wave * VW + j) + lane;
+    const int d = sch / 4;
+    const int x = (sch % 4) ^ ((d >> 2) & 3);
+    v_page[j] = 2 * (x % 2) + x / 2;
+    v_off[j] = d * kPage;
+  }
+  // scales: wave 0 loads K scales, wave 1 V scales, one key per lane
+  const int sc_page = lane / kPage, sc_tok = lane % kPage;
+
+  // page ids of chunk c: tiles t_first + kIdTiles c .. (one per thread; entries past
+  // the sequence end repeat its last page, whose keys are masked anyway)
+  auto issue_ids = [&](int c) {
+    const int e = 64 * wave + lane;
+    const int idx = min((t_first + kIdTiles * c) * kTilePages + e, npages - 1);
+    lds_load4(bt + idx, lds_offset(&ids_lds[c & 1][64 * wave]));
+  };
+  auto issue_tile = [&](int t, int slot) {
+    const int tt = min(t, t_last);  // past the last tile: harmless re-load of it
+    const int rel = tt - t_first;
+    const int* idr = &ids_lds[(rel / kIdTiles) & 1][(rel % kIdTiles) * kTilePages];
+    // each lane reads the page id its own loads need (lane-varying LDS reads)
+#pragma unroll
+    for (int j = 0; j < KW; ++j) {
+      const int64_t tileg = (int64_t)idr[k_page[j]] * hkv + g;
+      lds_load16(a.k_pages + tileg * kPage * D + k_off[j],
+                 lds_offset(&lds[slot][LY::K_OFF + 1024 * (wave * KW + j)]));
+    }
+#pragma unroll
+    for (int j = 0; j < VW; ++j) {
+      const int64_t tileg = (int64_t)idr[v_page[j]] * hkv + g;
+      lds_load16(a.v_pages + tileg * D * kPage + v_off[j],
+                 lds_offset(&lds[slot][LY::VT_OFF + 1024 * (wave * VW + j)]));
+    }
+    if constexpr (kPTH) {
+      if (wave < 2) {
+        const int64_t idx = ((int64_t)idr[sc_page] * hkv + g) * kPage + sc_tok;
+        const float* src = wave == 0 ? a.k_scales : a.v_scales;
+        lds_load4(src + idx, lds_offset(&lds[slot][wave == 0 ? LY::KS_OFF : LY::VS_OFF]));
+      }
+    }
+  };
+
   // ---- query codes: B operand of S^T = K . Q^T -----------------------------------
   // lane holds row `row`, dims 64 ks + 32 grp + 0..31 as 32 e4m3 codes per step.
   v8i qb[KS];
@@ -194,80 +308,60 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
     }
   }
   const float qk_base = a.q_scale * a.sm_log2 * (kPTH ? 1.0f : a.k_scale);
+  // P' = p * (v_scale_j / (v_ref * prob_scale)) never exceeds 448 when p <= 2^8 and
+  // prob_scale >= 2^8 / 448; below that P' is clamped
+  const bool clamp_p = a.prob_scale < 256.0f / kE4m3Max;
 
-  // ---- tile staging: global -> registers -> LDS -----------------------------------
-  auto load_tile = [&](int t, ST& s) {
-#pragma unroll
-    for (int u = 0; u < ST::KCH; ++u) {
-      const int c = tid + u * kThreads;
-      const int key = c / LY::NC, col = c % LY::NC;
-      const int pg = t * kTilePages + key / kPage;
-      s.k[u] = make_uint4(0, 0, 0, 0);
-      if (pg < npages) {
-        const int64_t tileg = (int64_t)bt[pg] * hkv + g;
-        s.k[u] = *reinterpret_cast<const uint4*>(
-            a.k_pages + (tileg * kPage + key % kPage) * D + col * 16);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < ST::VCH; ++u) {
-      const int c = tid + u * kThreads;
-      const int pl = c / D, d = c % D;
-      const int pg = t * kTilePages + pl;
-      s.v[u] = make_uint4(0, 0, 0, 0);
-      if (pg < npages) {
-        const int64_t tileg = (int64_t)bt[pg] * hkv + g;
-        s.v[u] = *reinterpret_cast<const uint4*>(a.v_pages + (tileg * D + d) * kPage);
-        // slots past the sequence end were never written: their bytes may be any
-        // code, NaN included, and 0 * NaN would poison the product
-        const int valid = L - pg * kPage;
-        if (valid < kPage) {
-          uint32_t w[4] = {s.v[u].x, s.v[u].y, s.v[u].z, s.v[u].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int keep = min(max(valid - 4 * j, 0), 4);  // bytes kept in word j
-            w[j] &= keep >= 4 ? 0xFFFFFFFFu : ((1u << (8 * keep)) - 1u);
-          }
-          s.v[u] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-      }
-    }
-    s.sc = 0.0f;
-    if constexpr (kPTH) {
-      if (tid < 2 * kTile) {
-        const int key = tid % kTile;
-        const int pg = t * kTilePages + key / kPage;
-        if (t * kTile + key < L) {
-          const int64_t idx = ((int64_t)bt[pg] * hkv + g) * kPage + key % kPage;
-          s.sc = tid < kTile ? a.k_scales[idx] : a.v_scales[idx];
-        }
-      }
-    }
+  // Wait for this wave's loads of the next tile (the loads of the kNewer tiles issued
+  // after it may stay in flight), then make every wave's loads visible.
+  auto wait_tile = [&]() {
+    constexpr int kNewer = kStages - 2;
+    if (kPTH && wave < 2) wait_vmcnt<(KW + VW + 1) * kNewer>();
+    else wait_vmcnt<(KW + VW) * kNewer>();
+    __builtin_amdgcn_s_barrier();
   };
-  auto store_tile = [&](int t, const ST& s, uint8_t* buf) {
+  // Slots past the sequence end of the last page were never written (any bytes, NaN
+  // included): zero their V bytes and scales before anyone reads the tile.
+  auto scrub_tile = [&](int t, uint8_t* st) {
+    const int valid = L - t * kTile;  // keys of the tile below the sequence end
+    if (valid >= kTile) return;
+    for (int ch = tid; ch < LY::V_INSTR * kWave; ch += kThreads) {
+      const int d = ch / 4;
+      const int x = (ch % 4) ^ ((d >> 2) & 3);
+      const int page = 2 * (x % 2) + x / 2;
+      const int keep = min(max(valid - page * kPage, 0), kPage);  // tokens kept
+      if (keep < kPage) {
+        uint32_t* w = reinterpret_cast<uint32_t*>(st + LY::VT_OFF + 16 * ch);
 #pragma unroll
-    for (int u = 0; u < ST::KCH; ++u) {
-      const int c = tid + u * kThreads;
-      const int key = c / LY::NC, col = c % LY::NC;
-      *reinterpret_cast<uint4*>(buf + LY::K_OFF + key * D + (col ^ (key % LY::NC)) * 16) = s.k[u];
+        for (int q = 0; q < 4; ++q) {
+          const int kq = min(max(keep - 4 * q, 0), 4);
+          w[q] &= kq >= 4 ? 0xFFFFFFFFu : ((1u << (8 * kq)) - 1u);
+        }
+      }
     }
-#pragma unroll
-    for (int u = 0; u < ST::VCH; ++u) {
-      const int c = tid + u * kThreads;
-      const int pl = c / D, d = c % D;
-      const int kb = pl / 2, a0 = 2 * (pl % 2);
-      uint8_t* rowp = buf + LY::VT_OFF + d * LY::VT_PITCH;
-      // dwords 0, 2 of the 16-token row belong to group 0, dwords 1, 3 to group 1
-      *reinterpret_cast<uint2*>(rowp + 4 * vt_dword(kb, a0)) = make_uint2(s.v[u].x, s.v[u].z);
-      *reinterpret_cast<uint2*>(rowp + 32 + 4 * vt_dword(kb, a0)) = make_uint2(s.v[u].y, s.v[u].w);
-    }
-    float* sc = reinterpret_cast<float*>(buf + LY::SC_OFF);
     if constexpr (kPTH) {
-      if (tid < kTile) {
-        sc[tid] = s.sc * qk_base;  // score multiplier of key tid
-      } else if (tid < 2 * kTile) {
-        sc[tid] = s.sc;                                               // v scale
-        sc[tid + kTile] = s.sc > 0.0f ? 1.0f / s.sc : 0.0f;           // its inverse
+      if (tid < kTile && tid >= valid) {
+        reinterpret_cast<float*>(st + LY::KS_OFF)[tid] = 0.0f;
+        reinterpret_cast<float*>(st + LY::VS_OFF)[tid] = 0.0f;
+      }
+    }
+    barrier_lds();
+  };
+  // Wave 0 derives the per-key factors of a resident tile; v_ref (the running V
+  // scale maximum) moves here, in key order, so every wave sees the same sequence.
+  float vref_run = kPTH ? 0.0f : a.v_scale;
+  auto derive_tile = [&](uint8_t* st) {
+    if constexpr (kPTH) {
+      if (wave == 0) {
+        const float ks = reinterpret_cast<const float*>(st + LY::KS_OFF)[lane];
+        const float vs = reinterpret_cast<const float*>(st + LY::VS_OFF)[lane];
+        const float vm = wave_max(vs);
+        vref_run = fmaxf(vref_run, vm);
+        const float f = vref_run > 0.0f ? vs / (vref_run * a.prob_scale) : 0.0f;
+        reinterpret_cast<float*>(st + LY::CF_OFF)[lane] = ks * qk_base;
+        reinterpret_cast<float*>(st + LY::FV_OFF)[lane] = f;
+        reinterpret_cast<float*>(st + LY::IF_OFF)[lane] = f > 0.0f ? 1.0f / f : 0.0f;
+        if (lane == 0) reinterpret_cast<float*>(st + LY::VREF_OFF)[0] = vref_run;
       }
     }
   };
@@ -276,70 +370,75 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
   v16f o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = (v16f){};
-  float m = -INFINITY;     // reference row maximum (log2 units), same in both lane halves
-  float lam = 0.0f;        // this lane's part of the row sum, in P' units / v_scale_j
-  float vref = kPTH ? 0.0f : a.v_scale;
-  float pmul = kPTH ? 0.0f : 1.0f / a.prob_scale;  // p -> P' factor (times v_scale_j)
+  float m = -INFINITY;   // reference row maximum (log2 units), same in both lane halves
+  float lam = 0.0f;      // this lane's part of the row sum (in p units)
+  float vref = kPTH ? 0.0f : a.v_scale;  // v_ref the accumulator is expressed in
 
+  // prologue: page ids of the first chunk, then tiles t_first .. t_first + kStages - 2
+  // in flight, the first resident
+  issue_ids(0);
+  wait_vmcnt<0>();
+  barrier_lds();
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) issue_tile(t_first + s, s);
   {
-    ST s0;
-    load_tile(t_first, s0);
-    store_tile(t_first, s0, lds[t_first & 1]);
+    // the first tile: wait for everything issued so far except the newer tiles
+    wait_tile();
+    scrub_tile(t_first, lds[0]);
+    derive_tile(lds[0]);
+    barrier_lds();
   }
-  __syncthreads();
 
   for (int t = t_first; t <= t_last; ++t) {
-    ST s1;
-    const bool more = t < t_last;
-    if (more) load_tile(t + 1, s1);
-    const uint8_t* buf = lds[t & 1];
-    const float* sc = reinterpret_cast<const float*>(buf + LY::SC_OFF);
-
-    // ---- running V-scale reference (per-token-head) ------------------------------
-    if constexpr (kPTH) {
-      float vm = sc[kTile + lane];
-      vm = wave_max(vm);
-      if (vm > vref) {
-        const float f = vref > 0.0f ? vref / vm : 0.0f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= f;
-        lam *= f;
-        vref = vm;
-        pmul = 1.0f / (vref * a.prob_scale);
-      }
-    }
+    const int slot = (t - t_first) % kStages;
+    uint8_t* buf = lds[slot];
+    if ((t - t_first) % kIdTiles == 0) issue_ids((t - t_first) / kIdTiles + 1);
+    issue_tile(t + kStages - 1, (t - t_first + kStages - 1) % kStages);
 
     // ---- S^T = K . Q^T for the two 32-key blocks --------------------------------
     v16f s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = (v16f){};
-      const int key = 32 * kb + row;
+      const int i = 32 * kb + row;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int c0 = 4 * ks + 2 * grp;
         const uint4 x0 = *reinterpret_cast<const uint4*>(
-            buf + LY::K_OFF + key * D + ((c0) ^ (key % LY::NC)) * 16);
+            buf + LY::K_OFF + 16 * (i * LY::NC + ((c0) ^ (i % LY::NC))));
         const uint4 x1 = *reinterpret_cast<const uint4*>(
-            buf + LY::K_OFF + key * D + ((c0 + 1) ^ (key % LY::NC)) * 16);
+            buf + LY::K_OFF + 16 * (i * LY::NC + ((c0 + 1) ^ (i % LY::NC))));
         const v8i ka = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                         (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         s[kb] = mfma(ka, qb[ks], s[kb]);
       }
     }
 
+    // ---- v_ref of this tile (per-token-head): rescale the accumulator if it grew ----
+    if constexpr (kPTH) {
+      const float vr = reinterpret_cast<const float*>(buf + LY::VREF_OFF)[0];
+      if (vr > vref) {
+        const float f = vref > 0.0f ? vref / vr : 0.0f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= f;
+        vref = vr;
+      }
+    }
+
     // ---- scale, mask, lazy rescale -----------------------------------------------
+    // lane group grp, register r of key block kb holds key 32 kb + 16 grp + r
     const int kbase = t * kTile;
     const bool need_mask = (kbase + kTile - 1 > w_hi_min) || (kbase < w_lo_max) ||
                            (kbase + kTile > L);
+    const float* cf = reinterpret_cast<const float*>(buf + LY::CF_OFF);
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int k0 = 32 * kb + 8 * q4 + 4 * grp;  // first of 4 consecutive keys
+        const int k0 = 32 * kb + 16 * grp + 4 * q4;
         float4 c4;
-        if constexpr (kPTH) c4 = *reinterpret_cast<const float4*>(sc + k0);
+        if constexpr (kPTH) c4 = *reinterpret_cast<const float4*>(cf + k0);
         else c4 = make_float4(qk_base, qk_base, qk_base, qk_base);
         const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
@@ -365,34 +464,39 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
     const float msafe = m == -INFINITY ? 0.0f : m;
 
     // ---- P' (e4m3) in the B-operand layout; row sum from the rounded values -------
+    const float* fv = reinterpret_cast<const float*>(buf + LY::FV_OFF);
+    const float* iv = reinterpret_cast<const float*>(buf + LY::IF_OFF);
+    const float pmul = 1.0f / a.prob_scale;
     uint32_t pw[8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int k0 = 32 * kb + 8 * q4 + 4 * grp;
-        float vs[4] = {1.0f, 1.0f, 1.0f, 1.0f}, ivs[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        const int k0 = 32 * kb + 16 * grp + 4 * q4;
+        float f[4] = {pmul, pmul, pmul, pmul}, fi[4] = {a.prob_scale, a.prob_scale,
+                                                        a.prob_scale, a.prob_scale};
         if constexpr (kPTH) {
-          const float4 v4 = *reinterpret_cast<const float4*>(sc + kTile + k0);
-          const float4 i4 = *reinterpret_cast<const float4*>(sc + 2 * kTile + k0);
-          vs[0] = v4.x; vs[1] = v4.y; vs[2] = v4.z; vs[3] = v4.w;
-          ivs[0] = i4.x; ivs[1] = i4.y; ivs[2] = i4.z; ivs[3] = i4.w;
+          const float4 v4 = *reinterpret_cast<const float4*>(fv + k0);
+          const float4 i4 = *reinterpret_cast<const float4*>(iv + k0);
+          f[0] = v4.x; f[1] = v4.y; f[2] = v4.z; f[3] = v4.w;
+          fi[0] = i4.x; fi[1] = i4.y; fi[2] = i4.z; fi[3] = i4.w;
         }
         float pq[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float p = __builtin_amdgcn_exp2f(s[kb][4 * q4 + e] - msafe);
-          pq[e] = fminf(p * (vs[e] * pmul), kE4m3Max);
+          pq[e] = p * f[e];
+          if (clamp_p) pq[e] = fminf(pq[e], kE4m3Max);
         }
         uint32_t word = __builtin_amdgcn_cvt_pk_fp8_f32(pq[0], pq[1], 0, false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(pq[2], pq[3], word, true);
         pw[4 * kb + q4] = word;
         const float2_t d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
         const float2_t d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
-        lam = fmaf(d01.x, ivs[0], lam);
-        lam = fmaf(d01.y, ivs[1], lam);
-        lam = fmaf(d23.x, ivs[2], lam);
-        lam = fmaf(d23.y, ivs[3], lam);
+        lam = fmaf(d01.x, fi[0], lam);
+        lam = fmaf(d01.y, fi[1], lam);
+        lam = fmaf(d23.x, fi[2], lam);
+        lam = fmaf(d23.y, fi[3], lam);
       }
     const v8i pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
                     (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
@@ -400,27 +504,34 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
     // ---- O^T += V^T . P'^T -------------------------------------------------------------
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const uint8_t* vr = buf + LY::VT_OFF + (32 * db + row) * LY::VT_PITCH + 32 * grp;
-      const uint4 x0 = *reinterpret_cast<const uint4*>(vr);
-      const uint4 x1 = *reinterpret_cast<const uint4*>(vr + 16);
+      const int d = 32 * db + row;
+      const int sw = (d >> 2) & 3;
+      const uint4 x0 = *reinterpret_cast<const uint4*>(
+          buf + LY::VT_OFF + 16 * (4 * d + ((2 * grp + 0) ^ sw)));
+      const uint4 x1 = *reinterpret_cast<const uint4*>(
+          buf + LY::VT_OFF + 16 * (4 * d + ((2 * grp + 1) ^ sw)));
       const v8i va = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                       (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
       o[db] = mfma(va, pb, o[db]);
     }
 
-    // The other buffer was last read while computing tile t - 1, which every wave
-    // finished before the barrier that ended that iteration.
-    if (more) {
-      store_tile(t + 1, s1, lds[(t + 1) & 1]);
-      __syncthreads();
+    // ---- next tile resident: wait, scrub its unwritten slots, derive its factors ---
+    if (t < t_last) {
+      uint8_t* nb = lds[(t - t_first + 1) % kStages];
+      wait_tile();
+      scrub_tile(t + 1, nb);
+      derive_tile(nb);
+      barrier_lds();
     }
   }
+  // drain the loads still in flight (re-loads past the last tile) before exit
+  wait_vmcnt<0>();
 
   // ---- normalise and store: lane holds row `row`, dims 32 db + 8 (r/4) + 4 grp + r%4
+  // O = sum_j P'_j v_code_j with P'_j ~ p_j v_scale_j / (v_ref prob_scale) (per-tensor:
+  // p_j / prob_scale), lam ~ sum_j p_j; out = O * v_ref * prob_scale / lam
   const float lsum = lam + __shfl_xor(lam, kRows);
-  // o * (v_ref * prob_scale) / (lsum * v_ref * prob_scale) for per-token-head scales;
-  // per-tensor: numerator o * prob_scale * v_scale, row sum lsum * prob_scale
-  const float inv = lsum > 0.0f ? (kPTH ? 1.0f : a.v_scale) / lsum : 0.0f;
+  const float inv = lsum > 0.0f ? vref * a.prob_scale / lsum : 0.0f;
   if (row_ok) {
     const int64_t orow = ((int64_t)(q0 + p_loc) * Hq + g * G + hh) * D;
 #pragma unroll
