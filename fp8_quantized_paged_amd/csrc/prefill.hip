@@ -62,45 +62,17 @@ __device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f c) {
 }
 
 // Key order inside a 64-key tile.  The A operand of S^T = K . Q^T is loaded so that
-// MFMA row i (0..63) holds key kappa(i) = 32 (i / 32) + 16 ((i / 4) % 2) + 4 ((i % 32) / 8)
-// + i % 4.  With the 32x32 result layout (lane l, register r of key block kb holds
-// row i = 32 kb + 8 (r / 4) + 4 (l / 32) + r % 4) this puts, in lane group gg = l / 32,
-// register r of key block kb on key 32 kb + 16 gg + r: page 2 kb + gg, token r.  So
-// the P' bytes a lane packs in register order are whole pages, and the matching V^T
-// operand bytes are whole 16-token rows of the dim-major V tiles, which the loads
-// copy unchanged.
+// MFMA row i (0..63) holds key tile_key(i) = 32 (i / 32) + 16 ((i / 4) % 2)
+// + 4 ((i % 32) / 8) + i % 4.  With the 32x32 result layout (lane l, register r of
+// key block kb holds row i = 32 kb + 8 (r / 4) + 4 (l / 32) + r % 4) this puts, in
+// lane group gg = l / 32, register r of key block kb on key 32 kb + 16 gg + r: page
+// 2 kb + gg, token r.  So the P' bytes a lane packs in register order are whole
+// pages, and the matching V^T operand bytes are whole 16-token rows of the
+// dim-major V tiles, which the loads copy unchanged.
 __device__ __forceinline__ int tile_key(int i) {
   const int j = i % 32;
   return 32 * (i / 32) + 16 * ((j / 4) % 2) + 4 * (j / 8) + j % 4;
 }
-
-// LDS layout of one pipeline stage (all regions are arrays of 16-byte chunks written
-// by direct global->LDS loads: instruction u of the workgroup fills chunks
-// 64 u .. 64 u + 63, one per lane, so placement is chosen by the address each lane
-// fetches):
-//   K:  chunk i * NC + (c ^ i % NC) holds bytes 16c .. 16c+15 of the key of MFMA row
-//       i (XOR swizzle: the 16 lanes of one read pass hit distinct bank groups).
-//   VT: chunk 4d + ((2 gg + kb) ^ ((d >> 2) & 3)) holds the 16 tokens of channel d of
-//       page 2 kb + gg (again a swizzle for conflict-free 16-lane passes).
-//   KS, VS: the 64 keys' K and V scales (per-token-head mode).
-//   CF, FV, IF: per-key factors derived by wave 0 from KS/VS: score multiplier
-//       k_scale * q_scale * softmax_scale * log2(e), P' factor v_scale / (v_ref *
-//       prob_scale), and its reciprocal.
-template <int D>
-struct Layout {
-  static constexpr int NC = D / 16;
-  static constexpr int K_OFF = 0;
-  static constexpr int VT_OFF = kTile * D;
-  static constexpr int KS_OFF = VT_OFF + kTile * D;
-  static constexpr int VS_OFF = KS_OFF + kTile * 4;
-  static constexpr int CF_OFF = VS_OFF + kTile * 4;
-  static constexpr int FV_OFF = CF_OFF + kTile * 4;
-  static constexpr int IF_OFF = FV_OFF + kTile * 4;
-  static constexpr int VREF_OFF = IF_OFF + kTile * 4;
-  static constexpr int BYTES = VREF_OFF + 16;
-  static constexpr int K_INSTR = kTile * NC / kWave;   // 16-byte loads per tile (K)
-  static constexpr int V_INSTR = kTilePages * D / kWave;
-};
 
 constexpr int kStages = 3;  // tiles resident: one computed, kStages - 1 in flight
 // Block-table entries are fetched into LDS by direct loads, kIdTiles tiles' worth at a
@@ -109,6 +81,41 @@ constexpr int kStages = 3;  // tiles resident: one computed, kStages - 1 in flig
 // a wait for every tile in flight.)
 constexpr int kIdTiles = 64;
 static_assert(kIdTiles * kTilePages == kThreads, "one page id per thread per chunk");
+
+// LDS layout of one pipeline stage.  Every region is an array of 16-byte chunks
+// written by direct global->LDS loads: load instruction u fills chunks 64 u .. 64 u
+// + 63, one per lane, so placement is chosen through the address each lane fetches.
+//   K:  row i (MFMA row, key tile_key(i)) at chunks i * KP .. + NC - 1 (chunk c =
+//       bytes 16c .. 16c+15 of the key); KP = NC + 1: the pad chunk per row spreads
+//       16 consecutive rows over all 64 banks, and keeps every operand address an
+//       immediate offset from one per-lane base.
+//   VT: channel d at chunks 5 d .. 5 d + 3: chunk 2 gg + kb = the 16 tokens of channel
+//       d of page 2 kb + gg, then one pad chunk (same bank argument).
+//   KS, VS: the 64 keys' K and V scales (per-token-head mode).
+//   CF, FV, IF: per-key factors derived by wave 0 from KS/VS: score multiplier
+//       k_scale * q_scale * softmax_scale * log2(e), P' factor v_scale / (v_ref *
+//       prob_scale) and its reciprocal; VREF: v_ref after this tile.
+template <int D>
+struct Layout {
+  static constexpr int NC = D / 16;
+  static constexpr int KP = NC + 1;
+  static constexpr int K_OFF = 0;
+  static constexpr int K_CHUNKS = kTile * KP;
+  static constexpr int VT_OFF = K_OFF + 16 * K_CHUNKS;
+  static constexpr int VT_CHUNKS = 5 * D;
+  static constexpr int KS_OFF = VT_OFF + 16 * VT_CHUNKS;
+  static constexpr int VS_OFF = KS_OFF + kTile * 4;
+  static constexpr int CF_OFF = VS_OFF + kTile * 4;
+  static constexpr int FV_OFF = CF_OFF + kTile * 4;
+  static constexpr int IF_OFF = FV_OFF + kTile * 4;
+  static constexpr int VREF_OFF = IF_OFF + kTile * 4;
+  static constexpr int BYTES = VREF_OFF + 16;
+  // load instructions per wave per tile (the totals rounded up to the wave count;
+  // the extra instructions repeat earlier ones, writing the same bytes again)
+  static constexpr int KW = (K_CHUNKS / kWave + kWaves - 1) / kWaves;
+  static constexpr int VW = (VT_CHUNKS / kWave + kWaves - 1) / kWaves;
+  static_assert(K_CHUNKS % kWave == 0 && VT_CHUNKS % kWave == 0, "chunk counts");
+};
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -127,11 +134,6 @@ struct PrefillArgs {
   int32_t out_f32;
 };
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
-// 11:8).  wait_vmcnt<N>: at most N vector memory operations outstanding, the other
-// counters untouched.  barrier_lds: this wave's LDS operations done, then the
-// workgroup barrier (unlike __syncthreads it does not wait for the direct-to-LDS
-// loads still in flight).
 // Direct global -> LDS loads (each lane's 16 or 4 bytes land at lds_off + lane * size).
 // Written as inline assembly on purpose: the compiler treats its own form of these
 // loads as pending LDS writes and waits for all of them before any LDS read, which
@@ -150,6 +152,11 @@ __device__ __forceinline__ uint32_t lds_offset(T* p) {  // p points into __share
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8).  wait_vmcnt<N>: at most N vector memory operations outstanding, the other
+// counters untouched.  barrier_lds: this wave's LDS operations done, then the
+// workgroup barrier (unlike __syncthreads it does not wait for the direct-to-LDS
+// loads still in flight).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt");
@@ -161,16 +168,18 @@ __device__ __forceinline__ void barrier_lds() {
   __builtin_amdgcn_s_barrier();
 }
 
+template <typename T>
+__device__ __forceinline__ T lds_read(const uint8_t* base, int byte_off) {
+  return *reinterpret_cast<const T*>(base + byte_off);
+}
+
 template <int D, int G, bool kPTH>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) {
   using LY = Layout<D>;
   constexpr int NP = kWgRows / G;  // query positions per workgroup
   constexpr int KS = D / 64;       // 64-dim steps of the QK contraction
   constexpr int DB = D / 32;       // 32-dim blocks of the output
-  // direct loads per wave per tile: K and V chunks, plus one scale load (waves 0, 1)
-  constexpr int KW = LY::K_INSTR / kWaves;
-  constexpr int VW = LY::V_INSTR / kWaves;
-  static_assert(KW >= 1 && VW >= 1, "tile shape");
+  constexpr int PER_TILE = LY::KW + LY::VW + (kPTH ? 1 : 0);  // loads per wave per tile
   __shared__ __align__(16) uint8_t lds[kStages][LY::BYTES];
   // physical page ids of the workgroup's tiles, kIdTiles tiles per chunk, two chunks
   __shared__ int ids_lds[2][kIdTiles * kTilePages];
@@ -218,116 +227,59 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
                                 a.window + 1)
                    : 0);
 
-  // ---- lane-constant parts of the direct loads ------------------------------------
-  // K: instruction j of this wave fills chunk s = 64 (wave * KW + j) + lane
-  int k_page[KW], k_off[KW];
-#pragma unroll
-  for (int j = 0; j < KW; ++j) {
-    const int sch = 64 * (wave * KW + j) + lane;
-    const int i = sch / LY::NC;
-    const int c = (sch % LY::NC) ^ (i % LY::NC);
-    const int key = tile_key(i);
-    k_page[j] = key / kPage;
-    k_off[j] = (key % kPage) * D + c * 16;
-  }
-  // V: chunk s = 64 (wave * VW + j) + lane holds channel d of page 2 kb + gg
-  int v_page[VW], v_off[VW];
-#pragma unroll
-  for (int j = 0; j < VW; ++j) {
-    const int sch = 64 * (wave * VW + j) + lane;
-    const int d = sch / 4;
-    const int x = (sch % 4) ^ ((d >> 2) & 3);
-    v_page[j] = 2 * (x % 2) + x / 2;
-    v_off[j] = d * kPage;
-  }
-  // scales: wave 0 loads K scales, wave 1 V scales, one key per lane
-  const int sc_page = lane / kPage, sc_tok = lane % kPage;
-
-  // page ids of chunk c: tiles t_first + kIdTiles c .. (one per thread; entries past
-  // the sequence end repeat its last page, whose keys are masked anyway)
-  auto issue_ids = [&](int c) {
-    const int e = 64 * wave + lane;
-    const int idx = min((t_first + kIdTiles * c) * kTilePages + e, npages - 1);
+  // ---- direct loads -----------------------------------------------------------------
+  auto issue_ids = [&](int c) {  // page ids of id chunk c, one per thread
+    const int idx = min((t_first + kIdTiles * c) * kTilePages + tid, npages - 1);
     lds_load4(bt + idx, lds_offset(&ids_lds[c & 1][64 * wave]));
   };
   auto issue_tile = [&](int t, int slot) {
     const int tt = min(t, t_last);  // past the last tile: harmless re-load of it
     const int rel = tt - t_first;
     const int* idr = &ids_lds[(rel / kIdTiles) & 1][(rel % kIdTiles) * kTilePages];
-    // each lane reads the page id its own loads need (lane-varying LDS reads)
 #pragma unroll
-    for (int j = 0; j < KW; ++j) {
-      const int64_t tileg = (int64_t)idr[k_page[j]] * hkv + g;
-      lds_load16(a.k_pages + tileg * kPage * D + k_off[j],
-                 lds_offset(&lds[slot][LY::K_OFF + 1024 * (wave * KW + j)]));
+    for (int j = 0; j < LY::KW; ++j) {
+      const int u = (wave + kWaves * j) % (LY::K_CHUNKS / kWave);
+      const int sch = 64 * u + lane;
+      const int i = sch / LY::KP;
+      const int c = sch % LY::KP;
+      const int key = tile_key(i);
+      const int64_t tileg = (int64_t)idr[key / kPage] * hkv + g;
+      const int col = c < LY::NC ? c : 0;  // pad chunk: any valid bytes
+      lds_load16(a.k_pages + (tileg * kPage + key % kPage) * D + 16 * col,
+                 lds_offset(&lds[slot][LY::K_OFF + 1024 * u]));
     }
 #pragma unroll
-    for (int j = 0; j < VW; ++j) {
-      const int64_t tileg = (int64_t)idr[v_page[j]] * hkv + g;
-      lds_load16(a.v_pages + tileg * D * kPage + v_off[j],
-                 lds_offset(&lds[slot][LY::VT_OFF + 1024 * (wave * VW + j)]));
+    for (int j = 0; j < LY::VW; ++j) {
+      const int u = (wave + kWaves * j) % (LY::VT_CHUNKS / kWave);
+      const int sch = 64 * u + lane;
+      const int d = sch / 5;
+      const int x = sch % 5;
+      const int page = x < 4 ? 2 * (x % 2) + x / 2 : 0;
+      const int64_t tileg = (int64_t)idr[page] * hkv + g;
+      lds_load16(a.v_pages + (tileg * D + d) * kPage,
+                 lds_offset(&lds[slot][LY::VT_OFF + 1024 * u]));
     }
-    if constexpr (kPTH) {
-      if (wave < 2) {
-        const int64_t idx = ((int64_t)idr[sc_page] * hkv + g) * kPage + sc_tok;
-        const float* src = wave == 0 ? a.k_scales : a.v_scales;
-        lds_load4(src + idx, lds_offset(&lds[slot][wave == 0 ? LY::KS_OFF : LY::VS_OFF]));
-      }
+    if constexpr (kPTH) {  // waves 0/2: K scales, 1/3: V scales (2 and 3 repeat)
+      const int64_t idx = ((int64_t)idr[lane / kPage] * hkv + g) * kPage + lane % kPage;
+      const bool kside = wave % 2 == 0;
+      lds_load4((kside ? a.k_scales : a.v_scales) + idx,
+                lds_offset(&lds[slot][kside ? LY::KS_OFF : LY::VS_OFF]));
     }
   };
-
-  // ---- query codes: B operand of S^T = K . Q^T -----------------------------------
-  // lane holds row `row`, dims 64 ks + 32 grp + 0..31 as 32 e4m3 codes per step.
-  v8i qb[KS];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)(q0 + min(p_loc, n - 1)) * Hq + g * G + hh) * D;
-    const bool unit_q = a.q_scale == 1.0f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4* src = reinterpret_cast<const uint4*>(qrow + 64 * ks + 32 * grp);
-      uint32_t w[8];
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const uint4 x = src[c4];
-        const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t bits = (xs[2 * h + e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-            const float f = bf16_bits_to_float(bits);
-            const uint32_t code = unit_q ? e4m3_encode(f) : e4m3_quantize(f, a.q_scale);
-            word |= (row_ok ? code : 0u) << (8 * e);
-          }
-          w[2 * c4 + h] = word;
-        }
-      }
-      qb[ks] = (v8i){(int)w[0], (int)w[1], (int)w[2], (int)w[3],
-                     (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-    }
-  }
-  const float qk_base = a.q_scale * a.sm_log2 * (kPTH ? 1.0f : a.k_scale);
-  // P' = p * (v_scale_j / (v_ref * prob_scale)) never exceeds 448 when p <= 2^8 and
-  // prob_scale >= 2^8 / 448; below that P' is clamped
-  const bool clamp_p = a.prob_scale < 256.0f / kE4m3Max;
-
-  // Wait for this wave's loads of the next tile (the loads of the kNewer tiles issued
-  // after it may stay in flight), then make every wave's loads visible.
+  // Wait for this wave's loads of the next tile (the loads of the tiles issued after
+  // it may stay in flight), then make every wave's loads visible.
   auto wait_tile = [&]() {
-    constexpr int kNewer = kStages - 2;
-    if (kPTH && wave < 2) wait_vmcnt<(KW + VW + 1) * kNewer>();
-    else wait_vmcnt<(KW + VW) * kNewer>();
+    wait_vmcnt<PER_TILE * (kStages - 2)>();
     __builtin_amdgcn_s_barrier();
   };
-  // Slots past the sequence end of the last page were never written (any bytes, NaN
-  // included): zero their V bytes and scales before anyone reads the tile.
+  // Slots past the sequence end were never written (any bytes, NaN included): zero
+  // their V bytes and scales before anyone reads the tile.
   auto scrub_tile = [&](int t, uint8_t* st) {
     const int valid = L - t * kTile;  // keys of the tile below the sequence end
     if (valid >= kTile) return;
-    for (int ch = tid; ch < LY::V_INSTR * kWave; ch += kThreads) {
-      const int d = ch / 4;
-      const int x = (ch % 4) ^ ((d >> 2) & 3);
+    for (int ch = tid; ch < LY::VT_CHUNKS; ch += kThreads) {
+      const int x = ch % 5;
+      if (x == 4) continue;
       const int page = 2 * (x % 2) + x / 2;
       const int keep = min(max(valid - page * kPage, 0), kPage);  // tokens kept
       if (keep < kPage) {
@@ -347,16 +299,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
     }
     barrier_lds();
   };
+  const float qk_base = a.q_scale * a.sm_log2 * (kPTH ? 1.0f : a.k_scale);
   // Wave 0 derives the per-key factors of a resident tile; v_ref (the running V
-  // scale maximum) moves here, in key order, so every wave sees the same sequence.
-  float vref_run = kPTH ? 0.0f : a.v_scale;
+  // scale maximum) moves here, tile by tile, so every wave sees the same sequence.
+  float vref_run = 0.0f;
   auto derive_tile = [&](uint8_t* st) {
     if constexpr (kPTH) {
       if (wave == 0) {
         const float ks = reinterpret_cast<const float*>(st + LY::KS_OFF)[lane];
         const float vs = reinterpret_cast<const float*>(st + LY::VS_OFF)[lane];
-        const float vm = wave_max(vs);
-        vref_run = fmaxf(vref_run, vm);
+        vref_run = fmaxf(vref_run, wave_max(vs));
         const float f = vref_run > 0.0f ? vs / (vref_run * a.prob_scale) : 0.0f;
         reinterpret_cast<float*>(st + LY::CF_OFF)[lane] = ks * qk_base;
         reinterpret_cast<float*>(st + LY::FV_OFF)[lane] = f;
@@ -366,6 +318,43 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
     }
   };
 
+  // ---- query codes: B operand of S^T = K . Q^T -----------------------------------
+  // lane holds row `row`, dims 64 ks + 32 grp + 0..31 as 32 e4m3 codes per step.
+  v8i qb[KS];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)(q0 + min(p_loc, n - 1)) * Hq + g * G + hh) * D;
+    auto quantise = [&](auto enc) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4* src = reinterpret_cast<const uint4*>(qrow + 64 * ks + 32 * grp);
+        uint32_t w[8];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const uint4 x = src[c4];
+          const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t bits = (xs[2 * h + e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+              word |= enc(bf16_bits_to_float(bits)) << (8 * e);
+            }
+            w[2 * c4 + h] = row_ok ? word : 0u;
+          }
+        }
+        qb[ks] = (v8i){(int)w[0], (int)w[1], (int)w[2], (int)w[3],
+                       (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+      }
+    };
+    // x / 1.0 == x exactly, so a unit scale skips the division
+    if (a.q_scale == 1.0f) quantise([](float f) { return e4m3_encode(f); });
+    else quantise([&](float f) { return e4m3_quantize(f, a.q_scale); });
+  }
+  // P' = p * (v_scale_j / (v_ref * prob_scale)) never exceeds 448 when p <= 2^8 and
+  // prob_scale >= 2^8 / 448; below that P' is clamped
+  const bool clamp_p = a.prob_scale < 256.0f / kE4m3Max;
+
   // ---- running state ---------------------------------------------------------------
   v16f o[DB];
 #pragma unroll
@@ -373,6 +362,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
   float m = -INFINITY;   // reference row maximum (log2 units), same in both lane halves
   float lam = 0.0f;      // this lane's part of the row sum (in p units)
   float vref = kPTH ? 0.0f : a.v_scale;  // v_ref the accumulator is expressed in
+  // per-lane operand bases inside a stage
+  const int k_lane = 16 * (row * LY::KP + 2 * grp);
+  const int v_lane = LY::VT_OFF + 16 * (5 * row + 2 * grp);
+  const int s_lane = 4 * 16 * grp;
 
   // prologue: page ids of the first chunk, then tiles t_first .. t_first + kStages - 2
   // in flight, the first resident
@@ -381,17 +374,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
   barrier_lds();
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s) issue_tile(t_first + s, s);
-  {
-    // the first tile: wait for everything issued so far except the newer tiles
-    wait_tile();
-    scrub_tile(t_first, lds[0]);
-    derive_tile(lds[0]);
-    barrier_lds();
-  }
+  wait_tile();
+  scrub_tile(t_first, lds[0]);
+  derive_tile(lds[0]);
+  barrier_lds();
 
   for (int t = t_first; t <= t_last; ++t) {
     const int slot = (t - t_first) % kStages;
-    uint8_t* buf = lds[slot];
+    const uint8_t* buf = lds[slot];
     if ((t - t_first) % kIdTiles == 0) issue_ids((t - t_first) / kIdTiles + 1);
     issue_tile(t + kStages - 1, (t - t_first + kStages - 1) % kStages);
 
@@ -400,119 +390,128 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = (v16f){};
-      const int i = 32 * kb + row;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int c0 = 4 * ks + 2 * grp;
-        const uint4 x0 = *reinterpret_cast<const uint4*>(
-            buf + LY::K_OFF + 16 * (i * LY::NC + ((c0) ^ (i % LY::NC))));
-        const uint4 x1 = *reinterpret_cast<const uint4*>(
-            buf + LY::K_OFF + 16 * (i * LY::NC + ((c0 + 1) ^ (i % LY::NC))));
+        const int off = LY::K_OFF + k_lane + 16 * (32 * kb * LY::KP + 4 * ks);
+        const uint4 x0 = lds_read<uint4>(buf, off);
+        const uint4 x1 = lds_read<uint4>(buf, off + 16);
         const v8i ka = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                         (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         s[kb] = mfma(ka, qb[ks], s[kb]);
       }
     }
 
-    // ---- v_ref of this tile (per-token-head): rescale the accumulator if it grew ----
-    if constexpr (kPTH) {
-      const float vr = reinterpret_cast<const float*>(buf + LY::VREF_OFF)[0];
-      if (vr > vref) {
-        const float f = vref > 0.0f ? vref / vr : 0.0f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= f;
-        vref = vr;
-      }
-    }
-
-    // ---- scale, mask, lazy rescale -----------------------------------------------
+    // ---- scale, mask ----------------------------------------------------------------
     // lane group grp, register r of key block kb holds key 32 kb + 16 grp + r
     const int kbase = t * kTile;
     const bool need_mask = (kbase + kTile - 1 > w_hi_min) || (kbase < w_lo_max) ||
                            (kbase + kTile > L);
-    const float* cf = reinterpret_cast<const float*>(buf + LY::CF_OFF);
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int k0 = 32 * kb + 16 * grp + 4 * q4;
         float4 c4;
-        if constexpr (kPTH) c4 = *reinterpret_cast<const float4*>(cf + k0);
-        else c4 = make_float4(qk_base, qk_base, qk_base, qk_base);
+        if constexpr (kPTH)
+          c4 = lds_read<float4>(buf, LY::CF_OFF + s_lane + 4 * (32 * kb + 4 * q4));
+        else
+          c4 = make_float4(qk_base, qk_base, qk_base, qk_base);
         const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = s[kb][4 * q4 + e] * cc[e];
-          if (need_mask) {
-            const int key = kbase + k0 + e;
-            x = (key >= lo && key <= hi && row_ok) ? x : -INFINITY;
-          }
-          s[kb][4 * q4 + e] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int e = 0; e < 4; ++e) s[kb][4 * q4 + e] *= cc[e];
       }
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + 32 * kb + 16 * grp + r;
+          s[kb][r] = (key >= lo && key <= hi && row_ok) ? s[kb][r] : -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+
+    // ---- rescale the accumulator when v_ref grew or a score passed m + slack -------
+    float fo = 1.0f;  // factor for o
+    if constexpr (kPTH) {
+      const float vr = lds_read<float>(buf, LY::VREF_OFF);
+      if (vr > vref) {
+        fo = vref > 0.0f ? vref / vr : 0.0f;
+        vref = vr;
+      }
+    }
     if (__builtin_amdgcn_ballot_w64(mx > m + kSlack) != 0) {
       const float rmax = fmaxf(mx, __shfl_xor(mx, kRows));
       const float mn = fmaxf(m, rmax);
       const float alpha = (m == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      fo *= alpha;
       lam *= alpha;
       m = mn;
+    }
+    if (__builtin_amdgcn_ballot_w64(fo != 1.0f) != 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        asm volatile("" : "+a"(o[db]));
+        o[db] *= fo;
+        asm volatile("" : "+a"(o[db]));
+      }
     }
     const float msafe = m == -INFINITY ? 0.0f : m;
 
     // ---- P' (e4m3) in the B-operand layout; row sum from the rounded values -------
-    const float* fv = reinterpret_cast<const float*>(buf + LY::FV_OFF);
-    const float* iv = reinterpret_cast<const float*>(buf + LY::IF_OFF);
     const float pmul = 1.0f / a.prob_scale;
     uint32_t pw[8];
+    auto make_p = [&](bool clamp) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int k0 = 32 * kb + 16 * grp + 4 * q4;
-        float f[4] = {pmul, pmul, pmul, pmul}, fi[4] = {a.prob_scale, a.prob_scale,
-                                                        a.prob_scale, a.prob_scale};
-        if constexpr (kPTH) {
-          const float4 v4 = *reinterpret_cast<const float4*>(fv + k0);
-          const float4 i4 = *reinterpret_cast<const float4*>(iv + k0);
-          f[0] = v4.x; f[1] = v4.y; f[2] = v4.z; f[3] = v4.w;
-          fi[0] = i4.x; fi[1] = i4.y; fi[2] = i4.z; fi[3] = i4.w;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float f[4] = {pmul, pmul, pmul, pmul};
+          float fi[4] = {a.prob_scale, a.prob_scale, a.prob_scale, a.prob_scale};
+          if constexpr (kPTH) {
+            const int so = s_lane + 4 * (32 * kb + 4 * q4);
+            const float4 v4 = lds_read<float4>(buf, LY::FV_OFF + so);
+            const float4 i4 = lds_read<float4>(buf, LY::IF_OFF + so);
+            f[0] = v4.x; f[1] = v4.y; f[2] = v4.z; f[3] = v4.w;
+            fi[0] = i4.x; fi[1] = i4.y; fi[2] = i4.z; fi[3] = i4.w;
+          }
+          float pq[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = __builtin_amdgcn_exp2f(s[kb][4 * q4 + e] - msafe);
+            pq[e] = clamp ? fminf(p * f[e], kE4m3Max) : p * f[e];
+          }
+          uint32_t word = __builtin_amdgcn_cvt_pk_fp8_f32(pq[0], pq[1], 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(pq[2], pq[3], word, true);
+          pw[4 * kb + q4] = word;
+          const float2_t d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+          const float2_t d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+          lam = fmaf(d01.x, fi[0], lam);
+          lam = fmaf(d01.y, fi[1], lam);
+          lam = fmaf(d23.x, fi[2], lam);
+          lam = fmaf(d23.y, fi[3], lam);
         }
-        float pq[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(s[kb][4 * q4 + e] - msafe);
-          pq[e] = p * f[e];
-          if (clamp_p) pq[e] = fminf(pq[e], kE4m3Max);
-        }
-        uint32_t word = __builtin_amdgcn_cvt_pk_fp8_f32(pq[0], pq[1], 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(pq[2], pq[3], word, true);
-        pw[4 * kb + q4] = word;
-        const float2_t d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
-        const float2_t d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
-        lam = fmaf(d01.x, fi[0], lam);
-        lam = fmaf(d01.y, fi[1], lam);
-        lam = fmaf(d23.x, fi[2], lam);
-        lam = fmaf(d23.y, fi[3], lam);
-      }
+    };
+    if (clamp_p) make_p(true);
+    else make_p(false);
     const v8i pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
                     (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
 
     // ---- O^T += V^T . P'^T -------------------------------------------------------------
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int d = 32 * db + row;
-      const int sw = (d >> 2) & 3;
-      const uint4 x0 = *reinterpret_cast<const uint4*>(
-          buf + LY::VT_OFF + 16 * (4 * d + ((2 * grp + 0) ^ sw)));
-      const uint4 x1 = *reinterpret_cast<const uint4*>(
-          buf + LY::VT_OFF + 16 * (4 * d + ((2 * grp + 1) ^ sw)));
+      const int off = v_lane + 16 * 5 * 32 * db;
+      const uint4 x0 = lds_read<uint4>(buf, off);
+      const uint4 x1 = lds_read<uint4>(buf, off + 16);
       const v8i va = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                       (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
       o[db] = mfma(va, pb, o[db]);
+      // keep the accumulator in AGPRs across iterations: the (rare) rescale then
+      // copies it out and back, instead of every iteration copying it to VGPRs
+      asm volatile("" : "+a"(o[db]));
     }
 
     // ---- next tile resident: wait, scrub its unwritten slots, derive its factors ---
