@@ -46,6 +46,7 @@ namespace pf {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
@@ -74,7 +75,8 @@ __device__ __forceinline__ int tile_key(int i) {
   return 32 * (i / 32) + 16 * ((j / 4) % 2) + 4 * (j / 8) + j % 4;
 }
 
-constexpr int kStages = 3;  // tiles resident: one computed, kStages - 1 in flight
+// Pipeline depth: tile t is in softmax/PV, t + 1 in QK, t + 2 and t + 3 in flight.
+constexpr int kStages = 4;
 // Block-table entries are fetched into LDS by direct loads, kIdTiles tiles' worth at a
 // time, one chunk ahead of use.  (Reading them with vector loads inside the tile loop
 // would put them in the same in-order completion count as the tile loads and force
@@ -83,26 +85,28 @@ constexpr int kIdTiles = 64;
 static_assert(kIdTiles * kTilePages == kThreads, "one page id per thread per chunk");
 
 // LDS layout of one pipeline stage.  Every region is an array of 16-byte chunks
-// written by direct global->LDS loads: load instruction u fills chunks 64 u .. 64 u
-// + 63, one per lane, so placement is chosen through the address each lane fetches.
-//   K:  row i (MFMA row, key tile_key(i)) at chunks i * KP .. + NC - 1 (chunk c =
-//       bytes 16c .. 16c+15 of the key); KP = NC + 1: the pad chunk per row spreads
-//       16 consecutive rows over all 64 banks, and keeps every operand address an
-//       immediate offset from one per-lane base.
-//   VT: channel d at chunks 5 d .. 5 d + 3: chunk 2 gg + kb = the 16 tokens of channel
-//       d of page 2 kb + gg, then one pad chunk (same bank argument).
+// written by direct global->LDS loads: one load instruction writes 64 consecutive
+// chunks, one per lane.  Each load instruction reads from a single page, so its
+// global address is that page's base (scalar registers) plus a per-lane offset that
+// does not change from tile to tile.
+//   K:  page p (tile keys 16 p .. 16 p + 15) at chunks p * KPC + [0, 16 NC); token t,
+//       dim chunk c (bytes 16 c .. 16 c + 15) at NC t + 2 ((c / 2) ^ phi(t)) + c % 2.
+//       The XOR on 32-byte pairs and the odd page stride KPC = 16 NC + 1 put the
+//       16 rows one operand read touches (8 tokens of 2 pages, one chunk each) on
+//       16 different bank groups.
+//   VT: page p, channel d at chunk p * D + d: the page's 16 tokens of that channel.
 //   KS, VS: the 64 keys' K and V scales (per-token-head mode).
 //   CF, FV, IF: per-key factors derived by wave 0 from KS/VS: score multiplier
 //       k_scale * q_scale * softmax_scale * log2(e), P' factor v_scale / (v_ref *
 //       prob_scale) and its reciprocal; VREF: v_ref after this tile.
 template <int D>
 struct Layout {
-  static constexpr int NC = D / 16;
-  static constexpr int KP = NC + 1;
+  static constexpr int NC = D / 16;            // 16-byte chunks per key row
+  static constexpr int KPC = 16 * NC + 1;      // chunk stride of K pages
   static constexpr int K_OFF = 0;
-  static constexpr int K_CHUNKS = kTile * KP;
+  static constexpr int K_CHUNKS = kTilePages * KPC;
   static constexpr int VT_OFF = K_OFF + 16 * K_CHUNKS;
-  static constexpr int VT_CHUNKS = 5 * D;
+  static constexpr int VT_CHUNKS = kTilePages * D;
   static constexpr int KS_OFF = VT_OFF + 16 * VT_CHUNKS;
   static constexpr int VS_OFF = KS_OFF + kTile * 4;
   static constexpr int CF_OFF = VS_OFF + kTile * 4;
@@ -110,11 +114,14 @@ struct Layout {
   static constexpr int IF_OFF = FV_OFF + kTile * 4;
   static constexpr int VREF_OFF = IF_OFF + kTile * 4;
   static constexpr int BYTES = VREF_OFF + 16;
-  // load instructions per wave per tile (the totals rounded up to the wave count;
-  // the extra instructions repeat earlier ones, writing the same bytes again)
-  static constexpr int KW = (K_CHUNKS / kWave + kWaves - 1) / kWaves;
-  static constexpr int VW = (VT_CHUNKS / kWave + kWaves - 1) / kWaves;
-  static_assert(K_CHUNKS % kWave == 0 && VT_CHUNKS % kWave == 0, "chunk counts");
+  // load instructions per page for K and for V (64 chunks each), and per wave per
+  // tile for each
+  static constexpr int PI = 16 * NC / kWave;
+  static constexpr int W = kTilePages * PI / kWaves;
+  static_assert(16 * NC == D && D % kWave == 0 && W >= 1, "head_dim");
+  static_assert(kWaves % PI == 0, "instruction split");
+  // pair swizzle of token t (keeps a 32-byte pair contiguous)
+  static __device__ __forceinline__ int phi(int t) { return (t / (16 / NC)) % (NC / 2); }
 };
 
 struct PrefillArgs {
@@ -142,6 +149,11 @@ struct PrefillArgs {
 __device__ __forceinline__ void lds_load16(const void* src, uint32_t lds_off) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds_off) : "memory", "m0");
+}
+// The same with a uniform 64-bit base in scalar registers and a 32-bit per-lane offset.
+__device__ __forceinline__ void lds_load16s(const void* base, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds_off) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_load4(const void* src, uint32_t lds_off) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
@@ -179,10 +191,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
   constexpr int NP = kWgRows / G;  // query positions per workgroup
   constexpr int KS = D / 64;       // 64-dim steps of the QK contraction
   constexpr int DB = D / 32;       // 32-dim blocks of the output
-  constexpr int PER_TILE = LY::KW + LY::VW + (kPTH ? 1 : 0);  // loads per wave per tile
+  constexpr int PER_TILE = 2 * LY::W + (kPTH ? 1 : 0);  // loads per wave per tile
   __shared__ __align__(16) uint8_t lds[kStages][LY::BYTES];
   // physical page ids of the workgroup's tiles, kIdTiles tiles per chunk, two chunks
-  __shared__ int ids_lds[2][kIdTiles * kTilePages];
+  __shared__ __align__(16) int ids_lds[2][kIdTiles * kTilePages];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -232,35 +244,42 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
     const int idx = min((t_first + kIdTiles * c) * kTilePages + tid, npages - 1);
     lds_load4(bt + idx, lds_offset(&ids_lds[c & 1][64 * wave]));
   };
+  // Wave w issues load instructions w, w + 4, ... of the tile's K and V: instruction
+  // q covers page q / PI, 64-chunk block jj = q % PI of it (jj is the same for all of
+  // a wave's instructions).  Per-lane offsets inside the page:
+  const int jj = wave % LY::PI;
+  uint32_t k_voff;
+  {
+    const int o = 64 * jj + lane;  // chunk inside the K page
+    const int t = o / LY::NC, r = o % LY::NC;
+    const int c = 2 * ((r / 2) ^ LY::phi(t)) + r % 2;
+    k_voff = (uint32_t)((t - 64 * jj / LY::NC) * D + 16 * c);
+  }
+  const uint32_t v_voff = 16u * lane;
   auto issue_tile = [&](int t, int slot) {
     const int tt = min(t, t_last);  // past the last tile: harmless re-load of it
     const int rel = tt - t_first;
-    const int* idr = &ids_lds[(rel / kIdTiles) & 1][(rel % kIdTiles) * kTilePages];
+    // the tile's four page ids in one read, made uniform; (page, head) byte offsets
+    // (K and V pages of one head have the same size, 16 D bytes)
+    const int4 id4 = *reinterpret_cast<const int4*>(
+        &ids_lds[(rel / kIdTiles) & 1][(rel % kIdTiles) * kTilePages]);
+    const int ids[4] = {__builtin_amdgcn_readfirstlane(id4.x), __builtin_amdgcn_readfirstlane(id4.y),
+                        __builtin_amdgcn_readfirstlane(id4.z), __builtin_amdgcn_readfirstlane(id4.w)};
 #pragma unroll
-    for (int j = 0; j < LY::KW; ++j) {
-      const int u = (wave + kWaves * j) % (LY::K_CHUNKS / kWave);
-      const int sch = 64 * u + lane;
-      const int i = sch / LY::KP;
-      const int c = sch % LY::KP;
-      const int key = tile_key(i);
-      const int64_t tileg = (int64_t)idr[key / kPage] * hkv + g;
-      const int col = c < LY::NC ? c : 0;  // pad chunk: any valid bytes
-      lds_load16(a.k_pages + (tileg * kPage + key % kPage) * D + 16 * col,
-                 lds_offset(&lds[slot][LY::K_OFF + 1024 * u]));
-    }
-#pragma unroll
-    for (int j = 0; j < LY::VW; ++j) {
-      const int u = (wave + kWaves * j) % (LY::VT_CHUNKS / kWave);
-      const int sch = 64 * u + lane;
-      const int d = sch / 5;
-      const int x = sch % 5;
-      const int page = x < 4 ? 2 * (x % 2) + x / 2 : 0;
-      const int64_t tileg = (int64_t)idr[page] * hkv + g;
-      lds_load16(a.v_pages + (tileg * D + d) * kPage,
-                 lds_offset(&lds[slot][LY::VT_OFF + 1024 * u]));
+    for (int j = 0; j < LY::W; ++j) {
+      const int pg = (kWaves / LY::PI) * j + wave / LY::PI;  // (wave + 4 j) / PI
+      const int id = pg == 0 ? ids[0] : pg == 1 ? ids[1] : pg == 2 ? ids[2] : ids[3];
+      const uint64_t off = (uint64_t)(uint32_t)(id * hkv + g) * (uint64_t)(16 * D) +
+                           (uint64_t)(1024 * jj);
+      lds_load16s(a.k_pages + off, k_voff,
+                  lds_offset(&lds[slot][LY::K_OFF + 16 * (pg * LY::KPC + 64 * jj)]));
+      lds_load16s(a.v_pages + off, v_voff,
+                  lds_offset(&lds[slot][LY::VT_OFF + 16 * (pg * D + 64 * jj)]));
     }
     if constexpr (kPTH) {  // waves 0/2: K scales, 1/3: V scales (2 and 3 repeat)
-      const int64_t idx = ((int64_t)idr[lane / kPage] * hkv + g) * kPage + lane % kPage;
+      const int page = lane / kPage;
+      const int id = page == 0 ? id4.x : page == 1 ? id4.y : page == 2 ? id4.z : id4.w;
+      const int64_t idx = ((int64_t)id * hkv + g) * kPage + lane % kPage;
       const bool kside = wave % 2 == 0;
       lds_load4((kside ? a.k_scales : a.v_scales) + idx,
                 lds_offset(&lds[slot][kside ? LY::KS_OFF : LY::VS_OFF]));
@@ -278,10 +297,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
     const int valid = L - t * kTile;  // keys of the tile below the sequence end
     if (valid >= kTile) return;
     for (int ch = tid; ch < LY::VT_CHUNKS; ch += kThreads) {
-      const int x = ch % 5;
-      if (x == 4) continue;
-      const int page = 2 * (x % 2) + x / 2;
-      const int keep = min(max(valid - page * kPage, 0), kPage);  // tokens kept
+      const int keep = min(max(valid - (ch / D) * kPage, 0), kPage);  // tokens kept
       if (keep < kPage) {
         uint32_t* w = reinterpret_cast<uint32_t*>(st + LY::VT_OFF + 16 * ch);
 #pragma unroll
@@ -309,10 +325,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
         const float ks = reinterpret_cast<const float*>(st + LY::KS_OFF)[lane];
         const float vs = reinterpret_cast<const float*>(st + LY::VS_OFF)[lane];
         vref_run = fmaxf(vref_run, wave_max(vs));
-        const float f = vref_run > 0.0f ? vs / (vref_run * a.prob_scale) : 0.0f;
+        // P' factor and its reciprocal (hardware reciprocals: any f works as long as
+        // the row sum maps P' back with the same f, up to rounding)
+        const float f = vref_run > 0.0f ? vs * __builtin_amdgcn_rcpf(vref_run * a.prob_scale)
+                                        : 0.0f;
         reinterpret_cast<float*>(st + LY::CF_OFF)[lane] = ks * qk_base;
         reinterpret_cast<float*>(st + LY::FV_OFF)[lane] = f;
-        reinterpret_cast<float*>(st + LY::IF_OFF)[lane] = f > 0.0f ? 1.0f / f : 0.0f;
+        reinterpret_cast<float*>(st + LY::IF_OFF)[lane] = f > 0.0f ? __builtin_amdgcn_rcpf(f) : 0.0f;
         if (lane == 0) reinterpret_cast<float*>(st + LY::VREF_OFF)[0] = vref_run;
       }
     }
@@ -351,186 +370,289 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
     if (a.q_scale == 1.0f) quantise([](float f) { return e4m3_encode(f); });
     else quantise([&](float f) { return e4m3_quantize(f, a.q_scale); });
   }
-  // P' = p * (v_scale_j / (v_ref * prob_scale)) never exceeds 448 when p <= 2^8 and
-  // prob_scale >= 2^8 / 448; below that P' is clamped
-  const bool clamp_p = a.prob_scale < 256.0f / kE4m3Max;
 
   // ---- running state ---------------------------------------------------------------
   v16f o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = (v16f){};
   float m = -INFINITY;   // reference row maximum (log2 units), same in both lane halves
-  float lam = 0.0f;      // this lane's part of the row sum (in p units)
+  // this lane's part of the row sum: p units (per-token-head mode) or P' units
+  // (per-tensor mode, where P' = p / prob_scale for every key)
+  float lam = 0.0f;
   float vref = kPTH ? 0.0f : a.v_scale;  // v_ref the accumulator is expressed in
   // per-lane operand bases inside a stage
-  const int k_lane = 16 * (row * LY::KP + 2 * grp);
-  const int v_lane = LY::VT_OFF + 16 * (5 * row + 2 * grp);
-  const int s_lane = 4 * 16 * grp;
-
-  // prologue: page ids of the first chunk, then tiles t_first .. t_first + kStages - 2
-  // in flight, the first resident
-  issue_ids(0);
-  wait_vmcnt<0>();
-  barrier_lds();
+  // K operand: MFMA row `row` of key block kb is key tile_key(32 kb + row): page
+  // 2 kb + (row / 4) % 2, token 4 (row / 8) + row % 4; dim step ks reads chunks
+  // 4 ks + 2 grp and the next (one 32-byte pair).  Key block 1 is two pages on.
+  int k_addr[KS];
+  {
+    const int tr = 4 * (row / 8) + row % 4;
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue_tile(t_first + s, s);
-  wait_tile();
-  scrub_tile(t_first, lds[0]);
-  derive_tile(lds[0]);
-  barrier_lds();
+    for (int ks = 0; ks < KS; ++ks)
+      k_addr[ks] = LY::K_OFF + 16 * (((row / 4) % 2) * LY::KPC + LY::NC * tr +
+                                     2 * ((2 * ks + grp) ^ LY::phi(tr)));
+  }
+  constexpr int K_KB = 16 * 2 * LY::KPC;
+  // V^T operand: channel 32 db + row; bytes 0-15 = page grp, 16-31 = page 2 + grp
+  const int v_lane = LY::VT_OFF + 16 * (grp * D + row);
+  constexpr int V_HI = 16 * 2 * D;
+  const int s_lane = 4 * 16 * grp;
+  const float pmul = 1.0f / a.prob_scale;
 
-  for (int t = t_first; t <= t_last; ++t) {
-    const int slot = (t - t_first) % kStages;
-    const uint8_t* buf = lds[slot];
-    if ((t - t_first) % kIdTiles == 0) issue_ids((t - t_first) / kIdTiles + 1);
-    issue_tile(t + kStages - 1, (t - t_first + kStages - 1) % kStages);
-
-    // ---- S^T = K . Q^T for the two 32-key blocks --------------------------------
-    v16f s[2];
+  // S^T = K . Q^T of a resident tile, for the two 32-key blocks
+  auto qk = [&](const uint8_t* buf, v16f (&sc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = (v16f){};
+      sc[kb] = (v16f){};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int off = LY::K_OFF + k_lane + 16 * (32 * kb * LY::KP + 4 * ks);
+        const int off = k_addr[ks] + K_KB * kb;
         const uint4 x0 = lds_read<uint4>(buf, off);
         const uint4 x1 = lds_read<uint4>(buf, off + 16);
         const v8i ka = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                         (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        s[kb] = mfma(ka, qb[ks], s[kb]);
+        sc[kb] = mfma(ka, qb[ks], sc[kb]);
       }
     }
+  };
 
-    // ---- scale, mask ----------------------------------------------------------------
-    // lane group grp, register r of key block kb holds key 32 kb + 16 grp + r
+  // Scores of a tile in log2 units relative to the current reference maximum,
+  // x = s * CF - msafe, for the 4 keys of group w (key block w / 4, registers
+  // 4 (w % 4) .. + 3).  Lane group grp, register r of key block kb holds key
+  // 32 kb + 16 grp + r.
+  auto scale_group = [&](int w, const uint8_t* buf, const v16f (&sc)[2], float msafe,
+                         float (&x)[32]) {
+    const int kb = w / 4, q4 = w % 4;
+    float4 c4;
+    if constexpr (kPTH)
+      c4 = lds_read<float4>(buf, LY::CF_OFF + s_lane + 16 * (8 * kb + q4));
+    else
+      c4 = make_float4(qk_base, qk_base, qk_base, qk_base);
+    const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * w + e] = fmaf(sc[kb][4 * q4 + e], cc[e], -msafe);
+  };
+  // Masks the keys of tile t a row must not see (-inf); returns the lane's maximum.
+  auto mask_max = [&](int t, float (&x)[32]) {
     const int kbase = t * kTile;
-    const bool need_mask = (kbase + kTile - 1 > w_hi_min) || (kbase < w_lo_max) ||
-                           (kbase + kTile > L);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float4 c4;
-        if constexpr (kPTH)
-          c4 = lds_read<float4>(buf, LY::CF_OFF + s_lane + 4 * (32 * kb + 4 * q4));
-        else
-          c4 = make_float4(qk_base, qk_base, qk_base, qk_base);
-        const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[kb][4 * q4 + e] *= cc[e];
-      }
-    if (need_mask) {
+    if ((kbase + kTile - 1 > w_hi_min) || (kbase < w_lo_max) || (kbase + kTile > L)) {
+      // visible keys relative to this lane's first key: element (kb, r) is key
+      // 32 kb + r of that range.  The empty asm keeps the per-key tests inside this
+      // (rarely taken) branch instead of hoisted into every tile.
+      int lo_r = lo - (kbase + 16 * grp);
+      int hi_r = hi - (kbase + 16 * grp);
+      if (!row_ok || hi_r < lo_r) lo_r = hi_r = 1 << 20;  // nothing visible
+      asm volatile("" : "+v"(lo_r), "+v"(hi_r));
+      const uint32_t span = (uint32_t)(hi_r - lo_r);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kbase + 32 * kb + 16 * grp + r;
-          s[kb][r] = (key >= lo && key <= hi && row_ok) ? s[kb][r] : -INFINITY;
+          const bool vis = (uint32_t)(32 * kb + r - lo_r) <= span;
+          x[16 * kb + r] = vis ? x[16 * kb + r] : -INFINITY;
         }
     }
+    float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, x[i]);
+    return mx;
+  };
 
-    // ---- rescale the accumulator when v_ref grew or a score passed m + slack -------
-    float fo = 1.0f;  // factor for o
-    if constexpr (kPTH) {
-      const float vr = lds_read<float>(buf, LY::VREF_OFF);
-      if (vr > vref) {
-        fo = vref > 0.0f ? vref / vr : 0.0f;
-        vref = vr;
-      }
-    }
-    if (__builtin_amdgcn_ballot_w64(mx > m + kSlack) != 0) {
-      const float rmax = fmaxf(mx, __shfl_xor(mx, kRows));
-      const float mn = fmaxf(m, rmax);
-      const float alpha = (m == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
-      fo *= alpha;
-      lam *= alpha;
-      m = mn;
-    }
-    if (__builtin_amdgcn_ballot_w64(fo != 1.0f) != 0) {
+  // prologue: page ids of the first chunk; tiles t_first .. t_first + kStages - 2 in
+  // flight; the first two made resident
+  issue_ids(0);
+  wait_vmcnt<0>();
+  barrier_lds();
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        asm volatile("" : "+a"(o[db]));
-        o[db] *= fo;
-        asm volatile("" : "+a"(o[db]));
-      }
-    }
-    const float msafe = m == -INFINITY ? 0.0f : m;
+  for (int st = 0; st < kStages - 1; ++st) issue_tile(t_first + st, st);
+  wait_vmcnt<PER_TILE * (kStages - 2)>();
+  __builtin_amdgcn_s_barrier();
+  scrub_tile(t_first, lds[0]);
+  derive_tile(lds[0]);
+  barrier_lds();
+  if (t_first < t_last) {
+    wait_vmcnt<PER_TILE * (kStages - 3)>();
+    __builtin_amdgcn_s_barrier();
+    scrub_tile(t_first + 1, lds[1]);
+    derive_tile(lds[1]);
+    barrier_lds();
+  }
 
-    // ---- P' (e4m3) in the B-operand layout; row sum from the rounded values -------
-    const float pmul = 1.0f / a.prob_scale;
-    uint32_t pw[8];
-    auto make_p = [&](bool clamp) {
+  // The tile loop, specialised on how P' is formed from p: PM 0: p * factor; PM 1:
+  // the same clamped to the e4m3 maximum; PM 2: p itself (per-tensor mode with
+  // prob_scale 1).  Iteration t: the scores of tile t + 1 are computed on the matrix
+  // cores while the vector unit forms P' of tile t; then the P.V product of tile t
+  // runs while the row sum and the next tile's scaled scores are formed.
+  auto main_loop = [&](auto pm_tag) {
+    constexpr int PM = decltype(pm_tag)::value;
+    float x[32];
+    float mx;
+    uint32_t pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // P' codes of the current tile
+    {
+      v16f sc[2];
+      qk(lds[0], sc);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int w = 0; w < 8; ++w) scale_group(w, lds[0], sc, 0.0f, x);
+      mx = mask_max(t_first, x);
+    }
+    for (int t = t_first; t <= t_last; ++t) {
+      const int rel = t - t_first;
+      const uint8_t* buf = lds[rel % kStages];
+      const uint8_t* nbuf = lds[(rel + 1) % kStages];  // past the last tile: unused
+      if (rel % kIdTiles == 0) issue_ids(rel / kIdTiles + 1);
+      issue_tile(t + kStages - 1, (rel + kStages - 1) % kStages);
+
+      // ---- rescale when v_ref grew or a score passed the reference by the slack ----
+      float fo = 1.0f;  // factor for o
+      if constexpr (kPTH) {
+        const float vr = lds_read<float>(buf, LY::VREF_OFF);
+        if (vr > vref) {
+          fo = vref > 0.0f ? vref / vr : 0.0f;
+          vref = vr;
+        }
+      }
+      const bool first = m == -INFINITY;
+      if (__builtin_amdgcn_ballot_w64(mx > (first ? -INFINITY : kSlack)) != 0) {
+        const float rmax = fmaxf(mx, __shfl_xor(mx, kRows));  // whole row, relative
+        const float delta = first ? (rmax == -INFINITY ? 0.0f : rmax) : fmaxf(0.0f, rmax);
+        if (!first) {
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+          fo *= alpha;
+          lam *= alpha;
+        }
+        m = first ? rmax : m + delta;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
+        for (int i = 0; i < 32; ++i) x[i] -= delta;
+      }
+      if (__builtin_amdgcn_ballot_w64(fo != 1.0f) != 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          asm volatile("" : "+a"(o[db]));
+          o[db] *= fo;
+          asm volatile("" : "+a"(o[db]));
+        }
+      }
+
+      // ---- phase 1: S^T of tile t + 1 on the matrix cores; P' of tile t (e4m3, in the
+      // B-operand layout) on the vector unit.  Each chunk holds one MFMA (its operands
+      // read one chunk ahead) and a share of the vector work; scheduling barriers
+      // keep the chunks in order, so the two units overlap.
+      constexpr int NQK = 2 * KS;          // MFMAs of S^T per tile
+      constexpr int WQ = 8 / NQK;          // P' words per chunk
+      auto k_operand = [&](int i) {        // chunk i: key block i % 2, dim step i / 2
+        const int off = k_addr[i / 2] + K_KB * (i % 2);
+        const uint4 x0 = lds_read<uint4>(nbuf, off);
+        const uint4 x1 = lds_read<uint4>(nbuf, off + 16);
+        return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      };
+      v16f sn[2] = {(v16f){}, (v16f){}};
+      v8i ka = k_operand(0);
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) {
+        const v8i cur = ka;
+        if (i + 1 < NQK) ka = k_operand(i + 1);
+        sn[i % 2] = mfma(cur, qb[i / 2], sn[i % 2]);
+#pragma unroll
+        for (int w = WQ * i; w < WQ * (i + 1); ++w) {
+          const int kb = w / 4, q4 = w % 4;
           float f[4] = {pmul, pmul, pmul, pmul};
-          float fi[4] = {a.prob_scale, a.prob_scale, a.prob_scale, a.prob_scale};
           if constexpr (kPTH) {
-            const int so = s_lane + 4 * (32 * kb + 4 * q4);
-            const float4 v4 = lds_read<float4>(buf, LY::FV_OFF + so);
-            const float4 i4 = lds_read<float4>(buf, LY::IF_OFF + so);
+            const float4 v4 = lds_read<float4>(buf, LY::FV_OFF + s_lane + 16 * (8 * kb + q4));
             f[0] = v4.x; f[1] = v4.y; f[2] = v4.z; f[3] = v4.w;
-            fi[0] = i4.x; fi[1] = i4.y; fi[2] = i4.z; fi[3] = i4.w;
           }
           float pq[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p = __builtin_amdgcn_exp2f(s[kb][4 * q4 + e] - msafe);
-            pq[e] = clamp ? fminf(p * f[e], kE4m3Max) : p * f[e];
+            const float p = __builtin_amdgcn_exp2f(x[4 * w + e]);
+            if constexpr (PM == 2) pq[e] = p;
+            else if constexpr (PM == 1) pq[e] = fminf(p * f[e], kE4m3Max);
+            else pq[e] = p * f[e];
           }
-          uint32_t word = __builtin_amdgcn_cvt_pk_fp8_f32(pq[0], pq[1], 0, false);
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(pq[2], pq[3], word, true);
-          pw[4 * kb + q4] = word;
-          const float2_t d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
-          const float2_t d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
-          lam = fmaf(d01.x, fi[0], lam);
-          lam = fmaf(d01.y, fi[1], lam);
-          lam = fmaf(d23.x, fi[2], lam);
-          lam = fmaf(d23.y, fi[3], lam);
+          // the two conversions fill bytes 0-1 and 2-3; the old contents are dead
+          const uint32_t lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(pq[0], pq[1], pw[w], false);
+          pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(pq[2], pq[3], lo2, true);
         }
-    };
-    if (clamp_p) make_p(true);
-    else make_p(false);
-    const v8i pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
-                    (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const v8i pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
+                      (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
 
-    // ---- O^T += V^T . P'^T -------------------------------------------------------------
+      // ---- phase 2: O^T += V^T . P'^T on the matrix cores; the row sum of the rounded
+      // P' and the scaled scores of tile t + 1 on the vector unit ------------------------
+      constexpr int WV = 8 / DB;           // row-sum words / score groups per chunk
+      auto v_operand = [&](int db) {
+        const int off = v_lane + 16 * 32 * db;
+        const uint4 x0 = lds_read<uint4>(buf, off);
+        const uint4 x1 = lds_read<uint4>(buf, off + V_HI);
+        return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      };
+      const float msafe = m == -INFINITY ? 0.0f : m;
+      v8i va = v_operand(0);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int off = v_lane + 16 * 5 * 32 * db;
-      const uint4 x0 = lds_read<uint4>(buf, off);
-      const uint4 x1 = lds_read<uint4>(buf, off + 16);
-      const v8i va = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      o[db] = mfma(va, pb, o[db]);
-      // keep the accumulator in AGPRs across iterations: the (rare) rescale then
-      // copies it out and back, instead of every iteration copying it to VGPRs
-      asm volatile("" : "+a"(o[db]));
-    }
+      for (int db = 0; db < DB; ++db) {
+        const v8i cur = va;
+        if (db + 1 < DB) va = v_operand(db + 1);
+        o[db] = mfma(cur, pb, o[db]);
+        // keep the accumulator in AGPRs across iterations: the (rare) rescale then
+        // copies it out and back, instead of every iteration copying it to VGPRs
+        asm volatile("" : "+a"(o[db]));
+#pragma unroll
+        for (int w = WV * db; w < WV * (db + 1); ++w) {
+          if constexpr (kPTH) {
+            const float4 i4 = lds_read<float4>(buf, LY::IF_OFF + s_lane + 16 * (8 * (w / 4) + w % 4));
+            const float2_t d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], false);
+            const float2_t d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], true);
+            lam = fmaf(d01.x, i4.x, lam);
+            lam = fmaf(d01.y, i4.y, lam);
+            lam = fmaf(d23.x, i4.z, lam);
+            lam = fmaf(d23.y, i4.w, lam);
+          } else {
+            const half2_t h01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw[w], 1.0f, false);
+            const half2_t h23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw[w], 1.0f, true);
+            const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+            lam = __builtin_amdgcn_fdot2(h01, one, lam, false);
+            lam = __builtin_amdgcn_fdot2(h23, one, lam, false);
+          }
+          scale_group(w, nbuf, sn, msafe, x);  // past the last tile: unused
+        }
+        asm volatile("" : "+v"(lam));  // keeps the row sum in this chunk
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mx = mask_max(t + 1, x);
 
-    // ---- next tile resident: wait, scrub its unwritten slots, derive its factors ---
-    if (t < t_last) {
-      uint8_t* nb = lds[(t - t_first + 1) % kStages];
-      wait_tile();
-      scrub_tile(t + 1, nb);
-      derive_tile(nb);
+      // ---- tile t + 2 resident (issued two iterations ago): wait, scrub its unwritten
+      // slots, derive its factors.  The barrier also closes this iteration's reads of
+      // the slot the next iteration's load overwrites.
+      if (t + 2 <= t_last) {
+        uint8_t* nb = lds[(rel + 2) % kStages];
+        wait_vmcnt<PER_TILE * (kStages - 3)>();
+        __builtin_amdgcn_s_barrier();
+        scrub_tile(t + 2, nb);
+        derive_tile(nb);
+      }
       barrier_lds();
     }
+  };
+  if (a.prob_scale < 256.0f / kE4m3Max) {
+    // P' = p * v_scale_j / (v_ref * prob_scale) can pass 448 only when prob_scale <
+    // 2^8 / 448 (p <= 2^8, v_scale_j <= v_ref)
+    main_loop(std::integral_constant<int, 1>{});
+  } else if (!kPTH && a.prob_scale == 1.0f) {
+    main_loop(std::integral_constant<int, 2>{});
+  } else {
+    main_loop(std::integral_constant<int, 0>{});
   }
   // drain the loads still in flight (re-loads past the last tile) before exit
   wait_vmcnt<0>();
 
   // ---- normalise and store: lane holds row `row`, dims 32 db + 8 (r/4) + 4 grp + r%4
-  // O = sum_j P'_j v_code_j with P'_j ~ p_j v_scale_j / (v_ref prob_scale) (per-tensor:
-  // p_j / prob_scale), lam ~ sum_j p_j; out = O * v_ref * prob_scale / lam
+  // O = sum_j P'_j v_code_j with P'_j ~ p_j v_scale_j / (v_ref prob_scale) and lam ~
+  // sum_j p_j: out = O * v_ref * prob_scale / lam; per-tensor: P'_j ~ p_j / prob_scale
+  // and lam ~ sum_j P'_j, out = O * v_scale / lam
   const float lsum = lam + __shfl_xor(lam, kRows);
-  const float inv = lsum > 0.0f ? vref * a.prob_scale / lsum : 0.0f;
+  const float inv = lsum > 0.0f ? vref * (kPTH ? a.prob_scale : 1.0f) / lsum : 0.0f;
   if (row_ok) {
     const int64_t orow = ((int64_t)(q0 + p_loc) * Hq + g * G + hh) * D;
 #pragma unroll
