@@ -96,9 +96,9 @@ static_assert(kIdTiles * kTilePages == kThreads, "one page id per thread per chu
 //       16 different bank groups.
 //   VT: page p, channel d at chunk p * D + d: the page's 16 tokens of that channel.
 //   KS, VS: the 64 keys' K and V scales (per-token-head mode).
-//   CF, FV, IF: per-key factors derived by wave 0 from KS/VS: score multiplier
-//       k_scale * q_scale * softmax_scale * log2(e), P' factor v_scale / (v_ref *
-//       prob_scale) and its reciprocal; VREF: v_ref after this tile.
+//   CF, FV, IF (one copy per wave): per-key factors derived from KS/VS: score
+//       multiplier k_scale * q_scale * softmax_scale * log2(e), P' factor v_scale /
+//       (v_ref * prob_scale) and its reciprocal; VREF: v_ref after this tile.
 template <int D>
 struct Layout {
   static constexpr int NC = D / 16;            // 16-byte chunks per key row
@@ -109,11 +109,15 @@ struct Layout {
   static constexpr int VT_CHUNKS = kTilePages * D;
   static constexpr int KS_OFF = VT_OFF + 16 * VT_CHUNKS;
   static constexpr int VS_OFF = KS_OFF + kTile * 4;
-  static constexpr int CF_OFF = VS_OFF + kTile * 4;
+  // one factor block per wave (each wave derives its own copy, so no barrier is
+  // needed between deriving and reading); offsets inside a block:
+  static constexpr int FAC_OFF = VS_OFF + kTile * 4;
+  static constexpr int CF_OFF = 0;
   static constexpr int FV_OFF = CF_OFF + kTile * 4;
   static constexpr int IF_OFF = FV_OFF + kTile * 4;
   static constexpr int VREF_OFF = IF_OFF + kTile * 4;
-  static constexpr int BYTES = VREF_OFF + 16;
+  static constexpr int FSZ = VREF_OFF + 16;
+  static constexpr int BYTES = FAC_OFF + kWaves * FSZ;
   // load instructions per page for K and for V (64 chunks each), and per wave per
   // tile for each
   static constexpr int PI = 16 * NC / kWave;
@@ -316,24 +320,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
     barrier_lds();
   };
   const float qk_base = a.q_scale * a.sm_log2 * (kPTH ? 1.0f : a.k_scale);
-  // Wave 0 derives the per-key factors of a resident tile; v_ref (the running V
-  // scale maximum) moves here, tile by tile, so every wave sees the same sequence.
+  // Every wave derives the per-key factors of a resident tile into its own block;
+  // v_ref (the running V scale maximum) moves here, tile by tile, identically in
+  // every wave.
   float vref_run = 0.0f;
+  const int fac = LY::FAC_OFF + wave * LY::FSZ;
   auto derive_tile = [&](uint8_t* st) {
     if constexpr (kPTH) {
-      if (wave == 0) {
-        const float ks = reinterpret_cast<const float*>(st + LY::KS_OFF)[lane];
-        const float vs = reinterpret_cast<const float*>(st + LY::VS_OFF)[lane];
-        vref_run = fmaxf(vref_run, wave_max(vs));
-        // P' factor and its reciprocal (hardware reciprocals: any f works as long as
-        // the row sum maps P' back with the same f, up to rounding)
-        const float f = vref_run > 0.0f ? vs * __builtin_amdgcn_rcpf(vref_run * a.prob_scale)
-                                        : 0.0f;
-        reinterpret_cast<float*>(st + LY::CF_OFF)[lane] = ks * qk_base;
-        reinterpret_cast<float*>(st + LY::FV_OFF)[lane] = f;
-        reinterpret_cast<float*>(st + LY::IF_OFF)[lane] = f > 0.0f ? __builtin_amdgcn_rcpf(f) : 0.0f;
-        if (lane == 0) reinterpret_cast<float*>(st + LY::VREF_OFF)[0] = vref_run;
-      }
+      const float ks = reinterpret_cast<const float*>(st + LY::KS_OFF)[lane];
+      const float vs = reinterpret_cast<const float*>(st + LY::VS_OFF)[lane];
+      vref_run = fmaxf(vref_run, wave_max(vs));
+      // P' factor and its reciprocal (hardware reciprocals: any f works as long as
+      // the row sum maps P' back with the same f, up to rounding)
+      const float f = vref_run > 0.0f ? vs * __builtin_amdgcn_rcpf(vref_run * a.prob_scale)
+                                      : 0.0f;
+      uint8_t* fb = st + fac;
+      reinterpret_cast<float*>(fb + LY::CF_OFF)[lane] = ks * qk_base;
+      reinterpret_cast<float*>(fb + LY::FV_OFF)[lane] = f;
+      reinterpret_cast<float*>(fb + LY::IF_OFF)[lane] = f > 0.0f ? __builtin_amdgcn_rcpf(f) : 0.0f;
+      if (lane == 0) reinterpret_cast<float*>(fb + LY::VREF_OFF)[0] = vref_run;
     }
   };
 
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
   // V^T operand: channel 32 db + row; bytes 0-15 = page grp, 16-31 = page 2 + grp
   const int v_lane = LY::VT_OFF + 16 * (grp * D + row);
   constexpr int V_HI = 16 * 2 * D;
-  const int s_lane = 4 * 16 * grp;
+  const int s_lane = fac + 4 * 16 * grp;  // this wave's factors, lane group grp
   const float pmul = 1.0f / a.prob_scale;
 
   // S^T = K . Q^T of a resident tile, for the two 32-key blocks
@@ -505,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
       // ---- rescale when v_ref grew or a score passed the reference by the slack ----
       float fo = 1.0f;  // factor for o
       if constexpr (kPTH) {
-        const float vr = lds_read<float>(buf, LY::VREF_OFF);
+        const float vr = lds_read<float>(buf, fac + LY::VREF_OFF);
         if (vr > vref) {
           fo = vref > 0.0f ? vref / vr : 0.0f;
           vref = vr;
@@ -534,11 +539,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
       }
 
       // ---- phase 1: S^T of tile t + 1 on the matrix cores; P' of tile t (e4m3, in the
-      // B-operand layout) on the vector unit.  Each chunk holds one MFMA (its operands
-      // read one chunk ahead) and a share of the vector work; scheduling barriers
-      // keep the chunks in order, so the two units overlap.
+      // B-operand layout) on the vector unit.  Each chunk holds one MFMA and a share
+      // of the vector work; every LDS operand a chunk uses (MFMA operand, per-key
+      // factors) is read ahead, and scheduling barriers keep the chunks in order, so
+      // the matrix cores, the vector unit and the LDS overlap.
       constexpr int NQK = 2 * KS;          // MFMAs of S^T per tile
-      constexpr int WQ = 8 / NQK;          // P' words per chunk
+      constexpr int WQ = 8 / NQK;          // P' words per phase-1 chunk
+      constexpr int WV = 8 / DB;           // row-sum words / score groups per phase-2 chunk
       auto k_operand = [&](int i) {        // chunk i: key block i % 2, dim step i / 2
         const int off = k_addr[i / 2] + K_KB * (i % 2);
         const uint4 x0 = lds_read<uint4>(nbuf, off);
@@ -546,21 +553,46 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
         return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
       };
+      auto v_operand = [&](int db) {
+        const int off = v_lane + 16 * 32 * db;
+        const uint4 x0 = lds_read<uint4>(buf, off);
+        const uint4 x1 = lds_read<uint4>(buf, off + V_HI);
+        return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      };
+      // per-key factors of word / score group w (keys 32 (w / 4) + 16 grp + 4 (w % 4) ..)
+      auto factor = [&](const uint8_t* b, int region, int w, float uniform) {
+        if constexpr (kPTH) return lds_read<float4>(b, region + s_lane + 16 * (8 * (w / 4) + w % 4));
+        else return make_float4(uniform, uniform, uniform, uniform);
+      };
       v16f sn[2] = {(v16f){}, (v16f){}};
-      v8i ka = k_operand(0);
+      v8i ka = k_operand(0), va;
+      float4 fvq[WQ], ifq[WV], cfq[WV];
+#pragma unroll
+      for (int u = 0; u < WQ; ++u) fvq[u] = factor(buf, LY::FV_OFF, u, pmul);
 #pragma unroll
       for (int i = 0; i < NQK; ++i) {
         const v8i cur = ka;
-        if (i + 1 < NQK) ka = k_operand(i + 1);
+        float4 fv[WQ];
+#pragma unroll
+        for (int u = 0; u < WQ; ++u) fv[u] = fvq[u];
+        if (i + 1 < NQK) {
+          ka = k_operand(i + 1);
+#pragma unroll
+          for (int u = 0; u < WQ; ++u) fvq[u] = factor(buf, LY::FV_OFF, WQ * (i + 1) + u, pmul);
+        } else {  // first phase-2 chunk's operands
+          va = v_operand(0);
+#pragma unroll
+          for (int u = 0; u < WV; ++u) {
+            ifq[u] = factor(buf, LY::IF_OFF, u, 1.0f);
+            cfq[u] = factor(nbuf, LY::CF_OFF, u, qk_base);
+          }
+        }
         sn[i % 2] = mfma(cur, qb[i / 2], sn[i % 2]);
 #pragma unroll
-        for (int w = WQ * i; w < WQ * (i + 1); ++w) {
-          const int kb = w / 4, q4 = w % 4;
-          float f[4] = {pmul, pmul, pmul, pmul};
-          if constexpr (kPTH) {
-            const float4 v4 = lds_read<float4>(buf, LY::FV_OFF + s_lane + 16 * (8 * kb + q4));
-            f[0] = v4.x; f[1] = v4.y; f[2] = v4.z; f[3] = v4.w;
-          }
+        for (int u = 0; u < WQ; ++u) {
+          const int w = WQ * i + u;
+          const float f[4] = {fv[u].x, fv[u].y, fv[u].z, fv[u].w};
           float pq[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -579,35 +611,37 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
                       (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
 
       // ---- phase 2: O^T += V^T . P'^T on the matrix cores; the row sum of the rounded
-      // P' and the scaled scores of tile t + 1 on the vector unit ------------------------
-      constexpr int WV = 8 / DB;           // row-sum words / score groups per chunk
-      auto v_operand = [&](int db) {
-        const int off = v_lane + 16 * 32 * db;
-        const uint4 x0 = lds_read<uint4>(buf, off);
-        const uint4 x1 = lds_read<uint4>(buf, off + V_HI);
-        return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      };
+      // P' and the scaled scores of tile t + 1 (past the last tile: unused) on the
+      // vector unit --------------------------------------------------------------------
       const float msafe = m == -INFINITY ? 0.0f : m;
-      v8i va = v_operand(0);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const v8i cur = va;
-        if (db + 1 < DB) va = v_operand(db + 1);
+        float4 fi[WV], fc[WV];
+#pragma unroll
+        for (int u = 0; u < WV; ++u) { fi[u] = ifq[u]; fc[u] = cfq[u]; }
+        if (db + 1 < DB) {
+          va = v_operand(db + 1);
+#pragma unroll
+          for (int u = 0; u < WV; ++u) {
+            ifq[u] = factor(buf, LY::IF_OFF, WV * (db + 1) + u, 1.0f);
+            cfq[u] = factor(nbuf, LY::CF_OFF, WV * (db + 1) + u, qk_base);
+          }
+        }
         o[db] = mfma(cur, pb, o[db]);
         // keep the accumulator in AGPRs across iterations: the (rare) rescale then
         // copies it out and back, instead of every iteration copying it to VGPRs
         asm volatile("" : "+a"(o[db]));
 #pragma unroll
-        for (int w = WV * db; w < WV * (db + 1); ++w) {
+        for (int u = 0; u < WV; ++u) {
+          const int w = WV * db + u;
           if constexpr (kPTH) {
-            const float4 i4 = lds_read<float4>(buf, LY::IF_OFF + s_lane + 16 * (8 * (w / 4) + w % 4));
             const float2_t d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], false);
             const float2_t d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], true);
-            lam = fmaf(d01.x, i4.x, lam);
-            lam = fmaf(d01.y, i4.y, lam);
-            lam = fmaf(d23.x, i4.z, lam);
-            lam = fmaf(d23.y, i4.w, lam);
+            lam = fmaf(d01.x, fi[u].x, lam);
+            lam = fmaf(d01.y, fi[u].y, lam);
+            lam = fmaf(d23.x, fi[u].z, lam);
+            lam = fmaf(d23.y, fi[u].w, lam);
           } else {
             const half2_t h01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw[w], 1.0f, false);
             const half2_t h23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw[w], 1.0f, true);
@@ -615,7 +649,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
             lam = __builtin_amdgcn_fdot2(h01, one, lam, false);
             lam = __builtin_amdgcn_fdot2(h23, one, lam, false);
           }
-          scale_group(w, nbuf, sn, msafe, x);  // past the last tile: unused
+          const float cc[4] = {fc[u].x, fc[u].y, fc[u].z, fc[u].w};
+          const int kb = w / 4, q4 = w % 4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * w + e] = fmaf(sn[kb][4 * q4 + e], cc[e], -msafe);
         }
         asm volatile("" : "+v"(lam));  // keeps the row sum in this chunk
         __builtin_amdgcn_sched_barrier(0);
@@ -623,16 +660,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
       mx = mask_max(t + 1, x);
 
       // ---- tile t + 2 resident (issued two iterations ago): wait, scrub its unwritten
-      // slots, derive its factors.  The barrier also closes this iteration's reads of
-      // the slot the next iteration's load overwrites.
+      // slots, derive its factors.  One barrier per tile: it publishes every wave's
+      // loads of tile t + 2 and closes this iteration's reads of tile t's slot, which
+      // the next iteration's loads overwrite (those reads were all consumed, hence
+      // complete, before it).
       if (t + 2 <= t_last) {
         uint8_t* nb = lds[(rel + 2) % kStages];
         wait_vmcnt<PER_TILE * (kStages - 3)>();
-        __builtin_amdgcn_s_barrier();
+        barrier_lds();
         scrub_tile(t + 2, nb);
         derive_tile(nb);
+      } else {
+        barrier_lds();
       }
-      barrier_lds();
     }
   };
   if (a.prob_scale < 256.0f / kE4m3Max) {
