@@ -504,6 +504,58 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
       const int rel = t - t_first;
       const uint8_t* buf = lds[rel % kStages];
       const uint8_t* nbuf = lds[(rel + 1) % kStages];  // past the last tile: unused
+      // ---- operand queue: chunk c < NQK is S^T MFMA c (K operand of tile t + 1, P'
+      // factors of tile t), chunk NQK + db is P.V MFMA db (V operand of tile t,
+      // row-sum factors of tile t, score factors of tile t + 1).  Operands are read two
+      // chunks ahead; the first two are read here, before the loads are issued and the
+      // rescale test runs, to cover their latency.
+      constexpr int NQK = 2 * KS;          // MFMAs of S^T per tile
+      constexpr int WQ = 8 / NQK;          // P' words per phase-1 chunk
+      constexpr int WV = 8 / DB;           // row-sum words / score groups per phase-2 chunk
+      constexpr int NCH = NQK + DB;
+      constexpr int MW = WQ > WV ? WQ : WV;
+      auto k_operand = [&](int i) {        // chunk i: key block i % 2, dim step i / 2
+        const int off = k_addr[i / 2] + K_KB * (i % 2);
+        const uint4 x0 = lds_read<uint4>(nbuf, off);
+        const uint4 x1 = lds_read<uint4>(nbuf, off + 16);
+        return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      };
+      auto v_operand = [&](int db) {
+        const int off = v_lane + 16 * 32 * db;
+        const uint4 x0 = lds_read<uint4>(buf, off);
+        const uint4 x1 = lds_read<uint4>(buf, off + V_HI);
+        return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      };
+      // per-key factors of word / score group w (keys 32 (w / 4) + 16 grp + 4 (w % 4) ..)
+      auto factor = [&](const uint8_t* b, int region, int w, float uniform) {
+        if constexpr (kPTH) return lds_read<float4>(b, region + s_lane + 16 * (8 * (w / 4) + w % 4));
+        else return make_float4(uniform, uniform, uniform, uniform);
+      };
+      struct Chunk {
+        v8i op;
+        float4 f[MW], f2[MW];
+      };
+      auto load_chunk = [&](int c, Chunk& q) {
+        if (c < NQK) {
+          q.op = k_operand(c);
+#pragma unroll
+          for (int u = 0; u < WQ; ++u) q.f[u] = factor(buf, LY::FV_OFF, WQ * c + u, pmul);
+        } else {
+          const int db = c - NQK;
+          q.op = v_operand(db);
+#pragma unroll
+          for (int u = 0; u < WV; ++u) {
+            q.f[u] = factor(buf, LY::IF_OFF, WV * db + u, 1.0f);
+            q.f2[u] = factor(nbuf, LY::CF_OFF, WV * db + u, qk_base);
+          }
+        }
+      };
+      Chunk cq[2];
+      load_chunk(0, cq[0]);
+      load_chunk(1, cq[1]);
+
       if (rel % kIdTiles == 0) issue_ids(rel / kIdTiles + 1);
       issue_tile(t + kStages - 1, (rel + kStages - 1) % kStages);
 
@@ -538,123 +590,71 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
         }
       }
 
-      // ---- phase 1: S^T of tile t + 1 on the matrix cores; P' of tile t (e4m3, in the
-      // B-operand layout) on the vector unit.  Each chunk holds one MFMA and a share
-      // of the vector work; every LDS operand a chunk uses (MFMA operand, per-key
-      // factors) is read ahead, and scheduling barriers keep the chunks in order, so
-      // the matrix cores, the vector unit and the LDS overlap.
-      constexpr int NQK = 2 * KS;          // MFMAs of S^T per tile
-      constexpr int WQ = 8 / NQK;          // P' words per phase-1 chunk
-      constexpr int WV = 8 / DB;           // row-sum words / score groups per phase-2 chunk
-      auto k_operand = [&](int i) {        // chunk i: key block i % 2, dim step i / 2
-        const int off = k_addr[i / 2] + K_KB * (i % 2);
-        const uint4 x0 = lds_read<uint4>(nbuf, off);
-        const uint4 x1 = lds_read<uint4>(nbuf, off + 16);
-        return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      };
-      auto v_operand = [&](int db) {
-        const int off = v_lane + 16 * 32 * db;
-        const uint4 x0 = lds_read<uint4>(buf, off);
-        const uint4 x1 = lds_read<uint4>(buf, off + V_HI);
-        return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      };
-      // per-key factors of word / score group w (keys 32 (w / 4) + 16 grp + 4 (w % 4) ..)
-      auto factor = [&](const uint8_t* b, int region, int w, float uniform) {
-        if constexpr (kPTH) return lds_read<float4>(b, region + s_lane + 16 * (8 * (w / 4) + w % 4));
-        else return make_float4(uniform, uniform, uniform, uniform);
-      };
+      // ---- phase 1 (chunks 0 .. NQK - 1): S^T of tile t + 1 on the matrix cores; P' of
+      // tile t (e4m3, in the B-operand layout) on the vector unit.  Phase 2 (chunks
+      // NQK ..): O^T += V^T . P'^T on the matrix cores; the row sum of the rounded P'
+      // and the scaled scores of tile t + 1 (past the last tile: unused) on the
+      // vector unit.  Each chunk holds one MFMA and a share of the vector work;
+      // scheduling barriers keep the chunks in order, so the matrix cores, the vector
+      // unit and the LDS overlap.
       v16f sn[2] = {(v16f){}, (v16f){}};
-      v8i ka = k_operand(0), va;
-      float4 fvq[WQ], ifq[WV], cfq[WV];
-#pragma unroll
-      for (int u = 0; u < WQ; ++u) fvq[u] = factor(buf, LY::FV_OFF, u, pmul);
-#pragma unroll
-      for (int i = 0; i < NQK; ++i) {
-        const v8i cur = ka;
-        float4 fv[WQ];
-#pragma unroll
-        for (int u = 0; u < WQ; ++u) fv[u] = fvq[u];
-        if (i + 1 < NQK) {
-          ka = k_operand(i + 1);
-#pragma unroll
-          for (int u = 0; u < WQ; ++u) fvq[u] = factor(buf, LY::FV_OFF, WQ * (i + 1) + u, pmul);
-        } else {  // first phase-2 chunk's operands
-          va = v_operand(0);
-#pragma unroll
-          for (int u = 0; u < WV; ++u) {
-            ifq[u] = factor(buf, LY::IF_OFF, u, 1.0f);
-            cfq[u] = factor(nbuf, LY::CF_OFF, u, qk_base);
-          }
-        }
-        sn[i % 2] = mfma(cur, qb[i / 2], sn[i % 2]);
-#pragma unroll
-        for (int u = 0; u < WQ; ++u) {
-          const int w = WQ * i + u;
-          const float f[4] = {fv[u].x, fv[u].y, fv[u].z, fv[u].w};
-          float pq[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p = __builtin_amdgcn_exp2f(x[4 * w + e]);
-            if constexpr (PM == 2) pq[e] = p;
-            else if constexpr (PM == 1) pq[e] = fminf(p * f[e], kE4m3Max);
-            else pq[e] = p * f[e];
-          }
-          // the two conversions fill bytes 0-1 and 2-3; the old contents are dead
-          const uint32_t lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(pq[0], pq[1], pw[w], false);
-          pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(pq[2], pq[3], lo2, true);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const v8i pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
-                      (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
-
-      // ---- phase 2: O^T += V^T . P'^T on the matrix cores; the row sum of the rounded
-      // P' and the scaled scores of tile t + 1 (past the last tile: unused) on the
-      // vector unit --------------------------------------------------------------------
+      v8i pb;
       const float msafe = m == -INFINITY ? 0.0f : m;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const v8i cur = va;
-        float4 fi[WV], fc[WV];
+      for (int c = 0; c < NCH; ++c) {
+        const Chunk cur = cq[c % 2];
+        if (c + 2 < NCH) load_chunk(c + 2, cq[c % 2]);
+        if (c < NQK) {
+          sn[c % 2] = mfma(cur.op, qb[c / 2], sn[c % 2]);
 #pragma unroll
-        for (int u = 0; u < WV; ++u) { fi[u] = ifq[u]; fc[u] = cfq[u]; }
-        if (db + 1 < DB) {
-          va = v_operand(db + 1);
+          for (int u = 0; u < WQ; ++u) {
+            const int w = WQ * c + u;
+            const float f[4] = {cur.f[u].x, cur.f[u].y, cur.f[u].z, cur.f[u].w};
+            float pq[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p = __builtin_amdgcn_exp2f(x[4 * w + e]);
+              if constexpr (PM == 2) pq[e] = p;
+              else if constexpr (PM == 1) pq[e] = fminf(p * f[e], kE4m3Max);
+              else pq[e] = p * f[e];
+            }
+            // the two conversions fill bytes 0-1 and 2-3; the old contents are dead
+            const uint32_t lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(pq[0], pq[1], pw[w], false);
+            pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(pq[2], pq[3], lo2, true);
+          }
+          if (c == NQK - 1)
+            pb = (v8i){(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
+                       (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+        } else {
+          const int db = c - NQK;
+          o[db] = mfma(cur.op, pb, o[db]);
+          // keep the accumulator in AGPRs across iterations: the (rare) rescale then
+          // copies it out and back, instead of every iteration copying it to VGPRs
+          asm volatile("" : "+a"(o[db]));
 #pragma unroll
           for (int u = 0; u < WV; ++u) {
-            ifq[u] = factor(buf, LY::IF_OFF, WV * (db + 1) + u, 1.0f);
-            cfq[u] = factor(nbuf, LY::CF_OFF, WV * (db + 1) + u, qk_base);
-          }
-        }
-        o[db] = mfma(cur, pb, o[db]);
-        // keep the accumulator in AGPRs across iterations: the (rare) rescale then
-        // copies it out and back, instead of every iteration copying it to VGPRs
-        asm volatile("" : "+a"(o[db]));
+            const int w = WV * db + u;
+            if constexpr (kPTH) {
+              const float2_t d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], false);
+              const float2_t d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], true);
+              lam = fmaf(d01.x, cur.f[u].x, lam);
+              lam = fmaf(d01.y, cur.f[u].y, lam);
+              lam = fmaf(d23.x, cur.f[u].z, lam);
+              lam = fmaf(d23.y, cur.f[u].w, lam);
+            } else {
+              const half2_t h01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw[w], 1.0f, false);
+              const half2_t h23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw[w], 1.0f, true);
+              const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+              lam = __builtin_amdgcn_fdot2(h01, one, lam, false);
+              lam = __builtin_amdgcn_fdot2(h23, one, lam, false);
+            }
+            const float cc[4] = {cur.f2[u].x, cur.f2[u].y, cur.f2[u].z, cur.f2[u].w};
+            const int kb = w / 4, q4 = w % 4;
 #pragma unroll
-        for (int u = 0; u < WV; ++u) {
-          const int w = WV * db + u;
-          if constexpr (kPTH) {
-            const float2_t d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], false);
-            const float2_t d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], true);
-            lam = fmaf(d01.x, fi[u].x, lam);
-            lam = fmaf(d01.y, fi[u].y, lam);
-            lam = fmaf(d23.x, fi[u].z, lam);
-            lam = fmaf(d23.y, fi[u].w, lam);
-          } else {
-            const half2_t h01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw[w], 1.0f, false);
-            const half2_t h23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw[w], 1.0f, true);
-            const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-            lam = __builtin_amdgcn_fdot2(h01, one, lam, false);
-            lam = __builtin_amdgcn_fdot2(h23, one, lam, false);
+            for (int e = 0; e < 4; ++e) x[4 * w + e] = fmaf(sn[kb][4 * q4 + e], cc[e], -msafe);
           }
-          const float cc[4] = {fc[u].x, fc[u].y, fc[u].z, fc[u].w};
-          const int kb = w / 4, q4 = w % 4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * w + e] = fmaf(sn[kb][4 * q4 + e], cc[e], -msafe);
+          asm volatile("" : "+v"(lam));  // keeps the row sum in this chunk
         }
-        asm volatile("" : "+v"(lam));  // keeps the row sum in this chunk
         __builtin_amdgcn_sched_barrier(0);
       }
       mx = mask_max(t + 1, x);
