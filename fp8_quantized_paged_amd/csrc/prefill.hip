@@ -260,27 +260,31 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
     k_voff = (uint32_t)((t - 64 * jj / LY::NC) * D + 16 * c);
   }
   const uint32_t v_voff = 16u * lane;
-  auto issue_tile = [&](int t, int slot) {
-    const int tt = min(t, t_last);  // past the last tile: harmless re-load of it
-    const int rel = tt - t_first;
-    // the tile's four page ids in one read, made uniform; (page, head) byte offsets
-    // (K and V pages of one head have the same size, 16 D bytes)
-    const int4 id4 = *reinterpret_cast<const int4*>(
+  // the four page ids of tile t (past the last tile: those of the last tile, whose
+  // re-load is harmless), in one LDS read
+  auto tile_ids = [&](int t) {
+    const int rel = min(t, t_last) - t_first;
+    return *reinterpret_cast<const int4*>(
         &ids_lds[(rel / kIdTiles) & 1][(rel % kIdTiles) * kTilePages]);
-    const int ids[4] = {__builtin_amdgcn_readfirstlane(id4.x), __builtin_amdgcn_readfirstlane(id4.y),
-                        __builtin_amdgcn_readfirstlane(id4.z), __builtin_amdgcn_readfirstlane(id4.w)};
-#pragma unroll
-    for (int j = 0; j < LY::W; ++j) {
+  };
+  // Load instruction k (0 .. PER_TILE - 1) of this wave for a tile with page ids id4:
+  // K and V block j = k / 2 (page ids made uniform; K and V pages of one head have the
+  // same size, 16 D bytes, hence the same (page, head) byte offset), then the scales.
+  auto issue_load = [&](int k, int slot, const int4 id4) {
+    if (k < 2 * LY::W) {
+      const int j = k / 2;
       const int pg = (kWaves / LY::PI) * j + wave / LY::PI;  // (wave + 4 j) / PI
-      const int id = pg == 0 ? ids[0] : pg == 1 ? ids[1] : pg == 2 ? ids[2] : ids[3];
+      const int id = __builtin_amdgcn_readfirstlane(
+          pg == 0 ? id4.x : pg == 1 ? id4.y : pg == 2 ? id4.z : id4.w);
       const uint64_t off = (uint64_t)(uint32_t)(id * hkv + g) * (uint64_t)(16 * D) +
                            (uint64_t)(1024 * jj);
-      lds_load16s(a.k_pages + off, k_voff,
-                  lds_offset(&lds[slot][LY::K_OFF + 16 * (pg * LY::KPC + 64 * jj)]));
-      lds_load16s(a.v_pages + off, v_voff,
-                  lds_offset(&lds[slot][LY::VT_OFF + 16 * (pg * D + 64 * jj)]));
-    }
-    if constexpr (kPTH) {  // waves 0/2: K scales, 1/3: V scales (2 and 3 repeat)
+      if (k % 2 == 0)
+        lds_load16s(a.k_pages + off, k_voff,
+                    lds_offset(&lds[slot][LY::K_OFF + 16 * (pg * LY::KPC + 64 * jj)]));
+      else
+        lds_load16s(a.v_pages + off, v_voff,
+                    lds_offset(&lds[slot][LY::VT_OFF + 16 * (pg * D + 64 * jj)]));
+    } else if constexpr (kPTH) {  // waves 0/2: K scales, 1/3: V scales (2, 3 repeat)
       const int page = lane / kPage;
       const int id = page == 0 ? id4.x : page == 1 ? id4.y : page == 2 ? id4.z : id4.w;
       const int64_t idx = ((int64_t)id * hkv + g) * kPage + lane % kPage;
@@ -288,6 +292,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
       lds_load4((kside ? a.k_scales : a.v_scales) + idx,
                 lds_offset(&lds[slot][kside ? LY::KS_OFF : LY::VS_OFF]));
     }
+  };
+  auto issue_tile = [&](int t, int slot) {
+    const int4 id4 = tile_ids(t);
+#pragma unroll
+    for (int k = 0; k < PER_TILE; ++k) issue_load(k, slot, id4);
   };
   // Wait for this wave's loads of the next tile (the loads of the tiles issued after
   // it may stay in flight), then make every wave's loads visible.
@@ -513,6 +522,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
       constexpr int WQ = 8 / NQK;          // P' words per phase-1 chunk
       constexpr int WV = 8 / DB;           // row-sum words / score groups per phase-2 chunk
       constexpr int NCH = NQK + DB;
+      static_assert(PER_TILE + 1 <= NCH, "one load per chunk");
       constexpr int MW = WQ > WV ? WQ : WV;
       auto k_operand = [&](int i) {        // chunk i: key block i % 2, dim step i / 2
         const int off = k_addr[i / 2] + K_KB * (i % 2);
@@ -557,7 +567,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
       load_chunk(1, cq[1]);
 
       if (rel % kIdTiles == 0) issue_ids(rel / kIdTiles + 1);
-      issue_tile(t + kStages - 1, (rel + kStages - 1) % kStages);
+      // loads of tile t + 3 (into tile t - 1's slot): issued one per chunk from chunk 1
+      // on, so that they overlap the matrix and vector work
+      const int4 ld_ids = tile_ids(t + kStages - 1);
+      const int ld_slot = (rel + kStages - 1) % kStages;
 
       // ---- rescale when v_ref grew or a score passed the reference by the slack ----
       float fo = 1.0f;  // factor for o
@@ -604,6 +617,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
       for (int c = 0; c < NCH; ++c) {
         const Chunk cur = cq[c % 2];
         if (c + 2 < NCH) load_chunk(c + 2, cq[c % 2]);
+        if (c >= 1 && c - 1 < PER_TILE) issue_load(c - 1, ld_slot, ld_ids);
         if (c < NQK) {
           sn[c % 2] = mfma(cur.op, qb[c / 2], sn[c % 2]);
 #pragma unroll
