@@ -334,10 +334,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
   // every wave.
   float vref_run = 0.0f;
   const int fac = LY::FAC_OFF + wave * LY::FSZ;
-  auto derive_tile = [&](uint8_t* st) {
+  auto derive_finish = [&](uint8_t* st, float ks, float vs) {
     if constexpr (kPTH) {
-      const float ks = reinterpret_cast<const float*>(st + LY::KS_OFF)[lane];
-      const float vs = reinterpret_cast<const float*>(st + LY::VS_OFF)[lane];
       vref_run = fmaxf(vref_run, wave_max(vs));
       // P' factor and its reciprocal (hardware reciprocals: any f works as long as
       // the row sum maps P' back with the same f, up to rounding)
@@ -349,6 +347,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
       reinterpret_cast<float*>(fb + LY::IF_OFF)[lane] = f > 0.0f ? __builtin_amdgcn_rcpf(f) : 0.0f;
       if (lane == 0) reinterpret_cast<float*>(fb + LY::VREF_OFF)[0] = vref_run;
     }
+  };
+  auto derive_tile = [&](uint8_t* st) {
+    if constexpr (kPTH)
+      derive_finish(st, reinterpret_cast<const float*>(st + LY::KS_OFF)[lane],
+                    reinterpret_cast<const float*>(st + LY::VS_OFF)[lane]);
   };
 
   // ---- query codes: B operand of S^T = K . Q^T -----------------------------------
@@ -473,7 +476,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
   };
 
   // prologue: page ids of the first chunk; tiles t_first .. t_first + kStages - 2 in
-  // flight; the first two made resident
+  // flight; the first two made resident, the factors of the first derived (iteration
+  // t derives those of tile t + 1)
   issue_ids(0);
   wait_vmcnt<0>();
   barrier_lds();
@@ -488,7 +492,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
     wait_vmcnt<PER_TILE * (kStages - 3)>();
     __builtin_amdgcn_s_barrier();
     scrub_tile(t_first + 1, lds[1]);
-    derive_tile(lds[1]);
     barrier_lds();
   }
 
@@ -562,6 +565,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
           }
         }
       };
+      // factors of tile t + 1 (its scales were made resident by the previous
+      // iteration): scales read here, factors written in chunk 1 (before the first
+      // score-factor read) or, with fewer than 4 S^T chunks, right away
+      uint8_t* const dbuf = lds[(rel + 1) % kStages];  // past the last tile: unused
+      float dks = 0.0f, dvs = 0.0f;
+      if constexpr (kPTH) {
+        dks = reinterpret_cast<const float*>(dbuf + LY::KS_OFF)[lane];
+        dvs = reinterpret_cast<const float*>(dbuf + LY::VS_OFF)[lane];
+        if constexpr (NQK < 4) derive_finish(dbuf, dks, dvs);
+      }
       Chunk cq[2];
       load_chunk(0, cq[0]);
       load_chunk(1, cq[1]);
@@ -618,6 +631,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
         const Chunk cur = cq[c % 2];
         if (c + 2 < NCH) load_chunk(c + 2, cq[c % 2]);
         if (c >= 1 && c - 1 < PER_TILE) issue_load(c - 1, ld_slot, ld_ids);
+        if constexpr (kPTH && NQK >= 4)
+          if (c == 1) derive_finish(dbuf, dks, dvs);
         if (c < NQK) {
           sn[c % 2] = mfma(cur.op, qb[c / 2], sn[c % 2]);
 #pragma unroll
@@ -674,7 +689,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
       mx = mask_max(t + 1, x);
 
       // ---- tile t + 2 resident (issued two iterations ago): wait, scrub its unwritten
-      // slots, derive its factors.  One barrier per tile: it publishes every wave's
+      // slots.  One barrier per tile: it publishes every wave's
       // loads of tile t + 2 and closes this iteration's reads of tile t's slot, which
       // the next iteration's loads overwrite (those reads were all consumed, hence
       // complete, before it).
@@ -683,7 +698,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
         wait_vmcnt<PER_TILE * (kStages - 3)>();
         barrier_lds();
         scrub_tile(t + 2, nb);
-        derive_tile(nb);
       } else {
         barrier_lds();
       }
