@@ -61,7 +61,7 @@ constexpr int kDecodeRing = 3;
 // Cache pages are read once per call: load them non-temporally (they bypass the
 // caches' normal retention instead of evicting the block table, scales and query).
 constexpr bool kStreamLoads = true;
-constexpr bool kSplitMajor = false;
+constexpr bool kSplitMajor = true;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -108,12 +108,23 @@ struct DecodeArgs {
   int32_t out_f32;
 };
 
+// 8-byte agent-scope (device-coherent) stores and loads of float pairs: the split
+// partials pass between workgroups on different XCDs, whose L2s are not coherent;
+// per-access coherence avoids whole-cache write-back / invalidate fences.
 __device__ __forceinline__ void store_agent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_agent2(float* p, float x, float y) {
+  const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, x) |
+                     ((uint64_t)__builtin_bit_cast(uint32_t, y) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_agent2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__builtin_bit_cast(float, (uint32_t)v),
+                     __builtin_bit_cast(float, (uint32_t)(v >> 32)));
 }
 
 __device__ __forceinline__ void store_out(void* out, int32_t out_f32, int64_t i, float v) {
@@ -157,11 +168,20 @@ __device__ __forceinline__ void allreduce_low_bits(float (&v)[NVL]) {
   }
 }
 
+// Waves per SIMD the register allocation aims for: three where that costs no spills
+// (head_dim 64 with per-tensor scales), otherwise the compiler's choice.
+template <int D, int G, bool kFp8, bool kPTH>
+constexpr int decode_waves_per_eu() { return kFp8 && !kPTH && D == 64 && G <= 8 ? 3 : 1; }
+
 template <int D, int G, bool kFp8, bool kPTH, int kRing>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    decode_waves_per_eu<D, G, kFp8, kPTH>()))) void decode_kernel(const DecodeArgs a) {
   using S = DecodeShape<D, G, kFp8>;
   constexpr int QW = G * D / 2;                  // query as bf16 pairs
-  constexpr int MERGE = (kWaves / 2) * G * D;    // wave-merge slots (floats)
+  constexpr int NE4 = G * D / 4;                 // float4 groups of a (b, g) output
+  // wave-merge slots (floats): the waves' partial outputs, later the split merge's
+  // (M, L, O) per float4 group of two waves
+  constexpr int MERGE = (kWaves / 2) * G * D > 12 * NE4 ? (kWaves / 2) * G * D : 12 * NE4;
   __shared__ uint32_t q_lds_all[kWaves][QW];
   __shared__ uint32_t w_lds_all[kWaves][S::W_WORDS];
   __shared__ float ml_lds[kWaves][G][2];
@@ -608,10 +628,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
   }
 
   // ---- split partial -> workspace; the last split of (b, g) merges them all ---------
-  // Partials are stored as agent-scope atomics, i.e. written through to the device
-  // coherence point (the L2 of each XCD is not coherent with the others); the wave
-  // then waits until they are performed before it counts itself done, and the last
-  // workgroup reads them back with agent-scope loads.
+  // Partials are stored with agent-scope atomics, i.e. written through to the device
+  // coherence point; the wave waits until they are performed before it counts itself
+  // done, and the last workgroup reads them back with agent-scope loads.
   const int64_t prow = (int64_t)ug * a.splits;  // partial rows of (b, g)
   if (wave == 0) {
 #pragma unroll
@@ -619,10 +638,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
       float* o = a.o_part + ((prow + s) * G + hh) * D;
 #pragma unroll
       for (int dd = 0; dd < S::DPL; ++dd) store_agent(o + lane + kWave * dd, acc[hh][dd]);
-      if (lane == 0) {
-        store_agent(a.ml_part + ((prow + s) * G + hh) * 2, M[hh]);
-        store_agent(a.ml_part + ((prow + s) * G + hh) * 2 + 1, Lsum[hh]);
-      }
+      if (lane == 0) store_agent2(a.ml_part + ((prow + s) * G + hh) * 2, M[hh], Lsum[hh]);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     int done = 0;
@@ -635,53 +651,99 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
   __syncthreads();
   if (!last_lds) return;
 
-  // Level-3 merge over the ns splits, in split order, by all threads of the
-  // workgroup: thread t handles output elements t, t + 256, ...; every batch of
-  // splits is fetched with all its loads in flight at once.
-  constexpr int kEPT = (G * D + kThreads - 1) / kThreads;
-  constexpr int kBatch = 32 / kEPT > 2 ? 32 / kEPT : 2;
-  float Mx[kEPT], lsum[kEPT], osum[kEPT];
+  // Level-3 merge over the ns splits, by the last workgroup: wave w takes splits w,
+  // w + 4, ... (in order), lane l the float4 groups l, l + 64, ... of the G x D
+  // outputs; batches of MB splits have all their loads in flight at once.  The four
+  // waves' (M, L, O) then combine in a fixed tree through LDS.
+  constexpr int E4L = (NE4 + kWave - 1) / kWave;
+  constexpr int MB = 4 / E4L > 1 ? 4 / E4L : 1;
+  float Mx[E4L], Ls[E4L];
+  float4 Os[E4L];
 #pragma unroll
-  for (int x = 0; x < kEPT; ++x) {
-    Mx[x] = -INFINITY;
-    lsum[x] = 0.0f;
-    osum[x] = 0.0f;
+  for (int k = 0; k < E4L; ++k) {
+    Mx[k] = -INFINITY;
+    Ls[k] = 0.0f;
+    Os[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   }
-  for (int j0 = 0; j0 < ns; j0 += kBatch) {
-    float mv[kEPT][kBatch], lv[kEPT][kBatch], ov[kEPT][kBatch];
+  auto combine = [](float& m0, float& l0, float4& o0, float m1, float l1, float4 o1) {
+    if (m1 == -INFINITY) return;
+    const float mn = fmaxf(m0, m1);
+    const float fa = m0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m0 - mn);
+    const float fb = __builtin_amdgcn_exp2f(m1 - mn);
+    o0.x = o0.x * fa + o1.x * fb;
+    o0.y = o0.y * fa + o1.y * fb;
+    o0.z = o0.z * fa + o1.z * fb;
+    o0.w = o0.w * fa + o1.w * fb;
+    l0 = l0 * fa + l1 * fb;
+    m0 = mn;
+  };
+  for (int j0 = wave; j0 < ns; j0 += kWaves * MB) {
+    float4 ov[MB][E4L];
+    float2 mlv[MB][E4L];
 #pragma unroll
-    for (int x = 0; x < kEPT; ++x) {
-      const int e = min(tid + x * kThreads, G * D - 1);
-      const int hh = e / D;
+    for (int u = 0; u < MB; ++u) {
+      const int j = min(j0 + kWaves * u, ns - 1);
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int j = min(j0 + u, ns - 1);
-        mv[x][u] = load_agent(a.ml_part + ((prow + j) * G + hh) * 2);
-        lv[x][u] = load_agent(a.ml_part + ((prow + j) * G + hh) * 2 + 1);
-        ov[x][u] = load_agent(a.o_part + (prow + j) * G * D + e);
+      for (int k = 0; k < E4L; ++k) {
+        const int e4 = min(lane + kWave * k, NE4 - 1);
+        const float* op = a.o_part + (prow + j) * G * D + 4 * e4;
+        const float2 lo2 = load_agent2(op), hi2 = load_agent2(op + 2);
+        ov[u][k] = make_float4(lo2.x, lo2.y, hi2.x, hi2.y);
+        mlv[u][k] = load_agent2(a.ml_part + ((prow + j) * G + (4 * e4) / D) * 2);
       }
     }
 #pragma unroll
-    for (int x = 0; x < kEPT; ++x)
+    for (int u = 0; u < MB; ++u)
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (j0 + u >= ns || mv[x][u] == -INFINITY) continue;
-        const float mn = fmaxf(Mx[x], mv[x][u]);
-        const float fa = exp2_or_zero(Mx[x] == -INFINITY ? -INFINITY : Mx[x] - mn);
-        const float fb = __builtin_amdgcn_exp2f(mv[x][u] - mn);
-        osum[x] = osum[x] * fa + ov[x][u] * fb;
-        lsum[x] = lsum[x] * fa + lv[x][u] * fb;
-        Mx[x] = mn;
+      for (int k = 0; k < E4L; ++k)
+        if (j0 + kWaves * u < ns) combine(Mx[k], Ls[k], Os[k], mlv[u][k].x, mlv[u][k].y, ov[u][k]);
+  }
+  // tree over the waves: waves [h, 2h) hand their (M, L, O) to waves [0, h)
+  float* mslot = merge_lds;                        // [2][NE4] M, L pairs
+  float4* oslot = reinterpret_cast<float4*>(merge_lds + 4 * NE4);  // [2][NE4]
+#pragma unroll
+  for (int half = kWaves / 2; half >= 1; half /= 2) {
+    if (wave >= half && wave < 2 * half) {
+#pragma unroll
+      for (int k = 0; k < E4L; ++k) {
+        const int e4 = lane + kWave * k;
+        if (e4 < NE4) {
+          const int i = (wave - half) * NE4 + e4;
+          mslot[2 * i] = Mx[k];
+          mslot[2 * i + 1] = Ls[k];
+          oslot[i] = Os[k];
+        }
       }
-  }
+    }
+    __syncthreads();
+    if (wave < half) {
 #pragma unroll
-  for (int x = 0; x < kEPT; ++x) {
-    const int e = tid + x * kThreads;
-    if (e < G * D)
-      store_out(a.out, a.out_f32, row0 * D + e, lsum[x] > 0.0f ? osum[x] / lsum[x] : 0.0f);
+      for (int k = 0; k < E4L; ++k) {
+        const int e4 = lane + kWave * k;
+        if (e4 < NE4) {
+          const int i = wave * NE4 + e4;
+          combine(Mx[k], Ls[k], Os[k], mslot[2 * i], mslot[2 * i + 1], oslot[i]);
+        }
+      }
+    }
+    __syncthreads();
   }
-  if (tid == 0)
-    __hip_atomic_store(&a.counters[ug], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wave == 0) {
+#pragma unroll
+    for (int k = 0; k < E4L; ++k) {
+      const int e4 = lane + kWave * k;
+      if (e4 < NE4) {
+        const float inv = Ls[k] > 0.0f ? 1.0f / Ls[k] : 0.0f;
+        const int64_t e = row0 * D + 4 * e4;
+        store_out(a.out, a.out_f32, e, Os[k].x * inv);
+        store_out(a.out, a.out_f32, e + 1, Os[k].y * inv);
+        store_out(a.out, a.out_f32, e + 2, Os[k].z * inv);
+        store_out(a.out, a.out_f32, e + 3, Os[k].w * inv);
+      }
+    }
+    if (lane == 0)
+      __hip_atomic_store(&a.counters[ug], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ---- host side ----------------------------------------------------------------------

@@ -131,4 +131,43 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
+// Direct global -> LDS loads (each lane's 16 or 4 bytes land at lds_off + lane * size).
+// Written as inline assembly on purpose: the compiler treats its own form of these
+// loads as pending LDS writes and waits for all of them before any LDS read, which
+// would drain the tile pipeline; here the waits are explicit (wait_vmcnt), and
+// unknown vector memory operations can only make the compiler's own waits stricter.
+__device__ __forceinline__ void lds_load16(const void* src, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_off) : "memory", "m0");
+}
+// The same with a uniform 64-bit base in scalar registers and a 32-bit per-lane offset.
+__device__ __forceinline__ void lds_load16s(const void* base, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds_off) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(const void* src, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_off) : "memory", "m0");
+}
+template <typename T>
+__device__ __forceinline__ uint32_t lds_offset(T* p) {  // p points into __shared__ memory
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8).  wait_vmcnt<N>: at most N vector memory operations outstanding, the other
+// counters untouched.  barrier_lds: this wave's LDS operations done, then the
+// workgroup barrier (unlike __syncthreads it does not wait for the direct-to-LDS
+// loads still in flight).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
 }  // namespace kvq

@@ -145,45 +145,6 @@ struct PrefillArgs {
   int32_t out_f32;
 };
 
-// Direct global -> LDS loads (each lane's 16 or 4 bytes land at lds_off + lane * size).
-// Written as inline assembly on purpose: the compiler treats its own form of these
-// loads as pending LDS writes and waits for all of them before any LDS read, which
-// would drain the tile pipeline; here the waits are explicit (wait_vmcnt), and
-// unknown vector memory operations can only make the compiler's own waits stricter.
-__device__ __forceinline__ void lds_load16(const void* src, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_off) : "memory", "m0");
-}
-// The same with a uniform 64-bit base in scalar registers and a 32-bit per-lane offset.
-__device__ __forceinline__ void lds_load16s(const void* base, uint32_t voff, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(base), "s"(lds_off) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_load4(const void* src, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(src), "s"(lds_off) : "memory", "m0");
-}
-template <typename T>
-__device__ __forceinline__ uint32_t lds_offset(T* p) {  // p points into __shared__ memory
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
-// 11:8).  wait_vmcnt<N>: at most N vector memory operations outstanding, the other
-// counters untouched.  barrier_lds: this wave's LDS operations done, then the
-// workgroup barrier (unlike __syncthreads it does not wait for the direct-to-LDS
-// loads still in flight).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-__device__ __forceinline__ void barrier_lds() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-}
-
 template <typename T>
 __device__ __forceinline__ T lds_read(const uint8_t* base, int byte_off) {
   return *reinterpret_cast<const T*>(base + byte_off);
@@ -518,15 +479,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
       const uint8_t* nbuf = lds[(rel + 1) % kStages];  // past the last tile: unused
       // ---- operand queue: chunk c < NQK is S^T MFMA c (K operand of tile t + 1, P'
       // factors of tile t), chunk NQK + db is P.V MFMA db (V operand of tile t,
-      // row-sum factors of tile t, score factors of tile t + 1).  Operands are read two
-      // chunks ahead; the first two are read here, before the loads are issued and the
-      // rescale test runs, to cover their latency.
+      // row-sum factors of tile t, score factors of tile t + 1).  Operands are read QD
+      // chunks ahead; the first QD are read here, before the rescale test runs, to
+      // cover their latency.
       constexpr int NQK = 2 * KS;          // MFMAs of S^T per tile
       constexpr int WQ = 8 / NQK;          // P' words per phase-1 chunk
       constexpr int WV = 8 / DB;           // row-sum words / score groups per phase-2 chunk
       constexpr int NCH = NQK + DB;
       static_assert(PER_TILE + 1 <= NCH, "one load per chunk");
       constexpr int MW = WQ > WV ? WQ : WV;
+      // queue depth (chunks read ahead)
+      constexpr int QD = 2;
       auto k_operand = [&](int i) {        // chunk i: key block i % 2, dim step i / 2
         const int off = k_addr[i / 2] + K_KB * (i % 2);
         const uint4 x0 = lds_read<uint4>(nbuf, off);
@@ -575,9 +538,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
         dvs = reinterpret_cast<const float*>(dbuf + LY::VS_OFF)[lane];
         if constexpr (NQK < 4) derive_finish(dbuf, dks, dvs);
       }
-      Chunk cq[2];
-      load_chunk(0, cq[0]);
-      load_chunk(1, cq[1]);
+      Chunk cq[QD];
+#pragma unroll
+      for (int c = 0; c < QD; ++c) load_chunk(c, cq[c]);
 
       if (rel % kIdTiles == 0) issue_ids(rel / kIdTiles + 1);
       // loads of tile t + 3 (into tile t - 1's slot): issued one per chunk from chunk 1
@@ -628,8 +591,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
       const float msafe = m == -INFINITY ? 0.0f : m;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const Chunk cur = cq[c % 2];
-        if (c + 2 < NCH) load_chunk(c + 2, cq[c % 2]);
+        const Chunk cur = cq[c % QD];
+        if (c + QD < NCH) load_chunk(c + QD, cq[c % QD]);
         if (c >= 1 && c - 1 < PER_TILE) issue_load(c - 1, ld_slot, ld_ids);
         if constexpr (kPTH && NQK >= 4)
           if (c == 1) derive_finish(dbuf, dks, dvs);
