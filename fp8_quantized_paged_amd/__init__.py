@@ -7,7 +7,8 @@ the library is not built: there is no CPU or PyTorch fallback.
 from .binding import (  # noqa: F401
     BF16, F32, FP8_E4M3, PAGE_SIZE, PER_TENSOR, PER_TOKEN_HEAD, SKIP_SLIDING_WINDOW,
     WARN_UNCALIBRATED_Q_OR_PROB, CacheDesc, KvqError, PagedCache, Scales, abi_version,
-    cache_write, decode_attention, decode_workspace, decode_workspace_bytes, exported, header_functions,
+    cache_write, decode_attention, decode_step, decode_workspace, decode_workspace_bytes,
+    exported, header_functions,
     last_error, layer_kv_dtype, prefill_attention, quantize_fp8, resolve_scales,
     status_string,
 )

@@ -96,6 +96,9 @@ _SIGS = {
     "kvq_decode_attention": (ctypes.c_int, [_PD, _p, _i32, _i32, _p, _i32, _p, _i32,
                                             ctypes.POINTER(Scales), _i32, _f32, _i32,
                                             _p, ctypes.c_int, _p, _sz, _p]),
+    "kvq_decode_step": (ctypes.c_int, [_PD, _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32,
+                                       ctypes.POINTER(Scales), _i32, _f32, _i32,
+                                       _p, ctypes.c_int, _p, _sz, _p]),
     "kvq_prefill_attention": (ctypes.c_int, [_PD, _p, _p, _i32, _i32, _p, _i32, _p,
                                              _i32, ctypes.POINTER(Scales), _i32, _i32,
                                              _f32, _p, ctypes.c_int, _p]),
@@ -266,6 +269,31 @@ def decode_attention(cache: PagedCache, q, block_table, seq_lens, max_seq_len: i
         _ptr(seq_lens), max_seq_len, ctypes.byref(scales), window, softmax_scale,
         pages_per_split, _ptr(out), _DTYPES[out_dtype], _ptr(workspace),
         workspace.numel(), _stream(stream)), "decode_attention")
+    return out
+
+
+def decode_step(cache: PagedCache, q, k_new, v_new, block_table, seq_lens, max_seq_len: int,
+                scales: Scales | None = None, window: int = 0, softmax_scale: float = 0.0,
+                pages_per_split: int = 0, out=None, out_dtype: str = "bf16", workspace=None,
+                stream=None):
+    """Cache write of each sequence's new token (k_new, v_new bf16 [B][Hkv][D], stored at
+    position seq_lens[b] - 1) and decode attention, in one launch."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    if scales is None:
+        scales = Scales(1.0, 1.0, 1.0, 1.0)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16 if out_dtype == "bf16"
+                          else torch.float32, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(cache, B, Hq, max_seq_len, window, pages_per_split,
+                                     q.device)
+    d = cache.desc()
+    _check(_lib.kvq_decode_step(
+        ctypes.byref(d), _ptr(q), _ptr(k_new), _ptr(v_new), B, Hq, _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), max_seq_len, ctypes.byref(scales), window,
+        softmax_scale, pages_per_split, _ptr(out), _DTYPES[out_dtype], _ptr(workspace),
+        workspace.numel(), _stream(stream)), "decode_step")
     return out
 
 

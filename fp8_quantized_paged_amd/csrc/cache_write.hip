@@ -36,64 +36,9 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   const int off = (int)(slot & 15);
   const int64_t tile = page * num_heads + h;  // (page, head) tile index
 
-  const int64_t src = (int64_t)t * token_stride + (int64_t)h * D + c * 8;
-  const uint4 kw = *reinterpret_cast<const uint4*>(k + src);
-  const uint4 vw = *reinterpret_cast<const uint4*>(v + src);
-  const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
-  const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
-  float kf[8], vf[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    kf[2 * i] = bf16_bits_to_float(kk[i] & 0xFFFFu);
-    kf[2 * i + 1] = bf16_bits_to_float(kk[i] >> 16);
-    vf[2 * i] = bf16_bits_to_float(vv[i] & 0xFFFFu);
-    vf[2 * i + 1] = bf16_bits_to_float(vv[i] >> 16);
-  }
-
-  if constexpr (!kFp8) {
-    // bf16 cache (sliding-window layers kept unquantised): plain copy.
-    uint16_t* kp = reinterpret_cast<uint16_t*>(k_pages);
-    uint16_t* vp = reinterpret_cast<uint16_t*>(v_pages);
-    *reinterpret_cast<uint4*>(kp + (tile * kPage + off) * D + c * 8) = kw;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vp[(tile * D + c * 8 + 2 * i) * kPage + off] = (uint16_t)(vv[i] & 0xFFFFu);
-      vp[(tile * D + c * 8 + 2 * i + 1) * kPage + off] = (uint16_t)(vv[i] >> 16);
-    }
-    return;
-  } else {
-    float ks = k_scale, vs = v_scale;
-    if constexpr (kPerTokenHead) {
-      uint32_t ka = 0, va = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ka = max(ka, abs_bits(kf[i]));
-        va = max(va, abs_bits(vf[i]));
-      }
-#pragma unroll
-      for (int o = kLanesPerRow / 2; o >= 1; o >>= 1) {
-        ka = max(ka, (uint32_t)__shfl_xor((int)ka, o));
-        va = max(va, (uint32_t)__shfl_xor((int)va, o));
-      }
-      ks = scale_from_amax_bits(ka);
-      vs = scale_from_amax_bits(va);
-      if (c == 0) {
-        k_scales[tile * kPage + off] = ks;
-        v_scales[tile * kPage + off] = vs;
-      }
-    }
-    uint32_t klo = 0, khi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      klo |= e4m3_quantize(kf[i], ks) << (8 * i);
-      khi |= e4m3_quantize(kf[4 + i], ks) << (8 * i);
-    }
-    *reinterpret_cast<uint2*>(k_pages + (tile * kPage + off) * D + c * 8) =
-        make_uint2(klo, khi);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      v_pages[(tile * D + c * 8 + i) * kPage + off] = (uint8_t)e4m3_quantize(vf[i], vs);
-  }
+  const int64_t src = (int64_t)t * token_stride + (int64_t)h * D;
+  store_token_row<D, kFp8, kPerTokenHead>(k + src, v + src, c, tile, off, k_pages, v_pages,
+                                          k_scales, v_scales, k_scale, v_scale);
 }
 
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x,

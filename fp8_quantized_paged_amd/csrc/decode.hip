@@ -106,6 +106,10 @@ struct DecodeArgs {
   int32_t* counters;  // [B*Hkv] finished splits; zero between calls
   void* out;
   int32_t out_f32;
+  // decode step only: the new token of each sequence (bf16 [B][Hkv][D]), written to
+  // the cache at position seq_lens[b] - 1 before it is read; null for plain decode
+  const uint16_t* k_new;
+  const uint16_t* v_new;
 };
 
 // 8-byte agent-scope (device-coherent) stores and loads of float pairs: the split
@@ -279,6 +283,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const int nwp = pe - pb > wave ? (pe - pb - wave + kWaves - 1) / kWaves : 0;
   if (a.window > 0) bt_lane = lane < nwp ? bt[pb + wave + kWaves * lane] : 0;
   uint32_t* w_lds = w_lds_all[wave];
+
+  // Decode step: the wave that owns the page of position L - 1 stores the new token's
+  // K and V (quantised exactly as the cache write does) before its loads start.  Only
+  // this wave reads that page (as its last one, long after): waiting for the stores to
+  // complete, then a workgroup-scope release/acquire, orders the two.
+  if (a.k_new != nullptr) {
+    const int lp = (L - 1) / kPage;
+    const int rel = lp - pb;
+    if (rel >= 0 && lp < pe && rel % kWaves == wave) {
+      const int page = __builtin_amdgcn_readlane(bt_lane, rel / kWaves);
+      const int64_t tile = (int64_t)page * a.num_kv_heads + g;
+      const int64_t src = ((int64_t)b * a.num_kv_heads + g) * D;
+      if (lane < D / 8)
+        store_token_row<D, kFp8, kPTH>(a.k_new + src, a.v_new + src, lane, tile,
+                                       (L - 1) % kPage, const_cast<uint8_t*>(a.k_pages),
+                                       const_cast<uint8_t*>(a.v_pages),
+                                       const_cast<float*>(a.k_scales),
+                                       const_cast<float*>(a.v_scales), a.k_scale, a.v_scale);
+      wait_vmcnt<0>();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+  }
 
   // One page's inputs for this lane: K rows of its token slots, V rows of its
   // channels, and the per-token scales of the scores it will hold.
@@ -656,7 +683,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // outputs; batches of MB splits have all their loads in flight at once.  The four
   // waves' (M, L, O) then combine in a fixed tree through LDS.
   constexpr int E4L = (NE4 + kWave - 1) / kWave;
-  constexpr int MB = 4 / E4L > 1 ? 4 / E4L : 1;
+  // splits per batch (its loads all in flight); kernels held to three waves per SIMD
+  // keep the batch small to stay within their register budget
+  constexpr int MB_REGS = decode_waves_per_eu<D, G, kFp8, kPTH>() >= 3 ? 4 : 16;
+  constexpr int MB = MB_REGS / E4L > 1 ? MB_REGS / E4L : 1;
   float Mx[E4L], Ls[E4L];
   float4 Os[E4L];
 #pragma unroll
@@ -857,13 +887,12 @@ extern "C" kvq_status kvq_decode_workspace_bytes(const kvq_cache_desc* cache,
   return KVQ_OK;
 }
 
-extern "C" kvq_status kvq_decode_attention(
+static kvq_status decode_impl(
     const kvq_cache_desc* cache, const void* q, int32_t num_seqs, int32_t num_q_heads,
     const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
     int32_t max_seq_len, const kvq_scales* scales, int32_t window, float softmax_scale,
     int32_t pages_per_split, void* out, kvq_dtype out_dtype, void* workspace,
-    size_t workspace_bytes, void* stream) {
-  clear_error();
+    size_t workspace_bytes, void* stream, const void* k_new, const void* v_new) {
   DecodePlan pl;
   if (kvq_status s = plan_decode(cache, num_seqs, num_q_heads, max_seq_len, window,
                                  pages_per_split, &pl))
@@ -919,6 +948,8 @@ extern "C" kvq_status kvq_decode_attention(
                           : nullptr;
   args.out = out;
   args.out_f32 = out_dtype == KVQ_F32;
+  args.k_new = static_cast<const uint16_t*>(k_new);
+  args.v_new = static_cast<const uint16_t*>(v_new);
   auto st = static_cast<hipStream_t>(stream);
   switch (D) {
     case 64: dispatch_group<64>(G, cache, args, num_seqs, pl, st); break;
@@ -928,4 +959,32 @@ extern "C" kvq_status kvq_decode_attention(
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_decode_attention(
+    const kvq_cache_desc* cache, const void* q, int32_t num_seqs, int32_t num_q_heads,
+    const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
+    int32_t max_seq_len, const kvq_scales* scales, int32_t window, float softmax_scale,
+    int32_t pages_per_split, void* out, kvq_dtype out_dtype, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  clear_error();
+  return decode_impl(cache, q, num_seqs, num_q_heads, block_table, block_table_stride,
+                     seq_lens, max_seq_len, scales, window, softmax_scale, pages_per_split,
+                     out, out_dtype, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+extern "C" kvq_status kvq_decode_step(
+    const kvq_cache_desc* cache, const void* q, const void* k_new, const void* v_new,
+    int32_t num_seqs, int32_t num_q_heads, const int32_t* block_table,
+    int32_t block_table_stride, const int32_t* seq_lens, int32_t max_seq_len,
+    const kvq_scales* scales, int32_t window, float softmax_scale, int32_t pages_per_split,
+    void* out, kvq_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (num_seqs > 0 && (!k_new || !v_new))
+    return fail(KVQ_ERR_INVALID_ARG, "k_new or v_new is NULL");
+  if (((uintptr_t)k_new | (uintptr_t)v_new) & 15u)
+    return fail(KVQ_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  return decode_impl(cache, q, num_seqs, num_q_heads, block_table, block_table_stride,
+                     seq_lens, max_seq_len, scales, window, softmax_scale, pages_per_split,
+                     out, out_dtype, workspace, workspace_bytes, stream, k_new, v_new);
 }

@@ -131,6 +131,74 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
+// Stores one (token, KV head) row of the cache: D bf16 values of K and of V, owned by
+// D / 8 consecutive lanes (lane c of the group holds values 8c .. 8c + 7) that must be
+// active together.  fp8: per-tensor scales k_scale / v_scale, or per-token-head scales
+// amax / 448 computed here and stored in the scale pools; codes are RNE/saturating
+// e4m3 of x / scale.  K goes token-major (tile, off, d), V dim-major (tile, d, off).
+template <int D, bool kFp8, bool kPerTokenHead>
+__device__ __forceinline__ void store_token_row(const uint16_t* k, const uint16_t* v, int c,
+                                                int64_t tile, int off, uint8_t* k_pages,
+                                                uint8_t* v_pages, float* k_scales,
+                                                float* v_scales, float k_scale,
+                                                float v_scale) {
+  constexpr int kLanesPerRow = D / 8;
+  const uint4 kw = *reinterpret_cast<const uint4*>(k + c * 8);
+  const uint4 vw = *reinterpret_cast<const uint4*>(v + c * 8);
+  const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
+  const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
+  if constexpr (!kFp8) {
+    // bf16 cache (sliding-window layers kept unquantised): plain copy.
+    uint16_t* kp = reinterpret_cast<uint16_t*>(k_pages);
+    uint16_t* vp = reinterpret_cast<uint16_t*>(v_pages);
+    *reinterpret_cast<uint4*>(kp + (tile * kPage + off) * D + c * 8) = kw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vp[(tile * D + c * 8 + 2 * i) * kPage + off] = (uint16_t)(vv[i] & 0xFFFFu);
+      vp[(tile * D + c * 8 + 2 * i + 1) * kPage + off] = (uint16_t)(vv[i] >> 16);
+    }
+  } else {
+    float kf[8], vf[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kf[2 * i] = bf16_bits_to_float(kk[i] & 0xFFFFu);
+      kf[2 * i + 1] = bf16_bits_to_float(kk[i] >> 16);
+      vf[2 * i] = bf16_bits_to_float(vv[i] & 0xFFFFu);
+      vf[2 * i + 1] = bf16_bits_to_float(vv[i] >> 16);
+    }
+    float ks = k_scale, vs = v_scale;
+    if constexpr (kPerTokenHead) {
+      uint32_t ka = 0, va = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ka = max(ka, abs_bits(kf[i]));
+        va = max(va, abs_bits(vf[i]));
+      }
+#pragma unroll
+      for (int o = kLanesPerRow / 2; o >= 1; o >>= 1) {
+        ka = max(ka, (uint32_t)__shfl_xor((int)ka, o));
+        va = max(va, (uint32_t)__shfl_xor((int)va, o));
+      }
+      ks = scale_from_amax_bits(ka);
+      vs = scale_from_amax_bits(va);
+      if (c == 0) {
+        k_scales[tile * kPage + off] = ks;
+        v_scales[tile * kPage + off] = vs;
+      }
+    }
+    uint32_t klo = 0, khi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      klo |= e4m3_quantize(kf[i], ks) << (8 * i);
+      khi |= e4m3_quantize(kf[4 + i], ks) << (8 * i);
+    }
+    *reinterpret_cast<uint2*>(k_pages + (tile * kPage + off) * D + c * 8) = make_uint2(klo, khi);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      v_pages[(tile * D + c * 8 + i) * kPage + off] = (uint8_t)e4m3_quantize(vf[i], vs);
+  }
+}
+
 // Direct global -> LDS loads (each lane's 16 or 4 bytes land at lds_off + lane * size).
 // Written as inline assembly on purpose: the compiler treats its own form of these
 // loads as pending LDS writes and waits for all of them before any LDS read, which

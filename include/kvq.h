@@ -234,6 +234,30 @@ kvq_status kvq_decode_attention(const kvq_cache_desc* cache, const void* q,
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * Decode step: the cache write of each sequence's new token and the decode attention
+ * of kvq_decode_attention, in one launch.  For every sequence b with L = seq_lens[b]
+ * > 0 and every KV head h, the row k_new[b][h] / v_new[b][h] is stored at position
+ * L - 1, i.e. at slot block_table[b][(L-1)/16] * 16 + (L-1) % 16, exactly as
+ * kvq_cache_write would store it (same quantisation and scales: per-tensor
+ * scales->k_scale / v_scale, or per-token-head amax / 448), and attention then runs
+ * over positions [lo, L) as in kvq_decode_attention, reading the new row.  Results
+ * (cache contents and output) equal kvq_cache_write followed by kvq_decode_attention
+ * ("Kernel and fusion optimizations" of "vLLM FP8 KV-Cache and Attention
+ * Quantization Update": work around the attention op fused into its launch).
+ * k_new, v_new [device]: bf16 [num_seqs][num_kv_heads][D], contiguous, 16-byte
+ * aligned.  The other arguments, their preconditions and the workspace rules are
+ * those of kvq_decode_attention; the cache is written, so no other call may use it
+ * concurrently.
+ */
+kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const void* k_new,
+                           const void* v_new, int32_t num_seqs, int32_t num_q_heads,
+                           const int32_t* block_table, int32_t block_table_stride,
+                           const int32_t* seq_lens, int32_t max_seq_len,
+                           const kvq_scales* scales, int32_t window, float softmax_scale,
+                           int32_t pages_per_split, void* out, kvq_dtype out_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Chunked causal prefill over an FP8 cache ("vLLM FP8 KV-Cache and Attention
  * Quantization Update", sections "Two-level accumulation" and "Kernel and fusion
  * optimizations"; prefill of head_dim 256 in section "Per-architecture results").

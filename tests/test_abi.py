@@ -134,6 +134,17 @@ def test_decode_workspace_and_checks():
     bad = kvq.Scales(0.0, 1.0, 1.0, 1.0)
     assert L.kvq_decode_attention(*args(4096, need, scales=ctypes.byref(bad))) == kvq.binding.ERR_INVALID_ARG
 
+    # decode step: the same checks, plus the new-token rows (non-null, 16-byte aligned);
+    # every call below fails before anything is enqueued
+    step = lambda kn, vn, ws, wsb, outdt=kvq.BF16: (
+        ctypes.byref(d), 4096, kn, vn, 8, 32, 4096, 1250, 4096, 20000, ctypes.byref(sc), 0,
+        0.0, 10, 4096, outdt, ws, wsb, None)
+    assert L.kvq_decode_step(*step(None, 8192, 4096, need)) == kvq.binding.ERR_INVALID_ARG
+    assert L.kvq_decode_step(*step(8192, None, 4096, need)) == kvq.binding.ERR_INVALID_ARG
+    assert L.kvq_decode_step(*step(8200, 8192, 4096, need)) == kvq.binding.ERR_INVALID_ARG
+    assert L.kvq_decode_step(*step(8192, 8192, None, 0)) == kvq.binding.ERR_WORKSPACE
+    assert L.kvq_decode_step(*step(8192, 8192, 4096, need, kvq.FP8_E4M3)) == kvq.binding.ERR_UNSUPPORTED
+
 
 def test_quantize_argument_checks():
     L = _lib()
