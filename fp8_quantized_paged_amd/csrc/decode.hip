@@ -56,16 +56,40 @@ constexpr int kTargetWorkgroups = 512;
 // s_waitcnt immediate (gfx9 encoding) that waits for every vector memory operation
 // and leaves the LDS/export counters free.
 constexpr int kWaitVmcnt0 = 0x0F70;
-// Page buffers per wave (pages in flight + the one being computed).
-constexpr int kDecodeRing = 3;
 // Cache pages are read once per call: load them non-temporally (they bypass the
 // caches' normal retention instead of evicting the block table, scales and query).
 constexpr bool kStreamLoads = true;
 constexpr bool kSplitMajor = true;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+// Which form a decode instantiation takes (measured on MI355X over head_dim 64 / 128 /
+// 256 and group sizes 1 .. 16).  The matrix-core form (see decode_kernel) costs a
+// quarter of the vector-ALU work per page but reads K with one token row per lane
+// (each 16-lane group touches 16 rows), so it wins where the vector form is
+// ALU-bound: groups of 16, and groups of 8 up to head_dim 128.  The bf16 skip path
+// always takes the vector form.
+template <int D, int G, bool kFp8>
+constexpr bool decode_uses_mfma() { return kFp8 && (G == 16 || (G == 8 && D <= 128)); }
 
 __device__ __forceinline__ u32x4_t stream_load(const u32x4_t* p) {
+  if constexpr (kStreamLoads) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+// Eight e4m3 codes (two dwords, byte order) -> their exact f16 values.
+__device__ __forceinline__ half8_t codes8_to_f16(uint32_t lo, uint32_t hi) {
+  const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ uint32_t stream_load(const uint32_t* p) {
   if constexpr (kStreamLoads) return __builtin_nontemporal_load(p);
   else return *p;
 }
@@ -173,14 +197,23 @@ __device__ __forceinline__ void allreduce_low_bits(float (&v)[NVL]) {
 }
 
 // Waves per SIMD the register allocation aims for: three where that costs no spills
-// (head_dim 64 with per-tensor scales), otherwise the compiler's choice.
+// (head_dim 64 with per-tensor scales; the matrix-core form for groups of 8, except
+// head_dim 128 with per-token-head scales), otherwise the compiler's choice.
 template <int D, int G, bool kFp8, bool kPTH>
-constexpr int decode_waves_per_eu() { return kFp8 && !kPTH && D == 64 && G <= 8 ? 3 : 1; }
+constexpr int decode_waves_per_eu() {
+  if (decode_uses_mfma<D, G, kFp8>()) return G == 8 && (D == 64 || !kPTH) ? 3 : 1;
+  return kFp8 && !kPTH && D == 64 && G <= 8 ? 3 : 1;
+}
+// Page buffers per wave: the matrix-core form keeps one page in flight (its registers
+// buy more waves instead), the vector form two.
+template <int D, int G, bool kFp8>
+constexpr int decode_ring() { return decode_uses_mfma<D, G, kFp8>() ? 2 : 3; }
 
 template <int D, int G, bool kFp8, bool kPTH, int kRing>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     decode_waves_per_eu<D, G, kFp8, kPTH>()))) void decode_kernel(const DecodeArgs a) {
   using S = DecodeShape<D, G, kFp8>;
+  constexpr bool kMfma = decode_uses_mfma<D, G, kFp8>();
   constexpr int QW = G * D / 2;                  // query as bf16 pairs
   constexpr int NE4 = G * D / 4;                 // float4 groups of a (b, g) output
   // wave-merge slots (floats): the waves' partial outputs, later the split merge's
@@ -307,6 +340,225 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
+  float lw[G];  // this wave's weight sum per head (relative to m_all)
+  if constexpr (kMfma) {
+    // ---- matrix-core path ---------------------------------------------------------
+    // Both products take f16 operands: every e4m3 value is exact in f16, and the f16
+    // MFMA returns its sum rounded to float32 as a float32 dot product would (probe:
+    // within 0.6 ulp of the sum of |products|), whereas the fp8 MFMA's internal sum
+    // is off by up to ~1e-4 of the sum of |products| -- too coarse for scores that
+    // span tens of log2 units over outlier channels.
+    // Per page, S^T[token][head] = K . Q^T is one 16x16 accumulator (tokens = rows,
+    // query heads = columns, heads past G are zero columns).  Lane (n = l % 16,
+    // qg = l / 16) supplies row n of K (a quarter of the token's channels) and column
+    // n of Q^T (the same quarter), and receives the scores of head n at tokens
+    // 4 qg .. 4 qg + 3.  Those four scores, turned into weights, are exactly the lane's
+    // part of the A operand of O = P . V (rows = heads, k = tokens 4 qg + r), so the
+    // weights never leave the lane.  V enters as B (k = tokens, columns = 16
+    // channels of one block): lane (n, qg) reads tokens 4 qg .. 4 qg + 3 of channel
+    // 16 blk + n, one dword of the dim-major tile per block.  The running output is
+    // D / 16 accumulators; lane (n, qg) holds heads 4 qg + r of channel 16 blk + n.
+    const int n = lane & 15;
+    const int qg = lane >> 4;
+    const bool hvalid = n < G;
+    constexpr int KB = D / 4;      // K bytes a lane supplies per page
+    constexpr int NKV = KB / 16;   // 16-byte loads of them
+    constexpr int NBLK = D / 16;   // PV accumulator blocks
+    struct MPage {
+      u32x4_t k[NKV];
+      uint32_t v[NBLK];
+      float ks[4], vs[4];
+    };
+    auto mload = [&](int i, MPage& r) {
+      const int page = __builtin_amdgcn_readlane(bt_lane, i);
+      const int64_t tile = (int64_t)page * a.num_kv_heads + g;
+      const u32x4_t* ksrc = reinterpret_cast<const u32x4_t*>(
+          a.k_pages + (tile * kPage + n) * D + qg * KB);
+#pragma unroll
+      for (int j = 0; j < NKV; ++j) r.k[j] = stream_load(ksrc + j);
+      // dword 4 d + qg of the tile's channel-d row holds tokens 4 qg .. 4 qg + 3
+      const uint32_t* vsrc =
+          reinterpret_cast<const uint32_t*>(a.v_pages + tile * D * kPage) + 4 * n + qg;
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) r.v[blk] = stream_load(vsrc + 64 * blk);
+      if constexpr (kPTH) {
+        const float4 ks = *reinterpret_cast<const float4*>(a.k_scales + tile * kPage + 4 * qg);
+        const float4 vs = *reinterpret_cast<const float4*>(a.v_scales + tile * kPage + 4 * qg);
+        r.ks[0] = ks.x; r.ks[1] = ks.y; r.ks[2] = ks.z; r.ks[3] = ks.w;
+        r.vs[0] = vs.x; r.vs[1] = vs.y; r.vs[2] = vs.z; r.vs[3] = vs.w;
+      }
+    };
+
+    MPage ring[kRing];
+#pragma unroll
+    for (int r = 0; r < kRing - 1; ++r)
+      if (r < nwp) mload(r, ring[r]);
+
+    // query: fused e4m3 quantisation into this wave's LDS copy, then the B operand
+    // (f16 values of the codes; zero columns past the group)
+    half8_t qb[D / 32];
+    {
+      uint8_t* q8 = reinterpret_cast<uint8_t*>(q_lds_all[wave]);
+      const bool unit_q = a.q_scale == 1.0f;
+#pragma unroll
+      for (int u = 0; u < QPW; ++u) {
+        const int e = lane + u * kWave;
+        const float x0 = bf16_bits_to_float(qraw[u] & 0xFFFFu);
+        const float x1 = bf16_bits_to_float(qraw[u] >> 16);
+        const uint32_t c0 = unit_q ? e4m3_encode(x0) : e4m3_quantize(x0, a.q_scale);
+        const uint32_t c1 = unit_q ? e4m3_encode(x1) : e4m3_quantize(x1, a.q_scale);
+        if (e < QW) reinterpret_cast<uint16_t*>(q8)[e] = (uint16_t)(c0 | (c1 << 8));
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const uint32_t* qrow =
+          reinterpret_cast<const uint32_t*>(q8 + (hvalid ? n : 0) * D + qg * KB);
+      const uint32_t m = hvalid ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+      for (int st = 0; st < D / 32; ++st)
+        qb[st] = codes8_to_f16(qrow[2 * st] & m, qrow[2 * st + 1] & m);
+    }
+
+    // running state of head n (lanes n, n + 16, n + 32, n + 48 agree on m_h, mv_h)
+    float m_h = -INFINITY, mv_h = -INFINITY, l_part = 0.0f;
+    v4f_t acc_o[NBLK];
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) acc_o[blk] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto mcompute = [&](int i, const MPage& r) {
+      const int t0 = (pb + wave + kWaves * i) * kPage;  // first position of the page
+      // ---- QK on the matrix cores: f16 values of the codes (exact), float32 sums ----
+      // Step st takes bytes 8 st .. 8 st + 7 of each lane's quarter row, in K and Q.
+      v4f_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int st = 0; st < D / 32; ++st) {
+        const u32x4_t kw = r.k[st / 2];
+        const half8_t ka = (st & 1) ? codes8_to_f16(kw.z, kw.w) : codes8_to_f16(kw.x, kw.y);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[st], sacc, 0, 0, 0);
+      }
+      // ---- scale, mask, lazy rescale ---------------------------------------------
+      const bool full = t0 >= lo && t0 + kPage <= L;  // wave-uniform
+      float x[4], sv[4];
+      bool over = false;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int pos = t0 + 4 * qg + rr;
+        const bool vis = full || (pos >= lo && pos < L);
+        const float sc = sacc[rr] * (kPTH ? qk_base * r.ks[rr] : qk_base);
+        x[rr] = vis ? sc : -INFINITY;
+        over |= x[rr] > m_h + kRescaleSlack;
+        if constexpr (kPTH) {
+          // masked slots may hold unwritten scales: never take their logarithm
+          sv[rr] = vis ? x[rr] + log2f(r.vs[rr]) : -INFINITY;
+          over |= sv[rr] > mv_h + kRescaleSlack;
+        }
+      }
+      if (__builtin_amdgcn_ballot_w64(over && hvalid) != 0) {
+        float pm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        pm = fmaxf(pm, __shfl_xor(pm, 16));
+        pm = fmaxf(pm, __shfl_xor(pm, 32));
+        const float mn = fmaxf(m_h, pm);
+        const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_h - mn);
+        m_h = mn;
+        l_part *= alpha;
+        float beta = alpha;
+        if constexpr (kPTH) {
+          float pv = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+          pv = fmaxf(pv, __shfl_xor(pv, 16));
+          pv = fmaxf(pv, __shfl_xor(pv, 32));
+          const float mvn = fmaxf(mv_h, pv);
+          beta = mvn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mv_h - mvn);
+          mv_h = mvn;
+        }
+        // accumulator row 4 qg + rr is head 4 qg + rr, whose factor lane 4 qg + rr holds
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float br = __shfl(beta, 4 * qg + rr);
+          // in place, one register at a time (a plain product lets the compiler build
+          // a scaled copy of every accumulator beside the originals)
+#pragma unroll
+          for (int blk = 0; blk < NBLK; ++blk)
+            asm volatile("v_mul_f32 %0, %0, %1" : "+v"(acc_o[blk][rr]) : "v"(br));
+        }
+      }
+      // ---- weights: the A operand of PV, f16 (they never exceed 2^8) ---------------
+      half4_t pa;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float p = __builtin_amdgcn_exp2f(x[rr] - m_h);
+        l_part += p;
+        const float w = kPTH ? __builtin_amdgcn_exp2f(sv[rr] - mv_h) : p;
+        pa[rr] = hvalid ? (_Float16)w : (_Float16)0.0f;
+      }
+      // Slots past the sequence end (last page only) were never written: their bytes
+      // may be any code, NaN included, and a zero weight times NaN is NaN.
+      uint32_t vmask = 0xFFFFFFFFu;
+      const int valid = L - t0;  // wave-uniform
+      if (valid < kPage) {
+        const int keep = min(max(valid - 4 * qg, 0), 4);
+        vmask = keep >= 4 ? 0xFFFFFFFFu : ((1u << (8 * keep)) - 1u);
+      }
+      // ---- PV on the matrix cores: f16 x f16 (codes exact in f16), float32 sums ----
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) {
+        const uint32_t vw = r.v[blk] & vmask;
+        const half2_t lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vw, 1.0f, false);
+        const half2_t hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vw, 1.0f, true);
+        const half4_t vb = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        acc_o[blk] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, acc_o[blk], 0, 0, 0);
+      }
+    };
+
+    int i0 = 0;
+    for (; i0 + kRing <= nwp; i0 += kRing) {
+#pragma unroll
+      for (int r = 0; r < kRing; ++r) {
+        mload(min(i0 + r + kRing - 1, nwp - 1), ring[(r + kRing - 1) % kRing]);
+        mcompute(i0 + r, ring[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRing - 1; ++r)
+      if (i0 + r < nwp) mcompute(i0 + r, ring[r]);
+
+    // ---- per-head state to wave-uniform values; output to the channel layout ------
+    float lt = l_part + __shfl_xor(l_part, 16);
+    lt += __shfl_xor(lt, 32);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      m_all[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                __builtin_bit_cast(int, m_h), hh));
+      mv_all[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                 __builtin_bit_cast(int, mv_h), hh));
+      lw[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                             __builtin_bit_cast(int, lt), hh));
+    }
+    // two waves at a time through merge_lds (room for two G x D blocks)
+#pragma unroll
+    for (int round = 0; round < 2; ++round) {
+      const bool mine = (wave >> 1) == round;
+      float* slot = merge_lds + (wave & 1) * G * D;
+      if (mine) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int hh = 4 * qg + rr;
+          if (hh < G) {
+#pragma unroll
+            for (int blk = 0; blk < NBLK; ++blk) slot[hh * D + 16 * blk + n] = acc_o[blk][rr];
+          }
+        }
+      }
+      __syncthreads();
+      if (mine) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+          for (int dd = 0; dd < S::DPL; ++dd) acc[hh][dd] = slot[hh * D + lane + kWave * dd];
+      }
+      __syncthreads();
+    }
+  } else {
   // One page's inputs for this lane: K rows of its token slots, V rows of its
   // channels, and the per-token scales of the scores it will hold.
   struct PageRegs {
@@ -579,14 +831,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   for (int r = 0; r < kRing - 1; ++r)
     if (i0 + r < nwp) compute_page(i0 + r, ring[r]);
 
-  // ---- this wave's result relative to m_all: o = acc * f, l ------------------------
-  float lw[G];
+
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     float x = 0.0f;
 #pragma unroll
     for (int k = 0; k < S::NVL; ++k) x += (owner && hh_of[k] == hh) ? l_mine[k] : 0.0f;
     lw[hh] = wave_sum(x);
+  }
+  }  // vector-ALU path
+
+  // ---- this wave's result relative to m_all: o = acc * f, l ------------------------
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
     float f = kFp8 && !kPTH ? a.v_scale : 1.0f;
     if constexpr (kFp8 && kPTH)
       f = m_all[hh] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv_all[hh] - m_all[hh]);
@@ -843,7 +1100,7 @@ template <int D, int G, bool kFp8, bool kPTH>
 static void launch(const DecodeArgs& args, int32_t B, int32_t Hkv, const DecodePlan& pl,
                    hipStream_t st) {
   const unsigned blocks = (unsigned)((int64_t)B * Hkv * pl.splits);
-  decode_kernel<D, G, kFp8, kPTH, kDecodeRing><<<blocks, kThreads, 0, st>>>(args);
+  decode_kernel<D, G, kFp8, kPTH, decode_ring<D, G, kFp8>()><<<blocks, kThreads, 0, st>>>(args);
 }
 
 template <int D, int G>

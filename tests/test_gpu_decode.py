@@ -56,8 +56,11 @@ def test_tiny_decode(kvq, mode):
     assert_close_to_oracle(gotb, want, f"tiny {mode} bf16 out")
 
 
+# group sizes 1 .. 16 at every head_dim: both kernel forms (vector ALU for small
+# groups, matrix cores for groups of 8 and 16)
 @pytest.mark.parametrize("D,Hq,Hkv", [(64, 4, 4), (64, 16, 2), (128, 32, 8), (128, 16, 1),
-                                       (256, 8, 4), (64, 64, 8), (128, 8, 4)])
+                                       (256, 8, 4), (64, 64, 8), (128, 8, 4), (128, 64, 8),
+                                       (64, 32, 2), (256, 32, 2), (256, 16, 2)])
 def test_ragged_batch(kvq, D, Hq, Hkv):
     lens = [0, 1, 15, 16, 17, 100, 1000, 33]
     case = workloads.make_decode_case(50 + D + Hq, lens, Hq, Hkv, D, table="perm",

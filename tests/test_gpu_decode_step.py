@@ -105,7 +105,8 @@ def check_step(kvq, case, dtype, mode, q_scale=1.0, k_scale=1.0, v_scale=1.0, pp
 
 
 @pytest.mark.parametrize("mode", ["per_token_head", "per_tensor"])
-@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 64, 8), (256, 8, 4), (64, 4, 4)])
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 64, 8), (256, 8, 4), (64, 4, 4),
+                                       (128, 128, 8)])
 def test_decode_step_matches_separate_calls(kvq, mode, D, Hq, Hkv):
     # ragged lengths: one token, a page boundary either side, several pages
     case = workloads.make_decode_case(300 + D + Hq, [1, 16, 17, 333, 1029], Hq, Hkv, D,
