@@ -364,6 +364,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int KB = D / 4;      // K bytes a lane supplies per page
     constexpr int NKV = KB / 16;   // 16-byte loads of them
     constexpr int NBLK = D / 16;   // PV accumulator blocks
+    constexpr bool kKTrade = D == 64;
     struct MPage {
       u32x4_t k[NKV];
       uint32_t v[NBLK];
@@ -372,8 +373,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     auto mload = [&](int i, MPage& r) {
       const int page = __builtin_amdgcn_readlane(bt_lane, i);
       const int64_t tile = (int64_t)page * a.num_kv_heads + g;
+      // head_dim 64: the wave reads the 1 KB K tile in order (lane l: token l / 4,
+      // bytes 16 (l % 4) ..), four lanes to a token row, and the lanes trade the
+      // pieces into the operand layout before use; otherwise each lane reads its
+      // quarter row directly
       const u32x4_t* ksrc = reinterpret_cast<const u32x4_t*>(
-          a.k_pages + (tile * kPage + n) * D + qg * KB);
+          kKTrade ? a.k_pages + tile * kPage * D + 16 * lane
+                  : a.k_pages + (tile * kPage + n) * D + qg * KB);
 #pragma unroll
       for (int j = 0; j < NKV; ++j) r.k[j] = stream_load(ksrc + j);
       // dword 4 d + qg of the tile's channel-d row holds tokens 4 qg .. 4 qg + 3
@@ -431,9 +437,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       // ---- QK on the matrix cores: f16 values of the codes (exact), float32 sums ----
       // Step st takes bytes 8 st .. 8 st + 7 of each lane's quarter row, in K and Q.
       v4f_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+      u32x4_t kq[NKV];
+#pragma unroll
+      for (int j = 0; j < NKV; ++j) kq[j] = r.k[j];
+      if constexpr (kKTrade) {  // lane (n, qg) takes its piece from lane 4 n + qg
+        const int src = (4 * n + qg) * 4;
+        kq[0].x = __builtin_amdgcn_ds_bpermute(src, (int)r.k[0].x);
+        kq[0].y = __builtin_amdgcn_ds_bpermute(src, (int)r.k[0].y);
+        kq[0].z = __builtin_amdgcn_ds_bpermute(src, (int)r.k[0].z);
+        kq[0].w = __builtin_amdgcn_ds_bpermute(src, (int)r.k[0].w);
+      }
 #pragma unroll
       for (int st = 0; st < D / 32; ++st) {
-        const u32x4_t kw = r.k[st / 2];
+        const u32x4_t kw = kq[st / 2];
         const half8_t ka = (st & 1) ? codes8_to_f16(kw.z, kw.w) : codes8_to_f16(kw.x, kw.y);
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[st], sacc, 0, 0, 0);
       }
