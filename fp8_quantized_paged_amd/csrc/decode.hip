@@ -204,8 +204,8 @@ constexpr int decode_waves_per_eu() {
   if (decode_uses_mfma<D, G, kFp8>()) return G == 8 && (D == 64 || !kPTH) ? 3 : 1;
   return kFp8 && !kPTH && D == 64 && G <= 8 ? 3 : 1;
 }
-// Page buffers per wave: the matrix-core form keeps one page in flight (its registers
-// buy more waves instead), the vector form two.
+// Page buffers per wave (pages in flight + the one being computed): registers in the
+// vector form; LDS slots (or registers, see decode_kernel) in the matrix-core form.
 template <int D, int G, bool kFp8>
 constexpr int decode_ring() { return decode_uses_mfma<D, G, kFp8>() ? 2 : 3; }
 
@@ -364,41 +364,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int KB = D / 4;      // K bytes a lane supplies per page
     constexpr int NKV = KB / 16;   // 16-byte loads of them
     constexpr int NBLK = D / 16;   // PV accumulator blocks
-    constexpr bool kKTrade = D == 64;
-    struct MPage {
-      u32x4_t k[NKV];
+    // Page inputs reach the operand layout -- which puts 16 token rows in every
+    // 16-lane group -- in one of two ways (measured per shape):
+    //  * staged (default): direct-to-LDS loads read the K and V tiles in order (each
+    //    lane 16 bytes, a wave 1 KB of contiguous tile per load) into a per-wave ring
+    //    of LDS slots, and the operand reads come from LDS.  Slot: K tile [16][D] |
+    //    V tile [D][16] | 256 B of scales (lanes 0-15: K, 16-31: V, then repeats).
+    //    The loads are counted by hand (NL per page; wait_vmcnt before a slot is read).
+    //  * registers (head_dim 64, per-tensor scales): K is read in order, four lanes to
+    //    a token row, and the lanes trade the pieces into place with lane permutes;
+    //    V is read as one dword (4 tokens of one channel) per lane and block.
+    constexpr bool kStage = !(D == 64 && !kPTH);
+    constexpr int SLOT = kStage ? 32 * D + (kPTH ? 256 : 0) : 16;
+    constexpr int NL = 2 * (D / 64) + (kPTH ? 1 : 0);
+    __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves][kRing][SLOT];
+    uint8_t* const stage = stage_all[wave][0];
+    struct RegPage {
+      u32x4_t k;
       uint32_t v[NBLK];
-      float ks[4], vs[4];
     };
-    auto mload = [&](int i, MPage& r) {
+    RegPage regs[kStage ? 1 : kRing];
+    auto mload = [&](int i, int slot) {
       const int page = __builtin_amdgcn_readlane(bt_lane, i);
       const int64_t tile = (int64_t)page * a.num_kv_heads + g;
-      // head_dim 64: the wave reads the 1 KB K tile in order (lane l: token l / 4,
-      // bytes 16 (l % 4) ..), four lanes to a token row, and the lanes trade the
-      // pieces into the operand layout before use; otherwise each lane reads its
-      // quarter row directly
-      const u32x4_t* ksrc = reinterpret_cast<const u32x4_t*>(
-          kKTrade ? a.k_pages + tile * kPage * D + 16 * lane
-                  : a.k_pages + (tile * kPage + n) * D + qg * KB);
+      const uint8_t* kb = a.k_pages + tile * kPage * D;
+      const uint8_t* vb = a.v_pages + tile * kPage * D;
+      if constexpr (kStage) {
+        uint8_t* dst = stage + slot * SLOT;
 #pragma unroll
-      for (int j = 0; j < NKV; ++j) r.k[j] = stream_load(ksrc + j);
-      // dword 4 d + qg of the tile's channel-d row holds tokens 4 qg .. 4 qg + 3
-      const uint32_t* vsrc =
-          reinterpret_cast<const uint32_t*>(a.v_pages + tile * D * kPage) + 4 * n + qg;
+        for (int j = 0; j < D / 64; ++j)
+          lds_load16s(kb, 16 * lane + 1024 * j, lds_offset(dst + 1024 * j));
 #pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk) r.v[blk] = stream_load(vsrc + 64 * blk);
-      if constexpr (kPTH) {
-        const float4 ks = *reinterpret_cast<const float4*>(a.k_scales + tile * kPage + 4 * qg);
-        const float4 vs = *reinterpret_cast<const float4*>(a.v_scales + tile * kPage + 4 * qg);
-        r.ks[0] = ks.x; r.ks[1] = ks.y; r.ks[2] = ks.z; r.ks[3] = ks.w;
-        r.vs[0] = vs.x; r.vs[1] = vs.y; r.vs[2] = vs.z; r.vs[3] = vs.w;
+        for (int j = 0; j < D / 64; ++j)
+          lds_load16s(vb, 16 * lane + 1024 * j, lds_offset(dst + 16 * D + 1024 * j));
+        if constexpr (kPTH)
+          lds_load4((lane < 16 ? a.k_scales : a.v_scales) + tile * kPage + (lane & 15),
+                    lds_offset(dst + 32 * D));
+      } else {
+        RegPage& r = regs[slot];
+        r.k = stream_load(reinterpret_cast<const u32x4_t*>(kb) + lane);
+        // dword 4 d + qg of the tile's channel-d row holds tokens 4 qg .. 4 qg + 3
+        const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(vb) + 4 * n + qg;
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) r.v[blk] = stream_load(vsrc + 64 * blk);
       }
     };
-
-    MPage ring[kRing];
+    // every wave with pages issues kRing - 1 page loads up front (indices clamped to
+    // its last page, so the counts below hold for any page count)
+    if (nwp > 0) {
 #pragma unroll
-    for (int r = 0; r < kRing - 1; ++r)
-      if (r < nwp) mload(r, ring[r]);
+      for (int r = 0; r < kRing - 1; ++r) mload(min(r, nwp - 1), r);
+    }
 
     // query: fused e4m3 quantisation into this wave's LDS copy, then the B operand
     // (f16 values of the codes; zero columns past the group)
@@ -432,21 +448,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) acc_o[blk] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto mcompute = [&](int i, const MPage& r) {
+    auto mcompute = [&](int i, int slot) {
       const int t0 = (pb + wave + kWaves * i) * kPage;  // first position of the page
+      const uint8_t* src = stage + slot * SLOT;
+      u32x4_t kq[NKV];  // K row n, bytes qg * KB .. of it
+      uint32_t vq[NBLK];  // tokens 4 qg .. 4 qg + 3 of channel 16 blk + n
+      if constexpr (kStage) {
+#pragma unroll
+        for (int j = 0; j < NKV; ++j)
+          kq[j] = *reinterpret_cast<const u32x4_t*>(src + n * D + qg * KB + 16 * j);
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk)  // bank-conflict free
+          vq[blk] = *reinterpret_cast<const uint32_t*>(src + 16 * D + (16 * blk + n) * 16 +
+                                                       4 * qg);
+      } else {  // lane (n, qg) takes its K piece from lane 4 n + qg
+        const RegPage& r = regs[slot];
+        const int from = (4 * n + qg) * 4;
+        kq[0].x = __builtin_amdgcn_ds_bpermute(from, (int)r.k.x);
+        kq[0].y = __builtin_amdgcn_ds_bpermute(from, (int)r.k.y);
+        kq[0].z = __builtin_amdgcn_ds_bpermute(from, (int)r.k.z);
+        kq[0].w = __builtin_amdgcn_ds_bpermute(from, (int)r.k.w);
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) vq[blk] = r.v[blk];
+      }
+      float ksc[4], vsc[4];
+      if constexpr (kPTH) {
+        const float4 k4 = *reinterpret_cast<const float4*>(src + 32 * D + 16 * qg);
+        const float4 v4 = *reinterpret_cast<const float4*>(src + 32 * D + 64 + 16 * qg);
+        ksc[0] = k4.x; ksc[1] = k4.y; ksc[2] = k4.z; ksc[3] = k4.w;
+        vsc[0] = v4.x; vsc[1] = v4.y; vsc[2] = v4.z; vsc[3] = v4.w;
+      }
       // ---- QK on the matrix cores: f16 values of the codes (exact), float32 sums ----
       // Step st takes bytes 8 st .. 8 st + 7 of each lane's quarter row, in K and Q.
       v4f_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
-      u32x4_t kq[NKV];
-#pragma unroll
-      for (int j = 0; j < NKV; ++j) kq[j] = r.k[j];
-      if constexpr (kKTrade) {  // lane (n, qg) takes its piece from lane 4 n + qg
-        const int src = (4 * n + qg) * 4;
-        kq[0].x = __builtin_amdgcn_ds_bpermute(src, (int)r.k[0].x);
-        kq[0].y = __builtin_amdgcn_ds_bpermute(src, (int)r.k[0].y);
-        kq[0].z = __builtin_amdgcn_ds_bpermute(src, (int)r.k[0].z);
-        kq[0].w = __builtin_amdgcn_ds_bpermute(src, (int)r.k[0].w);
-      }
 #pragma unroll
       for (int st = 0; st < D / 32; ++st) {
         const u32x4_t kw = kq[st / 2];
@@ -461,12 +495,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       for (int rr = 0; rr < 4; ++rr) {
         const int pos = t0 + 4 * qg + rr;
         const bool vis = full || (pos >= lo && pos < L);
-        const float sc = sacc[rr] * (kPTH ? qk_base * r.ks[rr] : qk_base);
+        const float sc = sacc[rr] * (kPTH ? qk_base * ksc[rr] : qk_base);
         x[rr] = vis ? sc : -INFINITY;
         over |= x[rr] > m_h + kRescaleSlack;
         if constexpr (kPTH) {
           // masked slots may hold unwritten scales: never take their logarithm
-          sv[rr] = vis ? x[rr] + log2f(r.vs[rr]) : -INFINITY;
+          sv[rr] = vis ? x[rr] + log2f(vsc[rr]) : -INFINITY;
           over |= sv[rr] > mv_h + kRescaleSlack;
         }
       }
@@ -518,7 +552,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       // ---- PV on the matrix cores: f16 x f16 (codes exact in f16), float32 sums ----
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk) {
-        const uint32_t vw = r.v[blk] & vmask;
+        const uint32_t vw = vq[blk] & vmask;
         const half2_t lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vw, 1.0f, false);
         const half2_t hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vw, 1.0f, true);
         const half4_t vb = {lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -526,17 +560,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       }
     };
 
+    // Page i lives in slot i % kRing.  A full step refills the slot computed last
+    // (its LDS reads done: lgkmcnt 0) and computes the next page once all but the
+    // newest kRing - 1 page loads have landed.
     int i0 = 0;
     for (; i0 + kRing <= nwp; i0 += kRing) {
 #pragma unroll
       for (int r = 0; r < kRing; ++r) {
-        mload(min(i0 + r + kRing - 1, nwp - 1), ring[(r + kRing - 1) % kRing]);
-        mcompute(i0 + r, ring[r]);
+        if constexpr (kStage) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        mload(min(i0 + r + kRing - 1, nwp - 1), (r + kRing - 1) % kRing);
+        if constexpr (kStage) wait_vmcnt<(kRing - 1) * NL>();
+        mcompute(i0 + r, r);
       }
     }
-#pragma unroll
-    for (int r = 0; r < kRing - 1; ++r)
-      if (i0 + r < nwp) mcompute(i0 + r, ring[r]);
+    // the last pages (fewer than kRing, already loaded): the loads issued after
+    // page i0 + r number kRing - 2 - r pages
+    static_assert(kRing == 2 || kRing == 3, "staging ring of 2 or 3 slots");
+    if (i0 < nwp) {
+      if constexpr (kStage) wait_vmcnt<(kRing - 2) * NL>();
+      mcompute(i0, 0);
+    }
+    if constexpr (kRing == 3) {
+      if (i0 + 1 < nwp) {
+        if constexpr (kStage) wait_vmcnt<0>();
+        mcompute(i0 + 1, 1);
+      }
+    }
 
     // ---- per-head state to wave-uniform values; output to the channel layout ------
     float lt = l_part + __shfl_xor(l_part, 16);
