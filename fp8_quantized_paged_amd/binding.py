@@ -159,13 +159,19 @@ def _torch():
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: the c_void_p argtypes convert it without an extra Python object
+    return None if t is None else t.data_ptr()
 
 
-def _stream(stream=None):
+def _stream(stream=None, device=None):
+    """Raw stream handle: ``stream`` if given, else torch's current stream of
+    ``device`` (a torch.device of the call's tensors; the current device if None)."""
+    if stream is not None:
+        return stream.cuda_stream
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    idx = device.index if device is not None and device.index is not None \
+        else torch.cuda.current_device()
+    return torch._C._cuda_getCurrentRawStream(idx)
 
 
 class PagedCache:
@@ -194,11 +200,16 @@ class PagedCache:
             self.k_scales = self.v_scales = None
 
     def desc(self) -> CacheDesc:
-        return CacheDesc(_DTYPES[self.dtype], _MODES[self.mode], self.num_pages, PAGE_SIZE,
-                         self.num_kv_heads, self.head_dim,
-                         self.k_pages.data_ptr(), self.v_pages.data_ptr(),
-                         None if self.k_scales is None else self.k_scales.data_ptr(),
-                         None if self.v_scales is None else self.v_scales.data_ptr())
+        """The C descriptor of the pools (built once: the pool tensors never move)."""
+        d = getattr(self, "_desc", None)
+        if d is None:
+            d = self._desc = CacheDesc(
+                _DTYPES[self.dtype], _MODES[self.mode], self.num_pages, PAGE_SIZE,
+                self.num_kv_heads, self.head_dim,
+                self.k_pages.data_ptr(), self.v_pages.data_ptr(),
+                None if self.k_scales is None else self.k_scales.data_ptr(),
+                None if self.v_scales is None else self.v_scales.data_ptr())
+        return d
 
     @property
     def nbytes(self) -> int:
@@ -214,14 +225,14 @@ def cache_write(cache: PagedCache, k, v, slot_mapping, k_scale: float = 1.0,
     d = cache.desc()
     _check(_lib.kvq_cache_write(ctypes.byref(d), _ptr(k), _ptr(v), token_stride,
                                 _ptr(slot_mapping), int(slot_mapping.numel()),
-                                k_scale, v_scale, _stream(stream)), "cache_write")
+                                k_scale, v_scale, _stream(stream, k.device)), "cache_write")
 
 
 def quantize_fp8(x, scale: float, out=None, stream=None):
     torch = _torch()
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    _check(_lib.kvq_quantize_fp8(_ptr(x), x.numel(), scale, _ptr(out), _stream(stream)),
+    _check(_lib.kvq_quantize_fp8(_ptr(x), x.numel(), scale, _ptr(out), _stream(stream, x.device)),
            "quantize_fp8")
     return out
 
@@ -268,7 +279,7 @@ def decode_attention(cache: PagedCache, q, block_table, seq_lens, max_seq_len: i
         ctypes.byref(d), _ptr(q), B, Hq, _ptr(block_table), block_table.shape[1],
         _ptr(seq_lens), max_seq_len, ctypes.byref(scales), window, softmax_scale,
         pages_per_split, _ptr(out), _DTYPES[out_dtype], _ptr(workspace),
-        workspace.numel(), _stream(stream)), "decode_attention")
+        workspace.numel(), _stream(stream, q.device)), "decode_attention")
     return out
 
 
@@ -293,7 +304,7 @@ def decode_step(cache: PagedCache, q, k_new, v_new, block_table, seq_lens, max_s
         ctypes.byref(d), _ptr(q), _ptr(k_new), _ptr(v_new), B, Hq, _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), max_seq_len, ctypes.byref(scales), window,
         softmax_scale, pages_per_split, _ptr(out), _DTYPES[out_dtype], _ptr(workspace),
-        workspace.numel(), _stream(stream)), "decode_step")
+        workspace.numel(), _stream(stream, q.device)), "decode_step")
     return out
 
 
@@ -314,5 +325,5 @@ def prefill_attention(cache: PagedCache, q, cu_q_lens, block_table, seq_lens,
         ctypes.byref(d), _ptr(q), _ptr(cu_q_lens), int(seq_lens.numel()), Hq,
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_q_len,
         ctypes.byref(scales), int(causal), window, softmax_scale, _ptr(out),
-        _DTYPES[out_dtype], _stream(stream)), "prefill_attention")
+        _DTYPES[out_dtype], _stream(stream, q.device)), "prefill_attention")
     return out

@@ -59,7 +59,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // Cache pages are read once per call: load them non-temporally (they bypass the
 // caches' normal retention instead of evicting the block table, scales and query).
 constexpr bool kStreamLoads = true;
-constexpr bool kSplitMajor = true;
+constexpr int kXcds = 8;  // MI355X: workgroups are dealt to 8 XCDs round robin
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
@@ -228,15 +228,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
-  // Workgroup order: split-major (all (b, g) units of split 0, then split 1, ...),
-  // so the workgroups in flight together read neighbouring pages of the pools.
-  const int nunits = (int)(gridDim.x / (unsigned)a.splits);
-  const int s = kSplitMajor ? (int)(blockIdx.x / (unsigned)nunits)
-                            : (int)(blockIdx.x % (unsigned)a.splits);
-  const int ug = kSplitMajor ? (int)(blockIdx.x % (unsigned)nunits)
-                             : (int)(blockIdx.x / (unsigned)a.splits);  // b * Hkv + g
-  const int g = ug % a.num_kv_heads;
-  const int b = ug / a.num_kv_heads;
+  // Workgroup order.  Pairs (b, s) run split-major (all sequences of split 0, then
+  // split 1, ...), so the workgroups in flight together read neighbouring pages of
+  // the pools.  The Hkv workgroups of one pair -- every KV head of the same pages --
+  // are numbered 8 apart, which places them on one XCD (workgroups are dealt to the
+  // eight XCDs round robin) so they stream the pages' head tiles side by side;
+  // without a multiple of 8 pairs the heads of a pair are simply consecutive.
+  const int H = a.num_kv_heads;
+  const int npairs = (int)(gridDim.x / (unsigned)H);
+  const int nb = npairs / a.splits;
+  int bs, g;
+  if (npairs % kXcds == 0) {
+    const int blk = (int)blockIdx.x;
+    bs = kXcds * (blk / (kXcds * H)) + blk % kXcds;
+    g = (blk / kXcds) % H;
+  } else {
+    bs = (int)blockIdx.x / H;
+    g = (int)blockIdx.x % H;
+  }
+  const int s = bs / nb;
+  const int b = bs % nb;
+  const int ug = b * H + g;
   const int* bt = a.block_table + (int64_t)b * a.bt_stride;
   const int64_t row0 = (int64_t)ug * G;  // first output row: b * Hq + g * G
   // Issued before the sequence length is known: the query words of the group and,
