@@ -330,27 +330,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   uint32_t* w_lds = w_lds_all[wave];
 
   // Decode step: the wave that owns the page of position L - 1 stores the new token's
-  // K and V (quantised exactly as the cache write does) before its loads start.  Only
-  // this wave reads that page (as its last one, long after): waiting for the stores to
-  // complete, then a workgroup-scope release/acquire, orders the two.
+  // K and V (quantised exactly as the cache write does).  That page is the wave's last;
+  // the store is issued before the load of that page -- after the first page loads
+  // when the last page is not among them, so its latency overlaps them.  One wave's
+  // memory operations are performed in program order (the AMDGPU memory model needs
+  // no instruction for wavefront-scope ordering), so wavefront-scope fences, which
+  // only keep the compiler from moving loads above the stores, order the two.
+  bool app_owner = false;
+  int app_page = 0;
   if (a.k_new != nullptr) {
     const int lp = (L - 1) / kPage;
     const int rel = lp - pb;
-    if (rel >= 0 && lp < pe && rel % kWaves == wave) {
-      const int page = __builtin_amdgcn_readlane(bt_lane, rel / kWaves);
-      const int64_t tile = (int64_t)page * a.num_kv_heads + g;
-      const int64_t src = ((int64_t)b * a.num_kv_heads + g) * D;
-      if (lane < D / 8)
-        store_token_row<D, kFp8, kPTH>(a.k_new + src, a.v_new + src, lane, tile,
-                                       (L - 1) % kPage, const_cast<uint8_t*>(a.k_pages),
-                                       const_cast<uint8_t*>(a.v_pages),
-                                       const_cast<float*>(a.k_scales),
-                                       const_cast<float*>(a.v_scales), a.k_scale, a.v_scale);
-      wait_vmcnt<0>();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    }
+    app_owner = rel >= 0 && lp < pe && rel % kWaves == wave;
+    if (app_owner) app_page = __builtin_amdgcn_readlane(bt_lane, rel / kWaves);
   }
+  auto append = [&]() {
+    const int64_t tile = (int64_t)app_page * a.num_kv_heads + g;
+    const int64_t src = ((int64_t)b * a.num_kv_heads + g) * D;
+    if (lane < D / 8)
+      store_token_row<D, kFp8, kPTH>(a.k_new + src, a.v_new + src, lane, tile,
+                                     (L - 1) % kPage, const_cast<uint8_t*>(a.k_pages),
+                                     const_cast<uint8_t*>(a.v_pages),
+                                     const_cast<float*>(a.k_scales),
+                                     const_cast<float*>(a.v_scales), a.k_scale, a.v_scale);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // whether the first page loads (kRing - 1 of them) include the wave's last page
+  const bool app_early = app_owner && nwp - 1 < kRing - 1;
+  const bool app_late = app_owner && !app_early;
+  if (app_early) append();
 
   float lw[G];  // this wave's weight sum per head (relative to m_all)
   if constexpr (kMfma) {
@@ -427,6 +436,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int r = 0; r < kRing - 1; ++r) mload(min(r, nwp - 1), r);
     }
+    if (app_late) append();
 
     // query: fused e4m3 quantisation into this wave's LDS copy, then the B operand
     // (f16 values of the codes; zero columns past the group)
@@ -857,6 +867,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int r = 0; r < kRing - 1; ++r)
     if (r < nwp) load_page(r, ring[r]);
+  if (app_late) append();
 
   // ---- query of the group: fused e4m3 quantisation (fp8) or plain bf16 ----------
   // Every wave quantises the whole group into its own LDS copy, so only a wave-level
