@@ -115,6 +115,11 @@ def test_decode_workspace_and_checks():
     # explicit pages_per_split: splits = ceil(1250 / 10) = 125
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 32, 20000, 0, 10, ctypes.byref(n)) == 0
     assert n.value == 256 + 8 * 32 * 125 * 130 * 4
+    # one long sequence: the automatic split count stops at 32 per (sequence, KV head)
+    # (8,192 pages -> 256 pages per split)
+    one = _desc(mode=kvq.PER_TENSOR)
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(one), 1, 32, 131072, 0, 0, ctypes.byref(n)) == 0
+    assert n.value == 256 + 1 * 32 * 32 * 130 * 4
     # a window bounds the visible pages: 128 keys span at most 9 pages
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 32, 20000, 128, 4, ctypes.byref(n)) == 0
     assert n.value == 256 + 8 * 32 * 3 * 130 * 4
