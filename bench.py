@@ -61,6 +61,12 @@ def parse():
                     help="FETCH_SIZE,WRITE_SIZE rocprofv3 --pmc output directories (csv): "
                          "write the decode kernel's measured HBM bytes per launch to "
                          "profiles/ and exit (no GPU needed)")
+    ap.add_argument("--itl", action="store_true",
+                    help="instead of the headline: the attention-only inter-token-latency "
+                         "sweep over context lengths (fp8 vs bf16 vs bf16 sliding-window "
+                         "layers) and its slopes; prints its own JSON line")
+    ap.add_argument("--itl-contexts", default="1024,4096,16384,32768,65536,131072",
+                    help="context lengths of the --itl sweep")
     return ap.parse_args()
 
 
@@ -208,6 +214,144 @@ def cpu_baseline(case, nseq, reps=1):
                       f"of {reps} runs; value = their algorithmic bytes / oracle seconds"}
 
 
+# ---- attention-only inter-token latency over context length ---------------------------------
+
+def run_itl(args):
+    """Per decode step, the attention of every layer of a model (fused new-token write +
+    decode, one HIP graph replay per step), over context lengths: Llama-3.1-8B-shaped
+    (32 layers, 8 sequences, 32/8 heads, D 128) with an fp8 (per-token-head) or a bf16
+    cache, and gpt-oss-20b-shaped (24 layers alternating full attention and a 128-token
+    window, 8 sequences, 64/8 heads, D 64) with every layer fp8, every layer bf16, or
+    full layers fp8 and window layers bf16 (the skip path).  Step time = a + slope *
+    context is fitted per variant; the fp8 / bf16 slope ratio and the context where fp8
+    overtakes bf16 follow.  Layers rotate over distinct caches totalling >= 1 GiB (>
+    the 256 MB Infinity Cache), so no layer is served from the previous one; window
+    layers keep only their visible pages (the rest of their block table points at a
+    page they never read)."""
+    import numpy as np
+    import torch
+
+    import fp8_quantized_paged_amd as kvq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ones = kvq.Scales(1.0, 1.0, 1.0, 1.0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20240607)
+    contexts = [int(x) for x in args.itl_contexts.split(",") if x]
+
+    def make_layer(B, L, Hq, Hkv, D, dtype, window):
+        """One layer's cache holding L tokens per sequence (N(0,1) bf16 rows through the
+        cache write), its block table, query and new-token rows."""
+        pages = (L + 15) // 16
+        if window:
+            vis = (window + 15) // 16 + 1
+            first = max(0, pages - vis)
+            P = B * (pages - first) + 1
+            bt = torch.zeros((B, pages), dtype=torch.int32, device=dev)
+            own = torch.arange(1, P, dtype=torch.int32, device=dev).reshape(B, -1)
+            bt[:, first:] = own
+        else:
+            first = 0
+            P = B * pages
+            bt = torch.arange(P, dtype=torch.int32, device=dev).reshape(B, pages)
+        c = kvq.PagedCache(P, Hkv, D, dtype, "per_token_head")
+        # slots of every written token (positions first*16 .. L-1 of each sequence)
+        pos = torch.arange(first * 16, L, device=dev)
+        slots = (bt[:, (pos // 16)].to(torch.int64) * 16 + pos % 16).reshape(-1)
+        for i in range(0, slots.numel(), 1 << 18):
+            sl = slots[i:i + (1 << 18)]
+            k = torch.randn((sl.numel(), Hkv, D), device=dev, generator=gen).to(torch.bfloat16)
+            v = torch.randn((sl.numel(), Hkv, D), device=dev, generator=gen).to(torch.bfloat16)
+            kvq.cache_write(c, k, v, sl)
+        q = torch.randn((B, Hq, D), device=dev, generator=gen).to(torch.bfloat16)
+        kn = torch.randn((B, Hkv, D), device=dev, generator=gen).to(torch.bfloat16)
+        vn = torch.randn((B, Hkv, D), device=dev, generator=gen).to(torch.bfloat16)
+        ws = kvq.decode_workspace(c, B, Hq, L, window, 0, dev)
+        return (c, q, kn, vn, bt, torch.full((B,), L, dtype=torch.int32, device=dev),
+                window, ws, c.nbytes)
+
+    def step_us(layers, order, B, Hq, D, L):
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            for i in order:
+                c, q, kn, vn, bt, sl, win, ws, _ = layers[i]
+                kvq.decode_step(c, q, kn, vn, bt, sl, L, ones, window=win, out=out,
+                                workspace=ws)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        n = 10
+        e0.record()
+        for _ in range(n):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    def model_step(nlayers, kinds, B, Hq, Hkv, D, L):
+        """kinds[i]: (dtype, window) of layer i; distinct caches per kind until >= 1 GiB."""
+        layers, order, by_kind = [], [], {}
+        for i in range(nlayers):
+            kind = kinds[i % len(kinds)]
+            lst = by_kind.setdefault(kind, [])
+            total = sum(layers[j][-1] for j in lst)
+            if len(lst) < 2 or (total < (1 << 30) and len(lst) < nlayers):
+                layers.append(make_layer(B, L, Hq, Hkv, D, kind[0], kind[1]))
+                lst.append(len(layers) - 1)
+            order.append(lst[i // len(kinds) % len(lst)])
+        us = step_us(layers, order, B, Hq, D, L)
+        del layers
+        torch.cuda.empty_cache()
+        return us
+
+    models = {
+        "llama-3.1-8b (32 layers, 8 seqs, 32/8 heads, D 128)": (
+            32, 8, 32, 8, 128,
+            {"fp8": [("fp8", 0)], "bf16": [("bf16", 0)]}),
+        "gpt-oss-20b (24 layers alternating full / window 128, 8 seqs, 64/8 heads, D 64)": (
+            24, 8, 64, 8, 64,
+            {"fp8": [("fp8", 0), ("fp8", 128)], "bf16": [("bf16", 0), ("bf16", 128)],
+             "fp8 + bf16 window layers": [("fp8", 0), ("bf16", 128)]}),
+    }
+    res = {"metric": "attention-only decode step time vs context (inter-token latency "
+                     "slope)", "unit": "us per step", "contexts": contexts, "models": {}}
+    for mname, (nl, B, Hq, Hkv, D, variants) in models.items():
+        mres = {}
+        for vname, kinds in variants.items():
+            times = []
+            for L in contexts:
+                t = model_step(nl, kinds, B, Hq, Hkv, D, L)
+                times.append(round(t, 1))
+                log(f"itl: {mname.split(' ')[0]} {vname} ctx {L}: {t:.1f} us")
+            slope, icpt = np.polyfit(np.asarray(contexts, float), np.asarray(times), 1)
+            mres[vname] = {"us": times, "slope_us_per_1k_ctx": round(slope * 1e3, 3),
+                           "intercept_us": round(icpt, 1)}
+        base = mres["bf16"]["slope_us_per_1k_ctx"]
+        for vname, v in mres.items():
+            if vname == "bf16":
+                continue
+            v["slope_ratio_vs_bf16"] = round(v["slope_us_per_1k_ctx"] / base, 3)
+            ds = base - v["slope_us_per_1k_ctx"]
+            di = v["intercept_us"] - mres["bf16"]["intercept_us"]
+            v["break_even_ctx_vs_bf16"] = round(di / ds * 1e3) if ds > 0 and di > 0 else 0
+        res["models"][mname] = mres
+    print(json.dumps(res), flush=True)
+
+
 # ---- GPU legs -------------------------------------------------------------------------------
 
 class Timer:
@@ -243,6 +387,11 @@ def main():
     if args.traffic_from:
         fetch_dir, write_dir = args.traffic_from.split(",")
         write_traffic_profile(fetch_dir, write_dir)
+        return
+    if args.itl:
+        if args.gpus != 1:
+            sys.exit("bench.py runs on one GPU only")
+        run_itl(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build "
