@@ -5,8 +5,8 @@ include/kvq.h); this package is its thin Python binding.  Importing it fails whe
 the library is not built: there is no CPU or PyTorch fallback.
 """
 from .binding import (  # noqa: F401
-    BF16, F32, FP8_E4M3, PAGE_SIZE, PER_TENSOR, PER_TOKEN_HEAD, SKIP_SLIDING_WINDOW,
-    WARN_UNCALIBRATED_Q_OR_PROB, CacheDesc, KvqError, PagedCache, Scales, abi_version,
+    BF16, F32, FP8_E4M3, PAGE_SIZE, PER_KV_HEAD, PER_TENSOR, PER_TOKEN_HEAD,
+    SKIP_SLIDING_WINDOW, WARN_UNCALIBRATED_Q_OR_PROB, CacheDesc, KvqError, PagedCache, Scales, abi_version,
     cache_write, decode_attention, decode_step, decode_workspace, decode_workspace_bytes,
     exported, header_functions,
     last_error, layer_kv_dtype, prefill_attention, quantize_fp8, resolve_scales,

@@ -47,11 +47,12 @@ if len(_hip_runtimes_mapped()) > 1:
 # ---- enums and structs (mirror include/kvq.h) -------------------------------------
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, FP8_E4M3, F32 = 0, 1, 2
-PER_TENSOR, PER_TOKEN_HEAD = 0, 1
+PER_TENSOR, PER_TOKEN_HEAD, PER_KV_HEAD = 0, 1, 2
 WARN_UNCALIBRATED_Q_OR_PROB = 1
 SKIP_SLIDING_WINDOW = 1
 PAGE_SIZE = 16
-_MODES = {"per_tensor": PER_TENSOR, "per_token_head": PER_TOKEN_HEAD}
+_MODES = {"per_tensor": PER_TENSOR, "per_token_head": PER_TOKEN_HEAD,
+          "per_kv_head": PER_KV_HEAD}
 _DTYPES = {"bf16": BF16, "fp8": FP8_E4M3, "f32": F32}
 
 
@@ -178,12 +179,14 @@ class PagedCache:
     """One layer's paged KV cache in the layout include/kvq.h fixes.
 
     fp8: k_pages uint8 [P][H][16][D] (token-major), v_pages uint8 [P][H][D][16]
-    (dim-major), per-token-head scale pools float32 [P][H][16].
+    (dim-major), per-token-head scale pools float32 [P][H][16], or per-KV-head scale
+    arrays float32 [H] (``k_head_scales`` / ``v_head_scales``, default 1.0).
     bf16: the same index orders with bfloat16 elements, no scales.
     """
 
     def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int,
-                 dtype: str = "fp8", mode: str = "per_token_head", device="cuda"):
+                 dtype: str = "fp8", mode: str = "per_token_head", device="cuda",
+                 k_head_scales=None, v_head_scales=None):
         torch = _torch()
         self.num_pages, self.num_kv_heads, self.head_dim = num_pages, num_kv_heads, head_dim
         self.dtype, self.mode = dtype, mode
@@ -196,6 +199,13 @@ class PagedCache:
             self.k_scales = torch.zeros((num_pages, num_kv_heads, PAGE_SIZE),
                                         dtype=torch.float32, device=device)
             self.v_scales = torch.zeros_like(self.k_scales)
+        elif dtype == "fp8" and mode == "per_kv_head":
+            def arr(x):
+                t = torch.ones(num_kv_heads, dtype=torch.float32)
+                if x is not None:
+                    t[:] = torch.as_tensor(x, dtype=torch.float32).reshape(num_kv_heads)
+                return t.to(device)
+            self.k_scales, self.v_scales = arr(k_head_scales), arr(v_head_scales)
         else:
             self.k_scales = self.v_scales = None
 

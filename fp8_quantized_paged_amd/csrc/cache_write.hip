@@ -4,6 +4,8 @@
 // (blog.secrett2633.cloud), section "Per-Token-Head vs Per-Tensor quantization":
 // per-tensor mode uses one K and one V scale per layer; per-token-head mode has
 // the kernel compute a scale for every (token, head) when it stores the cache.
+// "vLLM FP8 KV-Cache and Attention Quantization Update", section "Kernel and fusion
+// optimizations": per-KV-head mode quantises head h with its own layer scale.
 // Scale = amax / 448, code = clamp(round_rne(v / scale), +-448).
 //
 // Work split: one row = one (token, KV head) of D bf16 values; D/8 lanes own a
@@ -37,8 +39,16 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   const int64_t tile = page * num_heads + h;  // (page, head) tile index
 
   const int64_t src = (int64_t)t * token_stride + (int64_t)h * D;
+  // per-KV-head mode: k_scales / v_scales hold one scale per head (per-tensor: null)
+  float ks = k_scale, vs = v_scale;
+  if constexpr (kFp8 && !kPerTokenHead) {
+    if (k_scales != nullptr) {
+      ks = k_scales[h];
+      vs = v_scales[h];
+    }
+  }
   store_token_row<D, kFp8, kPerTokenHead>(k + src, v + src, c, tile, off, k_pages, v_pages,
-                                          k_scales, v_scales, k_scale, v_scale);
+                                          k_scales, v_scales, ks, vs);
 }
 
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x,
@@ -80,6 +90,10 @@ static void launch_cache_write(const kvq_cache_desc* c, const void* k, const voi
         kk, vv, stride, slots, n, c->num_kv_heads, kp, vp, nullptr, nullptr, 1.f, 1.f);
   else if (c->mode == KVQ_SCALE_PER_TOKEN_HEAD)
     cache_write_kernel<D, true, true><<<grid, 256, 0, st>>>(
+        kk, vv, stride, slots, n, c->num_kv_heads, kp, vp, c->k_scales, c->v_scales,
+        1.f, 1.f);
+  else if (c->mode == KVQ_SCALE_PER_KV_HEAD)
+    cache_write_kernel<D, true, false><<<grid, 256, 0, st>>>(
         kk, vv, stride, slots, n, c->num_kv_heads, kp, vp, c->k_scales, c->v_scales,
         1.f, 1.f);
   else

@@ -122,9 +122,10 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const uint8_t* k_pages;
   const uint8_t* v_pages;
-  const float* k_scales;
+  const float* k_scales;  // per-token-head pools [P][Hkv][16], or per-KV-head [Hkv]
   const float* v_scales;
-  float q_scale, k_scale, v_scale, sm_log2;
+  float q_scale, k_scale, v_scale, sm_log2;  // per-tensor K/V scales
+  int32_t head_scales;   // k_scales / v_scales are per-KV-head arrays
   int32_t window;
   float* o_part;      // [B*Hkv][splits][G][D]
   float* ml_part;     // [B*Hkv][splits][G][2]: reference max (log2), weight sum
@@ -288,7 +289,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                                   // filled once the query is in LDS
 
   // score multiplier (log2 domain); per-token K scales multiply in per page
-  const float qk_base = kFp8 ? a.q_scale * a.sm_log2 * (kPTH ? 1.0f : a.k_scale) : a.sm_log2;
+  // this KV head's layer scales: per-KV-head arrays or the per-tensor pair
+  float k_scale_g = a.k_scale, v_scale_g = a.v_scale;
+  if constexpr (kFp8 && !kPTH) {
+    if (a.head_scales) {
+      k_scale_g = a.k_scales[g];
+      v_scale_g = a.v_scales[g];
+    }
+  }
+  const float qk_base = kFp8 ? a.q_scale * a.sm_log2 * (kPTH ? 1.0f : k_scale_g) : a.sm_log2;
 
   // indices of the scores this lane holds after the butterfly
   int idx0 = 0;
@@ -353,7 +362,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                                      (L - 1) % kPage, const_cast<uint8_t*>(a.k_pages),
                                      const_cast<uint8_t*>(a.v_pages),
                                      const_cast<float*>(a.k_scales),
-                                     const_cast<float*>(a.v_scales), a.k_scale, a.v_scale);
+                                     const_cast<float*>(a.v_scales), k_scale_g, v_scale_g);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
@@ -933,7 +942,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // ---- this wave's result relative to m_all: o = acc * f, l ------------------------
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    float f = kFp8 && !kPTH ? a.v_scale : 1.0f;
+    float f = kFp8 && !kPTH ? v_scale_g : 1.0f;
     if constexpr (kFp8 && kPTH)
       f = m_all[hh] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv_all[hh] - m_all[hh]);
 #pragma unroll
@@ -1288,6 +1297,7 @@ static kvq_status decode_impl(
   args.q_scale = scales ? scales->q_scale : 1.0f;
   args.k_scale = scales ? scales->k_scale : 1.0f;
   args.v_scale = scales ? scales->v_scale : 1.0f;
+  args.head_scales = cache->dtype == KVQ_FP8_E4M3 && cache->mode == KVQ_SCALE_PER_KV_HEAD;
   args.sm_log2 = sm * kLog2e;
   args.window = window;
   args.counters = pl.bytes ? static_cast<int32_t*>(workspace) : nullptr;

@@ -36,11 +36,17 @@ kvq_status check_cache(const kvq_cache_desc* c) {
   if ((((uintptr_t)c->k_pages) | ((uintptr_t)c->v_pages)) & 255u)
     return fail(KVQ_ERR_INVALID_ARG, "page pools must be 256-byte aligned");
   if (c->dtype == KVQ_FP8_E4M3) {
-    if (c->mode != KVQ_SCALE_PER_TENSOR && c->mode != KVQ_SCALE_PER_TOKEN_HEAD)
+    if (c->mode != KVQ_SCALE_PER_TENSOR && c->mode != KVQ_SCALE_PER_TOKEN_HEAD &&
+        c->mode != KVQ_SCALE_PER_KV_HEAD)
       return fail(KVQ_ERR_INVALID_ARG, "scale mode %d", (int)c->mode);
     if (c->mode == KVQ_SCALE_PER_TOKEN_HEAD && c->num_pages > 0 &&
         (!c->k_scales || !c->v_scales))
       return fail(KVQ_ERR_INVALID_ARG, "per-token-head cache without scale pools");
+    if (c->mode == KVQ_SCALE_PER_KV_HEAD && (!c->k_scales || !c->v_scales))
+      return fail(KVQ_ERR_INVALID_ARG, "per-KV-head cache without scale arrays");
+    if (c->mode == KVQ_SCALE_PER_KV_HEAD && ((((uintptr_t)c->k_scales) |
+                                              ((uintptr_t)c->v_scales)) & 3u))
+      return fail(KVQ_ERR_INVALID_ARG, "scale arrays must be 4-byte aligned");
   }
   return KVQ_OK;
 }
@@ -73,7 +79,8 @@ kvq_status kvq_resolve_scales(kvq_scale_mode mode, float k_in, float v_in, float
   uint32_t warn = 0;
   if (mode == KVQ_SCALE_PER_TOKEN_HEAD) {
     *out = kvq_scales{1.0f, 1.0f, 1.0f, 1.0f};
-  } else if (mode == KVQ_SCALE_PER_TENSOR) {
+  } else if (mode == KVQ_SCALE_PER_TENSOR || mode == KVQ_SCALE_PER_KV_HEAD) {
+    // per-KV-head: the same rules for one head's (k, v) pair
     float k, v;
     if (k_in > 0.0f && v_in > 0.0f) {
       k = k_in;

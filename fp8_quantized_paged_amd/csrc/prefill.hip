@@ -137,9 +137,10 @@ struct PrefillArgs {
   const int32_t* seq_lens;
   const uint8_t* k_pages;
   const uint8_t* v_pages;
-  const float* k_scales;
+  const float* k_scales;  // per-token-head pools [P][Hkv][16], or per-KV-head [Hkv]
   const float* v_scales;
-  float q_scale, k_scale, v_scale, prob_scale, sm_log2;
+  float q_scale, k_scale, v_scale, prob_scale, sm_log2;  // per-tensor K/V scales
+  int32_t head_scales;   // k_scales / v_scales are per-KV-head arrays
   int32_t causal, window;
   void* out;
   int32_t out_f32;
@@ -289,7 +290,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
     }
     barrier_lds();
   };
-  const float qk_base = a.q_scale * a.sm_log2 * (kPTH ? 1.0f : a.k_scale);
+  // this KV head's layer scales: per-KV-head arrays or the per-tensor pair
+  float k_scale_g = a.k_scale, v_scale_g = a.v_scale;
+  if constexpr (!kPTH) {
+    if (a.head_scales) {
+      k_scale_g = a.k_scales[g];
+      v_scale_g = a.v_scales[g];
+    }
+  }
+  const float qk_base = a.q_scale * a.sm_log2 * (kPTH ? 1.0f : k_scale_g);
   // Every wave derives the per-key factors of a resident tile into its own block;
   // v_ref (the running V scale maximum) moves here, tile by tile, identically in
   // every wave.
@@ -357,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
   // this lane's part of the row sum: p units (per-token-head mode) or P' units
   // (per-tensor mode, where P' = p / prob_scale for every key)
   float lam = 0.0f;
-  float vref = kPTH ? 0.0f : a.v_scale;  // v_ref the accumulator is expressed in
+  float vref = kPTH ? 0.0f : v_scale_g;  // v_ref the accumulator is expressed in
   // per-lane operand bases inside a stage
   // K operand: MFMA row `row` of key block kb is key tile_key(32 kb + row): page
   // 2 kb + (row / 4) % 2, token 4 (row / 8) + row % 4; dim step ks reads chunks
@@ -781,6 +790,7 @@ extern "C" kvq_status kvq_prefill_attention(const kvq_cache_desc* cache, const v
   args.k_scale = scales->k_scale;
   args.v_scale = scales->v_scale;
   args.prob_scale = scales->prob_scale;
+  args.head_scales = cache->mode == KVQ_SCALE_PER_KV_HEAD;
   const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)D);
   args.sm_log2 = sm * pf::kLog2e;
   args.causal = causal != 0;

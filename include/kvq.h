@@ -61,7 +61,12 @@ typedef enum {
   /* One K and one V scale for the whole layer (checkpoint value, else 1.0). */
   KVQ_SCALE_PER_TENSOR = 0,
   /* One scale per (token, KV head), computed at cache-store time as amax/448. */
-  KVQ_SCALE_PER_TOKEN_HEAD = 1
+  KVQ_SCALE_PER_TOKEN_HEAD = 1,
+  /* One K and one V scale per KV head for the whole layer: FA3-style scale arrays
+   * ("vLLM FP8 KV-Cache and Attention Quantization Update", section "Kernel and
+   * fusion optimizations": one scale per KV head).  Every row of head h is
+   * quantised and read with k_scales[h] / v_scales[h]. */
+  KVQ_SCALE_PER_KV_HEAD = 2
 } kvq_scale_mode;
 
 /* Resolved per-tensor scales (see kvq_resolve_scales).  All > 0. */
@@ -81,7 +86,10 @@ typedef struct {
  *                                    key rows of D codes, contiguous
  *     v_pages  uint8 [P][H][D][16]   dim-major: one (page, head) tile holds D rows
  *                                    of 16 codes (one row per channel)
- *     k_scales, v_scales  float [P][H][16]   per-token-head mode only (else NULL)
+ *     k_scales, v_scales  float [P][H][16]   per-token-head mode
+ *                         float [H]          per-KV-head mode: each > 0 and finite
+ *                                            (a precondition: device values are not
+ *                                            checked); NULL in per-tensor mode
  *   dtype KVQ_BF16 (sliding-window layers kept in bf16):
  *     k_pages  bf16  [P][H][16][D],  v_pages  bf16  [P][H][D][16]; no scales.
  *
@@ -97,8 +105,8 @@ typedef struct {
   int32_t head_dim;
   void* k_pages;       /* [device] */
   void* v_pages;       /* [device] */
-  float* k_scales;     /* [device] per-token-head only */
-  float* v_scales;     /* [device] per-token-head only */
+  float* k_scales;     /* [device] per-token-head and per-KV-head modes only */
+  float* v_scales;     /* [device] per-token-head and per-KV-head modes only */
 } kvq_cache_desc;
 
 /* ------------------------------------------------------------------------------
@@ -124,7 +132,10 @@ const char* kvq_last_error(void);
  *     KVQ_ERR_INVALID_ARG) and both become max(k, v);
  *     q > 0 -> q else 1.0; prob > 0 -> prob else 1.0 (the page shows the q rule;
  *     prob follows the same reading);
- *     *warn_flags gets KVQ_WARN_UNCALIBRATED_Q_OR_PROB when q or prob is 1.0.
+ *     *warn_flags gets KVQ_WARN_UNCALIBRATED_Q_OR_PROB when q or prob is 1.0;
+ *   per-KV-head: the per-tensor rules, applied to one head's (k, v) pair; resolve
+ *     each head with its own call and upload the k and v results as the cache's
+ *     scale arrays.
  * The platform rule that doubles K/V scales for the FNUZ fp8 variant is never
  * applied: gfx950 uses the OCP e4m3 format.
  * out [host], warn_flags [host] (may be NULL).
@@ -151,6 +162,7 @@ kvq_dtype kvq_layer_kv_dtype(int32_t window, uint32_t skip_flags);
  *
  * For every token t < num_tokens with slot_mapping[t] >= 0, and every KV head h:
  *   fp8 per-tensor:      s = k_scale (resp. v_scale), s > 0
+ *   fp8 per-KV-head:     s = cache->k_scales[h] (resp. v_scales[h])
  *   fp8 per-token-head:  s = fl32(amax / 448), amax = max_d |x[d]| (NaN
  *                        propagates); amax == 0 -> s = 1.0; s is stored in the
  *                        scale pool at (page, h, offset)
@@ -161,7 +173,7 @@ kvq_dtype kvq_layer_kv_dtype(int32_t window, uint32_t skip_flags);
  *   (token_stride in elements, >= H*D; 0 means H*D).
  * slot_mapping [device]: int64 [num_tokens]; negative = skip.  Preconditions:
  *   every non-negative slot < num_pages*16, no slot repeated within one call.
- * k_scale, v_scale: per-tensor fp8 scales (> 0); ignored otherwise.
+ * k_scale, v_scale: per-tensor fp8 scales (> 0); ignored in the other modes.
  * num_tokens == 0 is a no-op.
  */
 kvq_status kvq_cache_write(const kvq_cache_desc* cache, const void* k, const void* v,
@@ -199,11 +211,12 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t num_s
  *   fp8 cache:  q codes = e4m3_rne_saturating(fl32(q / q_scale)) (the fused query
  *               quantisation), score_j = (q_codes . k_codes_j) * q_scale *
  *               k_scale_j * softmax_scale, where k_scale_j is the per-token-head
- *               scale or scales->k_scale; V likewise with v_scale_j.
+ *               scale, cache->k_scales[g] (per-KV-head) or scales->k_scale
+ *               (per-tensor); V likewise with v_scale_j.
  *   bf16 cache: score_j = (q . k_j) * softmax_scale on the bf16 values.
  *   out[b][h] = sum_j softmax(score)_j * v_j;  L == 0 gives zeros.
  * Arithmetic: products are exact, sums and the online softmax are float32; the
- * probability weights p_j * v_scale_j enter the P.V dot products rounded to bf16;
+ * probability weights p_j * v_scale_j enter the P.V dot products rounded to f16;
  * partial results of each split are merged in float32 (the pages' two-level
  * accumulation: level 1 inside a page, level 2 in the split's fp32 registers,
  * level 3 across splits, done by the last split of each (sequence, KV head) to
@@ -214,7 +227,8 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t num_s
  * block_table [device] int32 [num_seqs][block_table_stride]: physical page of each
  *   logical page.  seq_lens [device] int32 [num_seqs].
  * Preconditions: 0 <= seq_lens[b] <= max_seq_len; entries used are < num_pages.
- * scales [host]: per-tensor values (q_scale and, in per-tensor mode, k/v scales).
+ * scales [host]: per-tensor values (q_scale and, in per-tensor mode, k/v scales;
+ *   the per-KV-head mode takes k/v from the cache's scale arrays).
  * window: 0 = full attention, > 0 = the last `window` keys.
  * softmax_scale: 0 selects 1/sqrt(D).
  * pages_per_split: 0 = library choice; must match kvq_decode_workspace_bytes.
@@ -239,7 +253,8 @@ kvq_status kvq_decode_attention(const kvq_cache_desc* cache, const void* q,
  * > 0 and every KV head h, the row k_new[b][h] / v_new[b][h] is stored at position
  * L - 1, i.e. at slot block_table[b][(L-1)/16] * 16 + (L-1) % 16, exactly as
  * kvq_cache_write would store it (same quantisation and scales: per-tensor
- * scales->k_scale / v_scale, or per-token-head amax / 448), and attention then runs
+ * scales->k_scale / v_scale, per-KV-head arrays, or per-token-head amax / 448),
+ * and attention then runs
  * over positions [lo, L) as in kvq_decode_attention, reading the new row.  Results
  * (cache contents and output) equal kvq_cache_write followed by kvq_decode_attention
  * ("Kernel and fusion optimizations" of "vLLM FP8 KV-Cache and Attention
@@ -268,7 +283,9 @@ kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const voi
  * and, with causal != 0, sees keys 0 .. L - n_b + i (window > 0: only keys
  * > L - n_b + i - window).
  *   S = (q codes . k codes) on FP8 matrix cores, scaled by q_scale * k_scale_j *
- *   softmax_scale; online softmax in float32; probabilities quantised to e4m3 with
+ *   softmax_scale (k_scale_j: per-token-head scale, cache->k_scales[g] per-KV-head,
+ *   or scales->k_scale per-tensor; V alike); online softmax in float32;
+ *   probabilities quantised to e4m3 with
  *   prob_scale (per-token V scales folded in before rounding) and P.V on FP8
  *   matrix cores into a fresh float32 accumulator per key tile, added into the
  *   running float32 output (two-level accumulation).

@@ -9,6 +9,9 @@ Sources.
     checkpoint, else 1.0); per-token-head mode computes a separate scale for every
     (token, head) in the kernel at the moment the cache is stored, needing no
     checkpoint scale.
+  * "vLLM FP8 KV-Cache and Attention Quantization Update", section "Kernel and
+    fusion optimizations": scale arrays with one scale per KV head (per-KV-head
+    mode: per-tensor quantisation with the head's own scale).
   * The per-token-head scale is amax / 448 and the code is
     clamp(round_rne(v / scale), +-448).
   * Pages and block tables: "vLLM Qwen3.8-Flash-Next: FP8 support for the QSA
@@ -72,11 +75,14 @@ def quantize_rows(x, mode: str, tensor_scale: float = 1.0):
     """Quantise rows of D values.  Returns (codes uint8 [..., D], scales float32 [...]).
 
     mode "per_tensor": every row uses ``tensor_scale``.
+    mode "per_kv_head": ``x`` is [..., Hkv, D]; rows of head h use tensor_scale[h].
     mode "per_token_head": every row uses its own amax / 448.
     """
     x = np.asarray(x, dtype=np.float32)
     if mode == "per_tensor":
         s = np.full(x.shape[:-1], tensor_scale, dtype=np.float32)
+    elif mode == "per_kv_head":
+        s = np.broadcast_to(np.asarray(tensor_scale, np.float32), x.shape[:-1]).copy()
     elif mode == "per_token_head":
         s = per_token_head_scale(x)
     else:
@@ -95,12 +101,13 @@ def new_pools(num_pages: int, num_kv_heads: int, head_dim: int):
     }
 
 
-def cache_write(pools, k, v, slot_mapping, mode: str, k_scale: float = 1.0,
-                v_scale: float = 1.0) -> None:
+def cache_write(pools, k, v, slot_mapping, mode: str, k_scale=1.0, v_scale=1.0) -> None:
     """Quantise K/V rows of T tokens ([T][Hkv][D], float32 values of bf16) into pools.
 
     Token t goes to page slot_mapping[t] // 16, offset slot_mapping[t] % 16; tokens
-    whose slot is negative are skipped.
+    whose slot is negative are skipped.  k_scale / v_scale: a float (per_tensor) or
+    one float per KV head (per_kv_head); every stored row records its scale in the
+    pools' per-slot scales, so dequantisation reads the same way in every mode.
     """
     slots = np.asarray(slot_mapping, dtype=np.int64)
     keep = slots >= 0

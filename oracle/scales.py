@@ -21,7 +21,11 @@ Rules as the pages state them:
   * an fp8 cache used with q_scale == 1.0 or prob_scale == 1.0 raises a one-time
     "uncalibrated" warning;
   * the platform-specific doubling of K/V scales for the FNUZ fp8 variant is not
-    applied: the target's fp8 type is the OCP e4m3 format.
+    applied: the target's fp8 type is the OCP e4m3 format;
+  * per-KV-head scale arrays ("vLLM FP8 KV-Cache and Attention Quantization
+    Update", section "Kernel and fusion optimizations": one scale per KV head):
+    the pages give no loading rule; reading: each head's (k, v) pair follows the
+    per-tensor rules.
 
 Skip policy: a layer keeps a bf16 cache iff the sliding-window skip flag is set and
 the layer has a window (> 0); every other layer uses the fp8 cache.
@@ -52,8 +56,9 @@ def resolve(mode: str, k: float, v: float, q: float, prob: float):
     if mode == "per_token_head":
         # the page's early return: no per-tensor checks and no warning
         return Scales(1.0, 1.0, 1.0, 1.0), 0
-    if mode != "per_tensor":
+    if mode not in ("per_tensor", "per_kv_head"):
         raise ScaleError(mode)
+    # per_kv_head: the per-tensor rules for one KV head's (k, v) pair
     if k > 0.0 and v > 0.0:
         ks, vs = k, v
     elif k < 0.0 and v < 0.0:

@@ -41,8 +41,14 @@ def dev(x, dtype=None) -> torch.Tensor:
 def write_cache(kvq, case, dtype="fp8", mode="per_token_head", k_scale=1.0, v_scale=1.0,
                 rows=None, chunk=1 << 20):
     """Allocate a device cache for ``case`` and write every token (or ``rows``)
-    through kvq.cache_write, in chunks of tokens."""
-    c = kvq.PagedCache(case.num_pages, case.num_kv_heads, case.head_dim, dtype, mode)
+    through kvq.cache_write, in chunks of tokens.  per_kv_head: k_scale / v_scale are
+    the per-head arrays (the cache's scale arrays; the call's scalars are unused)."""
+    if mode == "per_kv_head":
+        c = kvq.PagedCache(case.num_pages, case.num_kv_heads, case.head_dim, dtype, mode,
+                           k_head_scales=k_scale, v_head_scales=v_scale)
+        k_scale = v_scale = 1.0
+    else:
+        c = kvq.PagedCache(case.num_pages, case.num_kv_heads, case.head_dim, dtype, mode)
     idx = np.arange(len(case.k)) if rows is None else np.asarray(rows)
     per_tok = case.num_kv_heads * case.head_dim
     step = max(1, chunk // per_tok)
@@ -59,7 +65,7 @@ def read_pools(c):
     v = c.v_pages.cpu().transpose(2, 3).contiguous()
     if c.dtype == "fp8":
         out = {"k_codes": k.numpy(), "v_codes": v.numpy()}
-        if c.k_scales is not None:
+        if c.k_scales is not None and c.mode == "per_token_head":
             out["k_scales"] = c.k_scales.cpu().numpy()
             out["v_scales"] = c.v_scales.cpu().numpy()
         return out

@@ -105,6 +105,28 @@ def test_cache_write_argument_checks():
     assert L.kvq_cache_write(ctypes.byref(pt), 16, 32, 0, 64, 1, -1.0, 1.0, None) == kvq.binding.ERR_INVALID_ARG
 
 
+def test_per_kv_head_mode():
+    """Per-KV-head caches need their scale arrays; resolution follows the per-tensor
+    rules for one head's (k, v) pair."""
+    L = _lib()
+    d = _desc(mode=kvq.PER_KV_HEAD, k_scales=None, v_scales=None)
+    assert L.kvq_cache_write(ctypes.byref(d), 16, 32, 0, 64, 1, 1.0, 1.0, None) == kvq.binding.ERR_INVALID_ARG
+    d = _desc(mode=kvq.PER_KV_HEAD, k_scales=258, v_scales=512)     # misaligned array
+    assert L.kvq_cache_write(ctypes.byref(d), 16, 32, 0, 64, 1, 1.0, 1.0, None) == kvq.binding.ERR_INVALID_ARG
+    d = _desc(mode=kvq.PER_KV_HEAD)
+    assert L.kvq_cache_write(ctypes.byref(d), 16, 32, 0, 64, 0, 1.0, 1.0, None) == kvq.binding.OK
+    # the call's per-tensor scalars are not used in this mode: 0 is no error here
+    assert L.kvq_cache_write(ctypes.byref(d), 16, 32, 0, 64, 0, 0.0, 0.0, None) == kvq.binding.OK
+    for raw in [(-1.0, -1.0, -1.0, -1.0), (0.5, 0.25, 2.0, 0.125), (0.3, -1.0, -1.0, 4.0)]:
+        got, warn = kvq.resolve_scales("per_kv_head", *raw)
+        want, wwarn = oscales.resolve("per_kv_head", *raw)
+        # the library holds float32 values
+        assert got.as_tuple() == tuple(float(np.float32(x)) for x in (
+            want.q_scale, want.k_scale, want.v_scale, want.prob_scale))
+        assert warn == wwarn
+        assert got.as_tuple() == kvq.resolve_scales("per_tensor", *raw)[0].as_tuple()
+
+
 def test_decode_workspace_and_checks():
     d = _desc()
     L = _lib()

@@ -119,6 +119,44 @@ def test_cache_write_scatter_and_skip():
         assert np.array_equal(pools["v_codes"][page, :, off], codes)
 
 
+def test_per_kv_head_lossless_on_scaled_grid():
+    """Per-KV-head scale arrays ("vLLM FP8 KV-Cache and Attention Quantization
+    Update", section "Kernel and fusion optimizations"): rows of head h that are
+    e4m3 grid values times s_h (powers of two, so the products are exact) come back
+    unchanged, each head at its own scale, and the codes equal the grid's codes."""
+    table = e4m3.decode_table()
+    grid = table[~np.isnan(table)].astype(np.float32)[::3]        # 84 values
+    s = np.array([0.25, 2.0, 0.0078125], np.float32)
+    x = grid[None, None, :] * s[None, :, None]                     # [1][3][84]
+    codes, scales = cache.quantize_rows(x, "per_kv_head", s)
+    assert np.array_equal(scales[0], s)
+    assert np.array_equal(codes[0], np.broadcast_to(e4m3.encode(grid), (3, grid.size)))
+    assert np.array_equal(cache.dequantize(codes, scales[..., None]), x.astype(np.float64))
+
+
+def test_per_kv_head_is_per_tensor_per_head():
+    """Head h of a per-KV-head write equals a per-tensor write of that head alone at
+    s_h; with every s_h equal the whole write equals the per-tensor one."""
+    case = workloads.make_decode_case(9, [40, 3], 8, 4, 64, table="perm")
+    s = np.array([0.5, 0.03, 1.0, 0.125], np.float32)
+    pools = cache.new_pools(case.num_pages, 4, 64)
+    cache.cache_write(pools, case.k, case.v, case.slots, "per_kv_head", s, s * 2)
+    page, off = case.slots // 16, case.slots % 16
+    for h in range(4):
+        codes, _ = cache.quantize_rows(case.k[:, h], "per_tensor", float(s[h]))
+        assert np.array_equal(pools["k_codes"][page, h, off], codes)
+        codes, _ = cache.quantize_rows(case.v[:, h], "per_tensor", float(2 * s[h]))
+        assert np.array_equal(pools["v_codes"][page, h, off], codes)
+        assert np.all(pools["k_scales"][page, h, off] == s[h])
+    same = cache.new_pools(case.num_pages, 4, 64)
+    cache.cache_write(same, case.k, case.v, case.slots, "per_kv_head",
+                      np.full(4, 0.2, np.float32), np.full(4, 0.3, np.float32))
+    ref = cache.new_pools(case.num_pages, 4, 64)
+    cache.cache_write(ref, case.k, case.v, case.slots, "per_tensor", 0.2, 0.3)
+    for name in ("k_codes", "v_codes"):
+        assert np.array_equal(same[name], ref[name])
+
+
 def test_quantize_q():
     q = np.array([[0.3, -2.0, 500.0]], np.float32)
     codes, qh = cache.quantize_q(q, 0.5)
