@@ -40,6 +40,7 @@ DECODE_KERNEL = "decode_kernel"
 COPY_BYTES = 1 << 30
 SETTLE_S = 0.1               # untimed steps after the warmup, before each timed region
 LEGS = ("decode", "bf16", "tiny", "long", "hybrid", "prefill")
+EXTRA_LEGS = ("prefill_d128", "prefill_d64", "per_kv_head")  # on request (--legs)
 
 
 def parse():
@@ -399,8 +400,8 @@ def main():
         sys.exit(2)
     legs = [x for x in args.legs.split(",") if x]
     for x in legs:
-        if x not in LEGS:
-            sys.exit(f"unknown leg {x!r}; choose from {LEGS}")
+        if x not in LEGS + EXTRA_LEGS:
+            sys.exit(f"unknown leg {x!r}; choose from {LEGS + EXTRA_LEGS}")
     import numpy as np
     import torch
 
@@ -701,6 +702,84 @@ def main():
                          "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
                          "kernel": "prefill_kernel"}}
         del c
+        torch.cuda.empty_cache()
+
+    for leg, (Hq_, Hkv_, D_) in (("prefill_d128", (32, 8, 128)), ("prefill_d64", (64, 8, 64))):
+        if leg not in legs:
+            continue
+        # Llama-3.1-8B- / gpt-oss-20b-shaped chunked prefill: 8,192 new queries on a
+        # 32,768-token fp8 cache (per-token-head scales), causal
+        pc = workloads.make_prefill_case(106, [32768], [8192], Hq_, Hkv_, D_,
+                                         table="identity", name=leg)
+        log(f"bench: {leg} workload generated")
+        c = kvq.PagedCache(pc.num_pages, pc.num_kv_heads, pc.head_dim, "fp8", "per_token_head")
+        for t0 in range(0, len(pc.k), 16384):
+            sl_ = slice(t0, t0 + 16384)
+            kvq.cache_write(c, to_dev(pc.k[sl_]), to_dev(pc.v[sl_]),
+                            torch.from_numpy(pc.slots[sl_].astype(np.int64)).to(dev))
+        pq, pcu = to_dev(pc.q), torch.from_numpy(pc.cu_q_lens).to(dev)
+        pbt, psl = torch.from_numpy(pc.block_table).to(dev), torch.from_numpy(pc.seq_lens).to(dev)
+        n_new = int(pc.cu_q_lens[1])
+        out = torch.empty(pc.q.shape, dtype=torch.bfloat16, device=dev)
+        us = timer.run(lambda i: kvq.prefill_attention(c, pq, pcu, pbt, psl, n_new, ones,
+                                                       out=out), 10, 3)
+        fl = prefill_flops(int(pc.seq_lens[0]) - n_new, n_new, Hq_, D_)
+        tf = fl / (float(np.mean(us)) * 1e-6) / 1e12
+        result[leg] = {
+            "workload": f"head_dim-{D_} chunked prefill: 8,192 new on a 32,768-token fp8 "
+                        f"cache, {Hq_}/{Hkv_} heads, causal, per-token-head scales",
+            **stats(us), "flops": fl,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                         "kernel": "prefill_kernel"}}
+        del c, pc
+        torch.cuda.empty_cache()
+
+    if "per_kv_head" in legs:
+        # the Llama-shaped decode step with per-KV-head scale arrays instead of
+        # per-token-head scales (the same inputs; 8 random head scales per pool)
+        case2 = workloads.llama8b_decode()
+        last2 = case2.last_token_rows()
+        hist2 = np.setdiff1d(np.arange(len(case2.k)), last2)
+        hk = (0.004 * 2.0 ** np.random.default_rng(5).uniform(0, 5, 8)).astype(np.float32)
+        hv = (0.004 * 2.0 ** np.random.default_rng(6).uniform(0, 5, 8)).astype(np.float32)
+        cs = [kvq.PagedCache(case2.num_pages, 8, 128, "fp8", "per_kv_head",
+                             k_head_scales=hk, v_head_scales=hv) for _ in range(args.rotate)]
+        for i in range(0, len(hist2), 16384):
+            sel = hist2[i:i + 16384]
+            kk, vv = to_dev(case2.k[sel]), to_dev(case2.v[sel])
+            ss = torch.from_numpy(case2.slots[sel].astype(np.int64)).to(dev)
+            for c in cs:
+                kvq.cache_write(c, kk, vv, ss)
+        q2, kn2, vn2 = to_dev(case2.q), to_dev(case2.k[last2]), to_dev(case2.v[last2])
+        bt2, sl2 = (torch.from_numpy(case2.block_table).to(dev),
+                    torch.from_numpy(case2.seq_lens).to(dev))
+        L2 = int(case2.seq_lens[0])
+        ws2 = kvq.decode_workspace(cs[0], 8, 32, L2, 0, 0, dev)
+        out2 = torch.empty((8, 32, 128), dtype=torch.bfloat16, device=dev)
+
+        def pstep(i):
+            kvq.decode_step(cs[i % len(cs)], q2, kn2, vn2, bt2, sl2, L2, ones, out=out2,
+                            workspace=ws2)
+        for i in range(args.warmup):
+            pstep(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            pstep(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us2 = e0.elapsed_time(e1) * 1e3 / args.steps
+        nb2 = decode_bytes(8, L2, 8, 32, 128, 1, 0) + write_bytes(8, 8, 128, 1, 0)
+        result["per_kv_head_decode_step"] = {
+            "workload": "Llama-shaped decode step (8 x 20,000, 32/8 heads, D 128) with "
+                        "per-KV-head scale arrays",
+            "us_per_step": round(us2, 2), "bytes": nb2,
+            "GB_s": round(nb2 / (us2 * 1e-6) / 1e9, 1),
+            "frac_hbm": round(nb2 / (us2 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del cs
         torch.cuda.empty_cache()
 
     if args.copy_calib:

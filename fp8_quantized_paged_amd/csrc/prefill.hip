@@ -76,7 +76,7 @@ __device__ __forceinline__ int tile_key(int i) {
 }
 
 // Pipeline depth: tile t is in softmax/PV, t + 1 in QK, t + 2 and t + 3 in flight.
-constexpr int kStages = 4;
+constexpr int kStagesMax = 4;  // tile ring slots (head_dim 128: 3, see prefill_kernel)
 // Block-table entries are fetched into LDS by direct loads, kIdTiles tiles' worth at a
 // time, one chunk ahead of use.  (Reading them with vector loads inside the tile loop
 // would put them in the same in-order completion count as the tile loads and force
@@ -151,8 +151,18 @@ __device__ __forceinline__ T lds_read(const uint8_t* base, int byte_off) {
   return *reinterpret_cast<const T*>(base + byte_off);
 }
 
+// head_dim 128: two waves per SIMD (two workgroups per CU), so one wave's vector work
+// overlaps the other's matrix work; that needs <= 256 registers per lane (a few spill)
+// and a three-slot tile ring (62 KB of LDS per workgroup).  head_dim 128, 8,192 new
+// keys on 32,768: 6.15 -> 4.41 ms per-token-head, 4.53 -> 3.21 ms per-tensor.  head_dim
+// 256 cannot (its accumulators alone take 128 registers), head_dim 64 measured no gain.
+template <int D>
+constexpr int prefill_waves_per_simd() { return D == 128 ? 2 : 1; }
+
 template <int D, int G, bool kPTH>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    prefill_waves_per_simd<D>()))) void prefill_kernel(const PrefillArgs a) {
+  constexpr int kStages = prefill_waves_per_simd<D>() == 2 ? 3 : kStagesMax;
   using LY = Layout<D>;
   constexpr int NP = kWgRows / G;  // query positions per workgroup
   constexpr int KS = D / 64;       // 64-dim steps of the QK contraction
