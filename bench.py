@@ -40,7 +40,8 @@ DECODE_KERNEL = "decode_kernel"
 COPY_BYTES = 1 << 30
 SETTLE_S = 0.1               # untimed steps after the warmup, before each timed region
 LEGS = ("decode", "bf16", "tiny", "long", "hybrid", "prefill")
-EXTRA_LEGS = ("prefill_d128", "prefill_d64", "per_kv_head")  # on request (--legs)
+EXTRA_LEGS = ("prefill_d128", "prefill_d64", "per_kv_head", "prefill_bf16_window")
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix throughput, AMD published
 
 
 def parse():
@@ -732,6 +733,33 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
                          "kernel": "prefill_kernel"}}
+        del c, pc
+        torch.cuda.empty_cache()
+
+    if "prefill_bf16_window" in legs:
+        # gpt-oss-20b-shaped sliding-window layer prefill over its bf16 cache: 8,192 new
+        # queries on a 32,768-token context, 64/8 heads, D 64, window 128, causal
+        pc = workloads.make_prefill_case(107, [32768], [8192], 64, 8, 64, table="identity",
+                                         window=128, name="bf16 window prefill")
+        c = kvq.PagedCache(pc.num_pages, 8, 64, "bf16", "per_tensor")
+        for t0 in range(0, len(pc.k), 16384):
+            sl_ = slice(t0, t0 + 16384)
+            kvq.cache_write(c, to_dev(pc.k[sl_]), to_dev(pc.v[sl_]),
+                            torch.from_numpy(pc.slots[sl_].astype(np.int64)).to(dev))
+        pq, pcu = to_dev(pc.q), torch.from_numpy(pc.cu_q_lens).to(dev)
+        pbt, psl = torch.from_numpy(pc.block_table).to(dev), torch.from_numpy(pc.seq_lens).to(dev)
+        out = torch.empty(pc.q.shape, dtype=torch.bfloat16, device=dev)
+        us = timer.run(lambda i: kvq.prefill_attention(c, pq, pcu, pbt, psl, 8192, ones,
+                                                       window=128, out=out), 10, 3)
+        fl = 4.0 * 64 * 64 * 8192 * 128      # every query sees 128 keys
+        tf = fl / (float(np.mean(us)) * 1e-6) / 1e12
+        result["prefill_bf16_window"] = {
+            "workload": "gpt-oss-20b-shaped window-128 layer prefill over its bf16 cache: "
+                        "8,192 new on 32,768 ctx, 64/8 heads, D 64",
+            **stats(us), "flops": fl,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         "kernel": "prefill_bf16_kernel"}}
         del c, pc
         torch.cuda.empty_cache()
 

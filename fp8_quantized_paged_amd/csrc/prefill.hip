@@ -40,6 +40,7 @@
 // of up to 640 chunks), so the running output lives in true float32 registers.
 #include "kvq_device.h"
 #include "kvq_host.h"
+#include "prefill_bf16.h"
 
 namespace kvq {
 namespace pf {
@@ -758,8 +759,6 @@ extern "C" kvq_status kvq_prefill_attention(const kvq_cache_desc* cache, const v
                                             void* out, kvq_dtype out_dtype, void* stream) {
   clear_error();
   if (kvq_status s = check_cache(cache)) return s;
-  if (cache->dtype != KVQ_FP8_E4M3)
-    return fail(KVQ_ERR_UNSUPPORTED, "prefill reads an fp8 cache (bf16 cache prefill is not built)");
   if (num_seqs < 0 || num_q_heads <= 0 || max_q_len < 0 || window < 0)
     return fail(KVQ_ERR_INVALID_ARG, "num_seqs %d num_q_heads %d max_q_len %d window %d",
                 num_seqs, num_q_heads, max_q_len, window);
@@ -777,6 +776,33 @@ extern "C" kvq_status kvq_prefill_attention(const kvq_cache_desc* cache, const v
   if (((uintptr_t)q | (uintptr_t)out) & 15u)
     return fail(KVQ_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
   if (block_table_stride <= 0) return fail(KVQ_ERR_INVALID_ARG, "block_table_stride <= 0");
+  if (cache->dtype == KVQ_BF16) {  // the skip path's bf16 cache: prefill_bf16.hip
+    if (!(softmax_scale >= 0.0f)) return fail(KVQ_ERR_INVALID_ARG, "softmax_scale < 0");
+    const int Db = cache->head_dim;
+    PrefillBf16Args ba;
+    ba.q = static_cast<const uint16_t*>(q);
+    ba.cu_q_lens = cu_q_lens;
+    ba.seq_lens = seq_lens;
+    ba.block_table = block_table;
+    ba.bt_stride = block_table_stride;
+    ba.k_pages = static_cast<const uint16_t*>(cache->k_pages);
+    ba.v_pages = static_cast<const uint16_t*>(cache->v_pages);
+    ba.num_kv_heads = cache->num_kv_heads;
+    ba.num_q_heads = num_q_heads;
+    ba.tiles = (max_q_len + 127) / 128;
+    ba.causal = causal != 0;
+    ba.window = window;
+    const float smb = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)Db);
+    ba.sm_log2 = smb * pf::kLog2e;
+    ba.out = out;
+    ba.out_f32 = out_dtype == KVQ_F32;
+    const int64_t bblocks = (int64_t)num_seqs * num_q_heads * ba.tiles;
+    if (bblocks > 0x7FFFFFFF) return fail(KVQ_ERR_INVALID_ARG, "grid too large");
+    launch_prefill_bf16(ba, Db, bblocks, static_cast<hipStream_t>(stream));
+    const hipError_t be = hipGetLastError();
+    if (be != hipSuccess) return fail(KVQ_ERR_HIP, "prefill launch: %s", hipGetErrorString(be));
+    return KVQ_OK;
+  }
   if (!scales) return fail(KVQ_ERR_INVALID_ARG, "scales is NULL");
   if (!(scales->q_scale > 0.0f) || !(scales->prob_scale > 0.0f) ||
       (cache->mode == KVQ_SCALE_PER_TENSOR && !(scales->k_scale > 0.0f && scales->v_scale > 0.0f)))

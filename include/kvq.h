@@ -292,7 +292,11 @@ kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const voi
  * q [device] bf16 [total_q][num_q_heads][D]; out [device] [total_q][num_q_heads][D].
  * cu_q_lens [device] int32 [num_seqs+1]; seq_lens [device] int32 [num_seqs];
  * block_table as for decode.  max_q_len >= every n_b.
- * Supported: fp8 cache, D in {64,128,256}, group size in {1,2,4,8,16}.
+ * bf16 cache (the sliding-window layers' skip path, "Hybrid attention and layer
+ *   skipping"): S = q . k on the bf16 values (bf16 matrix cores, exact products,
+ *   float32 sums) scaled by softmax_scale, float32 online softmax, weights rounded to
+ *   bf16 for P.V and normalised by the sum of the rounded weights; scales unused.
+ * Supported: fp8 or bf16 cache, D in {64,128,256}, group size in {1,2,4,8,16}.
  */
 kvq_status kvq_prefill_attention(const kvq_cache_desc* cache, const void* q,
                                  const int32_t* cu_q_lens, int32_t num_seqs,

@@ -164,3 +164,31 @@ def test_hd256_prefill_sampled(kvq):
     want = oracle_prefill(case, "per_token_head", rows=rows)
     assert np.isfinite(got).all()
     assert_close_to_oracle(got[rows], want[rows], "hd256 prefill sampled rows")
+
+
+# bf16 weights in P . V: relative rounding error <= 2^-9, renormalised
+P_ROUND_BF16 = 2.0 ** -9 / (1.0 - 2.0 ** -9)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(64, 64, 8), (128, 16, 2), (256, 8, 4)])
+@pytest.mark.parametrize("window", [0, 128])
+def test_prefill_bf16_cache(kvq, D, Hq, Hkv, window):
+    """Sliding-window layers keep a bf16 cache ("Hybrid attention and layer
+    skipping"): prefill over the raw bf16 values, causal, with and without a window."""
+    ctx, new = [0, 37, 300, 1000], [70, 1, 150, 200]
+    case = workloads.make_prefill_case(260 + D + window, ctx, new, Hq, Hkv, D,
+                                       table="perm", extra_pages=3)
+    log(f"prefill bf16 cache D={D} Hq={Hq} Hkv={Hkv} window={window}")
+    c = write_cache(kvq, case, "bf16")
+    got = run_prefill(kvq, c, case, window=window)
+    kp = np.zeros((case.num_pages, Hkv, 16, D))
+    vp = np.zeros_like(kp)
+    page, off = case.slots // 16, case.slots % 16
+    kp[page, :, off] = case.k
+    vp[page, :, off] = case.v
+    want, spread = attention.prefill(case.q.astype(np.float64), case.cu_q_lens, kp, vp,
+                                     case.block_table, case.seq_lens, True, window,
+                                     spread=True)
+    err = np.abs(got - want)
+    bound = ATOL + RTOL * np.abs(want) + P_ROUND_BF16 * spread
+    assert (err <= bound).all(), f"max excess {np.max(err - bound):.3g}"
