@@ -152,18 +152,24 @@ __device__ __forceinline__ T lds_read(const uint8_t* base, int byte_off) {
   return *reinterpret_cast<const T*>(base + byte_off);
 }
 
-// head_dim 128: two waves per SIMD (two workgroups per CU), so one wave's vector work
-// overlaps the other's matrix work; that needs <= 256 registers per lane (a few spill)
-// and a three-slot tile ring (62 KB of LDS per workgroup).  head_dim 128, 8,192 new
-// keys on 32,768: 6.15 -> 4.41 ms per-token-head, 4.53 -> 3.21 ms per-tensor.  head_dim
-// 256 cannot (its accumulators alone take 128 registers), head_dim 64 measured no gain.
-template <int D>
-constexpr int prefill_waves_per_simd() { return D == 128 ? 2 : 1; }
+// Two waves per SIMD (two workgroups per CU), so one wave's vector work overlaps the
+// other's matrix work, where it fits: <= 256 registers per lane and <= 80 KB of LDS
+// per workgroup.  head_dim 128 takes a three-slot tile ring (62 KB) and reads the
+// per-key factors from LDS where they are used instead of queueing them in registers
+// beside the operands (a few registers still spill); head_dim 64 per-token-head needs
+// the late factor reads to fit.  8,192 new keys on 32,768: head_dim 128 6.15 -> 4.02 ms
+// per-token-head, 4.53 -> 3.06 ms per-tensor; head_dim 64 per-token-head 13.3 -> 7.5
+// ms.  head_dim 256 cannot (its accumulators alone take 128 registers); head_dim 64
+// per-tensor measured 2% slower at two waves.
+template <int D, bool kPTH>
+constexpr int prefill_waves_per_simd() { return D == 128 || (D == 64 && kPTH) ? 2 : 1; }
 
 template <int D, int G, bool kPTH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
-    prefill_waves_per_simd<D>()))) void prefill_kernel(const PrefillArgs a) {
-  constexpr int kStages = prefill_waves_per_simd<D>() == 2 ? 3 : kStagesMax;
+    prefill_waves_per_simd<D, kPTH>()))) void prefill_kernel(const PrefillArgs a) {
+  constexpr bool kTwoWaves = prefill_waves_per_simd<D, kPTH>() == 2;
+  constexpr int kStages = kTwoWaves && D == 128 ? 3 : kStagesMax;
+  constexpr bool kLateFactors = kTwoWaves;  // factors read at their use, not queued
   using LY = Layout<D>;
   constexpr int NP = kWgRows / G;  // query positions per workgroup
   constexpr int KS = D / 64;       // 64-dim steps of the QK contraction
@@ -536,15 +542,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       auto load_chunk = [&](int c, Chunk& q) {
         if (c < NQK) {
           q.op = k_operand(c);
+          if constexpr (!kLateFactors) {
 #pragma unroll
-          for (int u = 0; u < WQ; ++u) q.f[u] = factor(buf, LY::FV_OFF, WQ * c + u, pmul);
+            for (int u = 0; u < WQ; ++u) q.f[u] = factor(buf, LY::FV_OFF, WQ * c + u, pmul);
+          }
         } else {
           const int db = c - NQK;
           q.op = v_operand(db);
+          if constexpr (!kLateFactors) {
 #pragma unroll
-          for (int u = 0; u < WV; ++u) {
-            q.f[u] = factor(buf, LY::IF_OFF, WV * db + u, 1.0f);
-            q.f2[u] = factor(nbuf, LY::CF_OFF, WV * db + u, qk_base);
+            for (int u = 0; u < WV; ++u) {
+              q.f[u] = factor(buf, LY::IF_OFF, WV * db + u, 1.0f);
+              q.f2[u] = factor(nbuf, LY::CF_OFF, WV * db + u, qk_base);
+            }
           }
         }
       };
@@ -621,7 +631,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
           for (int u = 0; u < WQ; ++u) {
             const int w = WQ * c + u;
-            const float f[4] = {cur.f[u].x, cur.f[u].y, cur.f[u].z, cur.f[u].w};
+            const float4 fu = kLateFactors ? factor(buf, LY::FV_OFF, w, pmul) : cur.f[u];
+            const float f[4] = {fu.x, fu.y, fu.z, fu.w};
             float pq[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -646,13 +657,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
           for (int u = 0; u < WV; ++u) {
             const int w = WV * db + u;
+            const float4 fi = kLateFactors ? factor(buf, LY::IF_OFF, w, 1.0f) : cur.f[u];
+            const float4 fc = kLateFactors ? factor(nbuf, LY::CF_OFF, w, qk_base) : cur.f2[u];
             if constexpr (kPTH) {
               const float2_t d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], false);
               const float2_t d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], true);
-              lam = fmaf(d01.x, cur.f[u].x, lam);
-              lam = fmaf(d01.y, cur.f[u].y, lam);
-              lam = fmaf(d23.x, cur.f[u].z, lam);
-              lam = fmaf(d23.y, cur.f[u].w, lam);
+              lam = fmaf(d01.x, fi.x, lam);
+              lam = fmaf(d01.y, fi.y, lam);
+              lam = fmaf(d23.x, fi.z, lam);
+              lam = fmaf(d23.y, fi.w, lam);
             } else {
               const half2_t h01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw[w], 1.0f, false);
               const half2_t h23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw[w], 1.0f, true);
@@ -660,7 +673,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
               lam = __builtin_amdgcn_fdot2(h01, one, lam, false);
               lam = __builtin_amdgcn_fdot2(h23, one, lam, false);
             }
-            const float cc[4] = {cur.f2[u].x, cur.f2[u].y, cur.f2[u].z, cur.f2[u].w};
+            const float cc[4] = {fc.x, fc.y, fc.z, fc.w};
             const int kb = w / 4, q4 = w % 4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[4 * w + e] = fmaf(sn[kb][4 * q4 + e], cc[e], -msafe);
