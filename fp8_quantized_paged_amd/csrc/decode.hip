@@ -538,8 +538,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       }
       if (__builtin_amdgcn_ballot_w64(over && hvalid) != 0) {
         float pm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        pm = fmaxf(pm, __shfl_xor(pm, 16));
-        pm = fmaxf(pm, __shfl_xor(pm, 32));
+        pm = max_xor<32>(max_xor<16>(pm));
         const float mn = fmaxf(m_h, pm);
         const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_h - mn);
         m_h = mn;
@@ -547,8 +546,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         float beta = alpha;
         if constexpr (kPTH) {
           float pv = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-          pv = fmaxf(pv, __shfl_xor(pv, 16));
-          pv = fmaxf(pv, __shfl_xor(pv, 32));
+          pv = max_xor<32>(max_xor<16>(pv));
           const float mvn = fmaxf(mv_h, pv);
           beta = mvn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mv_h - mvn);
           mv_h = mvn;
@@ -620,8 +618,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     }
 
     // ---- per-head state to wave-uniform values; output to the channel layout ------
-    float lt = l_part + __shfl_xor(l_part, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = sum_xor<32>(sum_xor<16>(l_part));
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       m_all[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(

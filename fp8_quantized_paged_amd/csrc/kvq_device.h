@@ -119,14 +119,59 @@ __device__ __forceinline__ float dpp_partner(float x) {
   else return dpp_mov<kDppMirror>(x);
 }
 
+// The values of lanes i and i ^ kSpan (kSpan 16 or 32), in some order, in every lane
+// i: v_permlane16_swap / v_permlane32_swap of x with itself.  Whichever halves the
+// instruction exchanges, one result holds x of lane i and the other x of its partner.
+template <int kSpan>
+__device__ __forceinline__ void lane_swap_pair(float x, float& a, float& b) {
+  const uint32_t u = __float_as_uint(x);
+  if constexpr (kSpan == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    static_assert(kSpan == 32, "span");
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+
+// max(x of lane i, x of lane i ^ kSpan) / the sum of the two, in every lane
+template <int kSpan = 32>
+__device__ __forceinline__ float max_xor(float x) {
+  float a, b;
+  lane_swap_pair<kSpan>(x, a, b);
+  return fmaxf(a, b);
+}
+template <int kSpan = 32>
+__device__ __forceinline__ float sum_xor(float x) {
+  float a, b;
+  lane_swap_pair<kSpan>(x, a, b);
+  return a + b;
+}
+
+// Maximum / sum over the 64 lanes, in every lane, all on the vector ALU (no LDS
+// round trips): a butterfly over the four lane bits of a 16-lane row by DPP, then
+// across rows by the two lane swaps.  Every lane of the wave must be active.
 __device__ __forceinline__ float wave_max(float x) {
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = fmaxf(x, dpp_partner<0>(x));
+  x = fmaxf(x, dpp_partner<1>(x));
+  x = fmaxf(x, dpp_partner<2>(x));
+  x = fmaxf(x, dpp_partner<3>(x));
+  float a, b;
+  lane_swap_pair<16>(x, a, b);
+  return max_xor<32>(fmaxf(a, b));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x += dpp_partner<0>(x);
+  x += dpp_partner<1>(x);
+  x += dpp_partner<2>(x);
+  x += dpp_partner<3>(x);
+  float a, b;
+  lane_swap_pair<16>(x, a, b);
+  return sum_xor<32>(a + b);
 }
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }

@@ -589,7 +589,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       }
       const bool first = m == -INFINITY;
       if (__builtin_amdgcn_ballot_w64(mx > (first ? -INFINITY : kSlack)) != 0) {
-        const float rmax = fmaxf(mx, __shfl_xor(mx, kRows));  // whole row, relative
+        const float rmax = max_xor<kRows>(mx);  // whole row, relative
         const float delta = first ? (rmax == -INFINITY ? 0.0f : rmax) : fmaxf(0.0f, rmax);
         if (!first) {
           const float alpha = __builtin_amdgcn_exp2f(-delta);
@@ -715,7 +715,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // O = sum_j P'_j v_code_j with P'_j ~ p_j v_scale_j / (v_ref prob_scale) and lam ~
   // sum_j p_j: out = O * v_ref * prob_scale / lam; per-tensor: P'_j ~ p_j / prob_scale
   // and lam ~ sum_j P'_j, out = O * v_scale / lam
-  const float lsum = lam + __shfl_xor(lam, kRows);
+  const float lsum = sum_xor<kRows>(lam);
   const float inv = lsum > 0.0f ? vref * (kPTH ? a.prob_scale : 1.0f) / lsum : 0.0f;
   if (row_ok) {
     const int64_t orow = ((int64_t)(q0 + p_loc) * Hq + g * G + hh) * D;

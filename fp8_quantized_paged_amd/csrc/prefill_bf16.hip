@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillBf1
       x[r] = vis ? s[r] * a.sm_log2 : -INFINITY;
       mx = fmaxf(mx, x[r]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor<32>(mx);
     const float mn = fmaxf(m, mx);
     const float msafe = mn == -INFINITY ? 0.0f : mn;  // nothing visible yet: all zero
     const float alpha = __builtin_amdgcn_exp2f(m - msafe);  // m = -inf -> 0
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillBf1
 
   // ---- normalise and store: register r of block db holds channel
   // 32 db + 8 (r / 4) + 4 hg + r % 4 of query `col`
-  const float lsum = l + __shfl_xor(l, 32);
+  const float lsum = sum_xor<32>(l);
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
   if (row_ok) {
     const int64_t orow = ((int64_t)(q0 + p) * a.num_q_heads + h) * D;
