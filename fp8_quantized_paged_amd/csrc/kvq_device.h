@@ -164,6 +164,19 @@ __device__ __forceinline__ float wave_max(float x) {
   return max_xor<32>(fmaxf(a, b));
 }
 
+// Maximum over the 64 lanes of unsigned values (also the maximum of non-negative
+// floats by their bits), in every lane.  Every lane of the wave must be active.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_mov_u<kDppXor1>(x));
+  x = max(x, dpp_mov_u<kDppXor2>(x));
+  x = max(x, dpp_mov_u<kDppHalfMirror>(x));
+  x = max(x, dpp_mov_u<kDppMirror>(x));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max((uint32_t)r16[0], (uint32_t)r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max((uint32_t)r32[0], (uint32_t)r32[1]);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
   x += dpp_partner<0>(x);
   x += dpp_partner<1>(x);

@@ -99,7 +99,7 @@ static_assert(kIdTiles * kTilePages == kThreads, "one page id per thread per chu
 //   KS, VS: the 64 keys' K and V scales (per-token-head mode).
 //   CF, FV, IF (one copy per wave): per-key factors derived from KS/VS: score
 //       multiplier k_scale * q_scale * softmax_scale * log2(e), P' factor v_scale /
-//       (v_ref * prob_scale) and its reciprocal; VREF: v_ref after this tile.
+//       (v_ref * prob_scale) and its reciprocal.
 template <int D>
 struct Layout {
   static constexpr int NC = D / 16;            // 16-byte chunks per key row
@@ -116,8 +116,7 @@ struct Layout {
   static constexpr int CF_OFF = 0;
   static constexpr int FV_OFF = CF_OFF + kTile * 4;
   static constexpr int IF_OFF = FV_OFF + kTile * 4;
-  static constexpr int VREF_OFF = IF_OFF + kTile * 4;
-  static constexpr int FSZ = VREF_OFF + 16;
+  static constexpr int FSZ = IF_OFF + kTile * 4;
   static constexpr int BYTES = FAC_OFF + kWaves * FSZ;
   // load instructions per page for K and for V (64 chunks each), and per wave per
   // tile for each
@@ -323,7 +322,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const int fac = LY::FAC_OFF + wave * LY::FSZ;
   auto derive_finish = [&](uint8_t* st, float ks, float vs) {
     if constexpr (kPTH) {
-      vref_run = fmaxf(vref_run, wave_max(vs));
+      // V scales are >= 0 (unwritten slots were scrubbed to 0): compare bits
+      vref_run = __uint_as_float(
+          max(__float_as_uint(vref_run), wave_max_u32(__float_as_uint(vs))));
       // P' factor and its reciprocal (hardware reciprocals: any f works as long as
       // the row sum maps P' back with the same f, up to rounding)
       const float f = vref_run > 0.0f ? vs * __builtin_amdgcn_rcpf(vref_run * a.prob_scale)
@@ -332,7 +333,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       reinterpret_cast<float*>(fb + LY::CF_OFF)[lane] = ks * qk_base;
       reinterpret_cast<float*>(fb + LY::FV_OFF)[lane] = f;
       reinterpret_cast<float*>(fb + LY::IF_OFF)[lane] = f > 0.0f ? __builtin_amdgcn_rcpf(f) : 0.0f;
-      if (lane == 0) reinterpret_cast<float*>(fb + LY::VREF_OFF)[0] = vref_run;
     }
   };
   auto derive_tile = [&](uint8_t* st) {
@@ -497,12 +497,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       qk(lds[0], sc);
 #pragma unroll
       for (int w = 0; w < 8; ++w) scale_group(w, lds[0], sc, 0.0f, x);
-      mx = mask_max(t_first, x);
     }
     for (int t = t_first; t <= t_last; ++t) {
       const int rel = t - t_first;
       const uint8_t* buf = lds[rel % kStages];
       const uint8_t* nbuf = lds[(rel + 1) % kStages];  // past the last tile: unused
+      const float vr = vref_run;  // v_ref after tile t (before tile t + 1 is derived)
       // ---- operand queue: chunk c < NQK is S^T MFMA c (K operand of tile t + 1, P'
       // factors of tile t), chunk NQK + db is P.V MFMA db (V operand of tile t,
       // row-sum factors of tile t, score factors of tile t + 1).  Operands are read QD
@@ -577,11 +577,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       // on, so that they overlap the matrix and vector work
       const int4 ld_ids = tile_ids(t + kStages - 1);
       const int ld_slot = (rel + kStages - 1) % kStages;
+      // masks and row maxima of tile t's scores (vector work that covers the latency
+      // of the operand reads above)
+      mx = mask_max(t, x);
 
       // ---- rescale when v_ref grew or a score passed the reference by the slack ----
       float fo = 1.0f;  // factor for o
       if constexpr (kPTH) {
-        const float vr = lds_read<float>(buf, fac + LY::VREF_OFF);
         if (vr > vref) {
           fo = vref > 0.0f ? vref / vr : 0.0f;
           vref = vr;
@@ -682,7 +684,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      mx = mask_max(t + 1, x);
 
       // ---- tile t + 2 resident (issued two iterations ago): wait, scrub its unwritten
       // slots.  One barrier per tile: it publishes every wave's
