@@ -63,6 +63,51 @@ __device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// d[e] = p[e] * (f of lane r0 + e of this lane's 16-lane row), e = 0..3: v_mul_f32 with
+// the DPP row_newbcast source operand, so the broadcast costs no instruction.  The
+// leading s_nop covers the two wait states a DPP read needs after a vector write of
+// its source register.
+__device__ __forceinline__ void mul4_row_bcast(float (&d)[4], float f, int r0,
+                                               const float (&p)[4]) {
+#define KVQ_MUL4(R0)                                                                     \
+  case R0:                                                                              \
+    asm("s_nop 1\n\t"                                                                   \
+        "v_mul_f32_dpp %0, %4, %5 row_newbcast:" #R0 " row_mask:0xf bank_mask:0xf\n\t"    \
+        "v_mul_f32_dpp %1, %4, %6 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"         \
+        "v_mul_f32_dpp %2, %4, %7 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"        \
+        "v_mul_f32_dpp %3, %4, %8 row_newbcast:%11 row_mask:0xf bank_mask:0xf"              \
+        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3])                              \
+        : "v"(f), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "n"(R0 + 1), "n"(R0 + 2),  \
+          "n"(R0 + 3));                                                                 \
+    break
+  switch (r0) {
+    KVQ_MUL4(0); KVQ_MUL4(4); KVQ_MUL4(8); default: KVQ_MUL4(12);
+  }
+#undef KVQ_MUL4
+}
+// acc += d[e] * (f of lane r0 + e of this lane's row), e = 0..3, as four v_fmac_f32 with
+// the DPP row_newbcast source (the compiler does not fold DPP into v_fmac).  The
+// leading s_nop covers the two wait states a DPP read needs after a vector write of
+// its source register.
+__device__ __forceinline__ void fmac4_row_bcast(float& acc, float f, int r0, float d0, float d1,
+                                                float d2, float d3) {
+#define KVQ_FMAC4(R0)                                                                       \
+  case R0:                                                                                 \
+    asm volatile("s_nop 1\n\t"                                                             \
+                 "v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #R0 " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %0, %1, %3 row_newbcast:%6 row_mask:0xf bank_mask:0xf\n\t"      \
+                 "v_fmac_f32_dpp %0, %1, %4 row_newbcast:%7 row_mask:0xf bank_mask:0xf\n\t"      \
+                 "v_fmac_f32_dpp %0, %1, %5 row_newbcast:%8 row_mask:0xf bank_mask:0xf"            \
+                 : "+v"(acc)                                                               \
+                 : "v"(f), "v"(d0), "v"(d1), "v"(d2), "v"(d3), "n"(R0 + 1), "n"(R0 + 2),   \
+                   "n"(R0 + 3));                                                           \
+    break
+  switch (r0) {
+    KVQ_FMAC4(0); KVQ_FMAC4(4); KVQ_FMAC4(8); default: KVQ_FMAC4(12);
+  }
+#undef KVQ_FMAC4
+}
+
 // Key order inside a 64-key tile.  The A operand of S^T = K . Q^T is loaded so that
 // MFMA row i (0..63) holds key tile_key(i) = 32 (i / 32) + 16 ((i / 4) % 2)
 // + 4 ((i % 32) / 8) + i % 4.  With the 32x32 result layout (lane l, register r of
@@ -76,8 +121,18 @@ __device__ __forceinline__ int tile_key(int i) {
   return 32 * (i / 32) + 16 * ((j / 4) % 2) + 4 * (j / 8) + j % 4;
 }
 
-// Pipeline depth: tile t is in softmax/PV, t + 1 in QK, t + 2 and t + 3 in flight.
-constexpr int kStagesMax = 4;  // tile ring slots (head_dim 128: 3, see prefill_kernel)
+// Pipeline.  K (with the per-token scales) and V travel in separate LDS rings: the K
+// operand of tile t + 1 is read one tile before the V operand of tile t + 1, so each
+// ring is refilled as soon as its own contents are dead.  Iteration t runs phase 1
+// (S^T of tile t + 1, P' of tile t), one workgroup barrier, then phase 2 (P.V of tile
+// t, row sum and scaled scores).  The barrier of iteration t publishes K of tile t + 2
+// and V of tile t + 1.  Phase 1 issues the loads of K of tile t + 3 (its slot held K of
+// tile t, last read before the previous barrier) and of V of tile t + 2 (its slot held
+// V of tile t - 2, likewise), so each load has one and a half iterations to land, and
+// the operand reads of phase 2's first chunks are issued before the barrier.
+constexpr int kKSlots = 3;
+constexpr int kVSlots = 4;
+constexpr int kFSlots = 2;  // per-wave factor blocks: tiles t and t + 1
 // Block-table entries are fetched into LDS by direct loads, kIdTiles tiles' worth at a
 // time, one chunk ahead of use.  (Reading them with vector loads inside the tile loop
 // would put them in the same in-order completion count as the tile loads and force
@@ -85,39 +140,35 @@ constexpr int kStagesMax = 4;  // tile ring slots (head_dim 128: 3, see prefill_
 constexpr int kIdTiles = 64;
 static_assert(kIdTiles * kTilePages == kThreads, "one page id per thread per chunk");
 
-// LDS layout of one pipeline stage.  Every region is an array of 16-byte chunks
-// written by direct global->LDS loads: one load instruction writes 64 consecutive
-// chunks, one per lane.  Each load instruction reads from a single page, so its
-// global address is that page's base (scalar registers) plus a per-lane offset that
-// does not change from tile to tile.
-//   K:  page p (tile keys 16 p .. 16 p + 15) at chunks p * KPC + [0, 16 NC); token t,
-//       dim chunk c (bytes 16 c .. 16 c + 15) at NC t + 2 ((c / 2) ^ phi(t)) + c % 2.
-//       The XOR on 32-byte pairs and the odd page stride KPC = 16 NC + 1 put the
-//       16 rows one operand read touches (8 tokens of 2 pages, one chunk each) on
-//       16 different bank groups.
-//   VT: page p, channel d at chunk p * D + d: the page's 16 tokens of that channel.
-//   KS, VS: the 64 keys' K and V scales (per-token-head mode).
-//   CF, FV, IF (one copy per wave): per-key factors derived from KS/VS: score
-//       multiplier k_scale * q_scale * softmax_scale * log2(e), P' factor v_scale /
-//       (v_ref * prob_scale) and its reciprocal.
+// LDS layout.  Every tile region is an array of 16-byte chunks written by direct
+// global->LDS loads: one load instruction writes 64 consecutive chunks, one per lane.
+// Each load instruction reads from a single page, so its global address is that
+// page's base (scalar registers) plus a per-lane offset that does not change from
+// tile to tile.
+//   K slot: page p (tile keys 16 p .. 16 p + 15) at chunks p * KPC + [0, 16 NC);
+//       token t, dim chunk c (bytes 16 c .. 16 c + 15) at NC t + 2 ((c / 2) ^ phi(t))
+//       + c % 2.  The XOR on 32-byte pairs and the odd page stride KPC = 16 NC + 1 put
+//       the 16 rows one operand read touches (8 tokens of 2 pages, one chunk each) on
+//       16 different bank groups.  Then KS, VS: the 64 keys' K and V scales
+//       (per-token-head mode).
+//   V slot: page p, channel d at chunk p * D + d: the page's 16 tokens of that channel.
+//   Factor block (per wave, per tile): per-key factors derived from KS/VS: CF, the
+//       score multiplier k_scale * q_scale * softmax_scale * log2(e); FV, the P'
+//       factor v_scale / (v_ref * prob_scale); IF, its reciprocal.
 template <int D>
 struct Layout {
   static constexpr int NC = D / 16;            // 16-byte chunks per key row
   static constexpr int KPC = 16 * NC + 1;      // chunk stride of K pages
-  static constexpr int K_OFF = 0;
   static constexpr int K_CHUNKS = kTilePages * KPC;
-  static constexpr int VT_OFF = K_OFF + 16 * K_CHUNKS;
-  static constexpr int VT_CHUNKS = kTilePages * D;
-  static constexpr int KS_OFF = VT_OFF + 16 * VT_CHUNKS;
+  static constexpr int KS_OFF = 16 * K_CHUNKS;
   static constexpr int VS_OFF = KS_OFF + kTile * 4;
-  // one factor block per wave (each wave derives its own copy, so no barrier is
-  // needed between deriving and reading); offsets inside a block:
-  static constexpr int FAC_OFF = VS_OFF + kTile * 4;
+  static constexpr int K_BYTES = VS_OFF + kTile * 4;
+  static constexpr int VT_CHUNKS = kTilePages * D;
+  static constexpr int V_BYTES = 16 * VT_CHUNKS;
   static constexpr int CF_OFF = 0;
   static constexpr int FV_OFF = CF_OFF + kTile * 4;
   static constexpr int IF_OFF = FV_OFF + kTile * 4;
-  static constexpr int FSZ = IF_OFF + kTile * 4;
-  static constexpr int BYTES = FAC_OFF + kWaves * FSZ;
+  static constexpr int F_BYTES = IF_OFF + kTile * 4;
   // load instructions per page for K and for V (64 chunks each), and per wave per
   // tile for each
   static constexpr int PI = 16 * NC / kWave;
@@ -153,28 +204,28 @@ __device__ __forceinline__ T lds_read(const uint8_t* base, int byte_off) {
 
 // Two waves per SIMD (two workgroups per CU), so one wave's vector work overlaps the
 // other's matrix work, where it fits: <= 256 registers per lane and <= 80 KB of LDS
-// per workgroup.  head_dim 128 takes a three-slot tile ring (62 KB) and reads the
-// per-key factors from LDS where they are used instead of queueing them in registers
-// beside the operands (a few registers still spill); head_dim 64 per-token-head needs
-// the late factor reads to fit.  8,192 new keys on 32,768: head_dim 128 6.15 -> 4.02 ms
-// per-token-head, 4.53 -> 3.06 ms per-tensor; head_dim 64 per-token-head 13.3 -> 7.5
-// ms.  head_dim 256 cannot (its accumulators alone take 128 registers); head_dim 64
-// per-tensor measured 2% slower at two waves.
+// per workgroup.  head_dim 128, and head_dim 64 per-token-head, read the per-key
+// factors (P' scale, its reciprocal, the K-scale score factor) from LDS at the
+// instruction that uses them instead of queueing them in registers one chunk ahead
+// with the operands (the queue cost 16-32 registers, which spilled ~50 at head_dim 64
+// per-token-head).  head_dim 256 cannot (its accumulators alone take 128 registers);
+// head_dim 64 per-tensor measured 2% slower at two waves.
 template <int D, bool kPTH>
 constexpr int prefill_waves_per_simd() { return D == 128 || (D == 64 && kPTH) ? 2 : 1; }
 
 template <int D, int G, bool kPTH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     prefill_waves_per_simd<D, kPTH>()))) void prefill_kernel(const PrefillArgs a) {
-  constexpr bool kTwoWaves = prefill_waves_per_simd<D, kPTH>() == 2;
-  constexpr int kStages = kTwoWaves && D == 128 ? 3 : kStagesMax;
-  constexpr bool kLateFactors = kTwoWaves;  // factors read at their use, not queued
+  constexpr bool kLateFactors = prefill_waves_per_simd<D, kPTH>() == 2;  // read at use
   using LY = Layout<D>;
   constexpr int NP = kWgRows / G;  // query positions per workgroup
   constexpr int KS = D / 64;       // 64-dim steps of the QK contraction
   constexpr int DB = D / 32;       // 32-dim blocks of the output
-  constexpr int PER_TILE = 2 * LY::W + (kPTH ? 1 : 0);  // loads per wave per tile
-  __shared__ __align__(16) uint8_t lds[kStages][LY::BYTES];
+  constexpr int PER_K = LY::W + (kPTH ? 1 : 0);  // K-side loads per wave per tile
+  constexpr int PER_V = LY::W;                    // V-side loads per wave per tile
+  __shared__ __align__(16) uint8_t k_lds[kKSlots][LY::K_BYTES];
+  __shared__ __align__(16) uint8_t v_lds[kVSlots][LY::V_BYTES];
+  __shared__ __align__(16) uint8_t f_lds[kWaves][kFSlots][LY::F_BYTES];
   // physical page ids of the workgroup's tiles, kIdTiles tiles per chunk, two chunks
   __shared__ __align__(16) int ids_lds[2][kIdTiles * kTilePages];
 
@@ -242,66 +293,60 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // re-load is harmless), in one LDS read
   auto tile_ids = [&](int t) {
     const int rel = min(t, t_last) - t_first;
-    return *reinterpret_cast<const int4*>(
+    const int4 v = *reinterpret_cast<const int4*>(
         &ids_lds[(rel / kIdTiles) & 1][(rel % kIdTiles) * kTilePages]);
+    return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                     __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
   };
-  // Load instruction k (0 .. PER_TILE - 1) of this wave for a tile with page ids id4:
-  // K and V block j = k / 2 (page ids made uniform; K and V pages of one head have the
-  // same size, 16 D bytes, hence the same (page, head) byte offset), then the scales.
-  auto issue_load = [&](int k, int slot, const int4 id4) {
-    if (k < 2 * LY::W) {
-      const int j = k / 2;
-      const int pg = (kWaves / LY::PI) * j + wave / LY::PI;  // (wave + 4 j) / PI
-      const int id = __builtin_amdgcn_readfirstlane(
-          pg == 0 ? id4.x : pg == 1 ? id4.y : pg == 2 ? id4.z : id4.w);
-      const uint64_t off = (uint64_t)(uint32_t)(id * hkv + g) * (uint64_t)(16 * D) +
-                           (uint64_t)(1024 * jj);
-      if (k % 2 == 0)
-        lds_load16s(a.k_pages + off, k_voff,
-                    lds_offset(&lds[slot][LY::K_OFF + 16 * (pg * LY::KPC + 64 * jj)]));
-      else
-        lds_load16s(a.v_pages + off, v_voff,
-                    lds_offset(&lds[slot][LY::VT_OFF + 16 * (pg * D + 64 * jj)]));
+  // This wave's load instruction k of a tile with (uniform) page ids id4 (K and V pages of one head have the same size, 16 D bytes, hence the same
+  // (page, head) byte offset).  K side: k < W covers K block k, then (per-token-head)
+  // the scales; V side: V block k.
+  auto page_off = [&](int k, const int4 id4) {
+    const int pg = (kWaves / LY::PI) * k + wave / LY::PI;  // (wave + 4 k) / PI
+    const int id = pg == 0 ? id4.x : pg == 1 ? id4.y : pg == 2 ? id4.z : id4.w;
+    return (uint64_t)(uint32_t)(id * hkv + g) * (uint64_t)(16 * D) + (uint64_t)(1024 * jj);
+  };
+  auto issue_k = [&](int k, uint8_t* slot, const int4 id4) {
+    if (k < LY::W) {
+      const int pg = (kWaves / LY::PI) * k + wave / LY::PI;
+      lds_load16s(a.k_pages + page_off(k, id4), k_voff,
+                  lds_offset(slot + 16 * (pg * LY::KPC + 64 * jj)));
     } else if constexpr (kPTH) {  // waves 0/2: K scales, 1/3: V scales (2, 3 repeat)
       const int page = lane / kPage;
       const int id = page == 0 ? id4.x : page == 1 ? id4.y : page == 2 ? id4.z : id4.w;
       const int64_t idx = ((int64_t)id * hkv + g) * kPage + lane % kPage;
       const bool kside = wave % 2 == 0;
       lds_load4((kside ? a.k_scales : a.v_scales) + idx,
-                lds_offset(&lds[slot][kside ? LY::KS_OFF : LY::VS_OFF]));
+                lds_offset(slot + (kside ? LY::KS_OFF : LY::VS_OFF)));
     }
   };
-  auto issue_tile = [&](int t, int slot) {
-    const int4 id4 = tile_ids(t);
-#pragma unroll
-    for (int k = 0; k < PER_TILE; ++k) issue_load(k, slot, id4);
+  auto issue_v = [&](int k, uint8_t* slot, const int4 id4) {
+    const int pg = (kWaves / LY::PI) * k + wave / LY::PI;
+    lds_load16s(a.v_pages + page_off(k, id4), v_voff,
+                lds_offset(slot + 16 * (pg * D + 64 * jj)));
   };
-  // Wait for this wave's loads of the next tile (the loads of the tiles issued after
-  // it may stay in flight), then make every wave's loads visible.
-  auto wait_tile = [&]() {
-    wait_vmcnt<PER_TILE * (kStages - 2)>();
+  // This wave's direct loads done, then every wave's (a compiler barrier on each side
+  // keeps the LDS reads of the new contents after it).
+  auto publish = [&]() {
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
   // Slots past the sequence end were never written (any bytes, NaN included): zero
-  // their V bytes and scales before anyone reads the tile.
-  auto scrub_tile = [&](int t, uint8_t* st) {
+  // the V bytes of a tile that ends past it before anyone reads them (its scales are
+  // masked where they are read).
+  auto scrub_v = [&](int t, uint8_t* st) {
     const int valid = L - t * kTile;  // keys of the tile below the sequence end
     if (valid >= kTile) return;
     for (int ch = tid; ch < LY::VT_CHUNKS; ch += kThreads) {
       const int keep = min(max(valid - (ch / D) * kPage, 0), kPage);  // tokens kept
       if (keep < kPage) {
-        uint32_t* w = reinterpret_cast<uint32_t*>(st + LY::VT_OFF + 16 * ch);
+        uint32_t* w = reinterpret_cast<uint32_t*>(st + 16 * ch);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int kq = min(max(keep - 4 * q, 0), 4);
           w[q] &= kq >= 4 ? 0xFFFFFFFFu : ((1u << (8 * kq)) - 1u);
         }
-      }
-    }
-    if constexpr (kPTH) {
-      if (tid < kTile && tid >= valid) {
-        reinterpret_cast<float*>(st + LY::KS_OFF)[tid] = 0.0f;
-        reinterpret_cast<float*>(st + LY::VS_OFF)[tid] = 0.0f;
       }
     }
     barrier_lds();
@@ -319,26 +364,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // v_ref (the running V scale maximum) moves here, tile by tile, identically in
   // every wave.
   float vref_run = 0.0f;
-  const int fac = LY::FAC_OFF + wave * LY::FSZ;
-  auto derive_finish = [&](uint8_t* st, float ks, float vs) {
+  auto read_scales = [&](const uint8_t* kslot, float& ks, float& vs) {
     if constexpr (kPTH) {
-      // V scales are >= 0 (unwritten slots were scrubbed to 0): compare bits
+      ks = reinterpret_cast<const float*>(kslot + LY::KS_OFF)[lane];
+      vs = reinterpret_cast<const float*>(kslot + LY::VS_OFF)[lane];
+    }
+  };
+  auto derive = [&](int t, uint8_t* fb, float ks, float vs) {
+    if constexpr (kPTH) {
+      // keys past the sequence end hold unwritten scales: take them as 0
+      if (t * kTile + lane >= L) ks = vs = 0.0f;
+      // V scales are >= 0: compare bits
       vref_run = __uint_as_float(
           max(__float_as_uint(vref_run), wave_max_u32(__float_as_uint(vs))));
       // P' factor and its reciprocal (hardware reciprocals: any f works as long as
       // the row sum maps P' back with the same f, up to rounding)
       const float f = vref_run > 0.0f ? vs * __builtin_amdgcn_rcpf(vref_run * a.prob_scale)
                                       : 0.0f;
-      uint8_t* fb = st + fac;
       reinterpret_cast<float*>(fb + LY::CF_OFF)[lane] = ks * qk_base;
       reinterpret_cast<float*>(fb + LY::FV_OFF)[lane] = f;
       reinterpret_cast<float*>(fb + LY::IF_OFF)[lane] = f > 0.0f ? __builtin_amdgcn_rcpf(f) : 0.0f;
     }
-  };
-  auto derive_tile = [&](uint8_t* st) {
-    if constexpr (kPTH)
-      derive_finish(st, reinterpret_cast<const float*>(st + LY::KS_OFF)[lane],
-                    reinterpret_cast<const float*>(st + LY::VS_OFF)[lane]);
   };
 
   // ---- query codes: B operand of S^T = K . Q^T -----------------------------------
@@ -393,14 +439,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     const int tr = 4 * (row / 8) + row % 4;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      k_addr[ks] = LY::K_OFF + 16 * (((row / 4) % 2) * LY::KPC + LY::NC * tr +
+      k_addr[ks] = 16 * (((row / 4) % 2) * LY::KPC + LY::NC * tr +
                                      2 * ((2 * ks + grp) ^ LY::phi(tr)));
   }
   constexpr int K_KB = 16 * 2 * LY::KPC;
   // V^T operand: channel 32 db + row; bytes 0-15 = page grp, 16-31 = page 2 + grp
-  const int v_lane = LY::VT_OFF + 16 * (grp * D + row);
+  const int v_lane = 16 * (grp * D + row);
   constexpr int V_HI = 16 * 2 * D;
-  const int s_lane = fac + 4 * 16 * grp;  // this wave's factors, lane group grp
+  const int s_lane = 4 * 16 * grp;  // factors of lane group grp inside a block
   const float pmul = 1.0f / a.prob_scale;
 
   // S^T = K . Q^T of a resident tile, for the two 32-key blocks
@@ -462,24 +508,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     return mx;
   };
 
-  // prologue: page ids of the first chunk; tiles t_first .. t_first + kStages - 2 in
-  // flight; the first two made resident, the factors of the first derived (iteration
-  // t derives those of tile t + 1)
+  // prologue: page ids of the first chunk; K of tiles t_first, t_first + 1 and V of
+  // t_first resident; then K of t_first + 2 and V of t_first + 1 in flight (the order
+  // the loop's waits count on); factors of t_first derived (iteration t derives those
+  // of tile t + 1).
   issue_ids(0);
   wait_vmcnt<0>();
   barrier_lds();
+  {
+    const int4 i0 = tile_ids(t_first), i1 = tile_ids(t_first + 1);
 #pragma unroll
-  for (int st = 0; st < kStages - 1; ++st) issue_tile(t_first + st, st);
-  wait_vmcnt<PER_TILE * (kStages - 2)>();
-  __builtin_amdgcn_s_barrier();
-  scrub_tile(t_first, lds[0]);
-  derive_tile(lds[0]);
-  barrier_lds();
-  if (t_first < t_last) {
-    wait_vmcnt<PER_TILE * (kStages - 3)>();
-    __builtin_amdgcn_s_barrier();
-    scrub_tile(t_first + 1, lds[1]);
-    barrier_lds();
+    for (int k = 0; k < PER_K; ++k) issue_k(k, k_lds[0], i0);
+#pragma unroll
+    for (int k = 0; k < PER_K; ++k) issue_k(k, k_lds[1], i1);
+#pragma unroll
+    for (int k = 0; k < PER_V; ++k) issue_v(k, v_lds[0], i0);
+    wait_vmcnt<0>();
+    publish();
+    scrub_v(t_first, v_lds[0]);
+    const int4 i2 = tile_ids(t_first + 2);
+#pragma unroll
+    for (int k = 0; k < PER_K; ++k) issue_k(k, k_lds[2], i2);
+#pragma unroll
+    for (int k = 0; k < PER_V; ++k) issue_v(k, v_lds[1], i1);
+  }
+  {
+    float ks = 0.0f, vs = 0.0f;
+    read_scales(k_lds[0], ks, vs);
+    derive(t_first, f_lds[wave][0], ks, vs);
   }
 
   // The tile loop, specialised on how P' is formed from p: PM 0: p * factor; PM 1:
@@ -489,97 +545,113 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // runs while the row sum and the next tile's scaled scores are formed.
   auto main_loop = [&](auto pm_tag) {
     constexpr int PM = decltype(pm_tag)::value;
+    // ---- operand queue: chunk c < NQK is S^T MFMA c (K operand of tile t + 1, P'
+    // factors of tile t), chunk NQK + db is P.V MFMA db (V operand of tile t, row-sum
+    // factors of tile t, score factors of tile t + 1).  Operands are read QD chunks
+    // ahead, across the barrier and into the next iteration.
+    constexpr int NQK = 2 * KS;          // MFMAs of S^T per tile
+    constexpr int WQ = 8 / NQK;          // P' words per phase-1 chunk
+    constexpr int WV = 8 / DB;           // row-sum words / score groups per phase-2 chunk
+    constexpr int NCH = NQK + DB;
+    constexpr int QD = 2;                // queue depth (chunks read ahead)
+    static_assert(QD <= NQK && QD <= DB, "queue depth");
+    // the loads in phase-1 chunks 1 .. NQK - 1 (chunk 0 would wait for the page-id
+    // read), LPC per chunk: K of tile t + 3, then V of tile t + 2
+    constexpr int NLD = PER_K + PER_V;
+    constexpr int LPC = NQK > 1 ? (NLD + NQK - 2) / (NQK - 1) : NLD;
+    struct Chunk {
+      v8i op;
+      float4 f2[WV];  // score factors (phase-2 chunks, queued mode)
+    };
+    auto k_operand = [&](const uint8_t* kb, int i) {  // key block i % 2, dim step i / 2
+      const int off = k_addr[i / 2] + K_KB * (i % 2);
+      const uint4 x0 = lds_read<uint4>(kb, off);
+      const uint4 x1 = lds_read<uint4>(kb, off + 16);
+      return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                   (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    };
+    auto v_operand = [&](const uint8_t* vb, int db) {
+      const int off = v_lane + 16 * 32 * db;
+      const uint4 x0 = lds_read<uint4>(vb, off);
+      const uint4 x1 = lds_read<uint4>(vb, off + V_HI);
+      return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                   (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    };
+    // per-key factors of word / score group w (keys 32 (w / 4) + 16 grp + 4 (w % 4) ..)
+    auto factor = [&](const uint8_t* fb, int region, int w, float uniform) {
+      if constexpr (kPTH) return lds_read<float4>(fb, region + s_lane + 16 * (8 * (w / 4) + w % 4));
+      else return make_float4(uniform, uniform, uniform, uniform);
+    };
+    // chunk c of an iteration whose K operand tile is in kb, V operand tile in vb,
+    // factors of its tile in fb and of the next tile in fbn
+    auto load_chunk = [&](int c, const uint8_t* kb, const uint8_t* vb, const uint8_t* fb,
+                          const uint8_t* fbn, Chunk& q) {
+      if (c < NQK) {
+        q.op = k_operand(kb, c);
+      } else {
+        const int db = c - NQK;
+        q.op = v_operand(vb, db);
+        if constexpr (!kLateFactors) {
+#pragma unroll
+          for (int u = 0; u < WV; ++u) q.f2[u] = factor(fbn, LY::CF_OFF, WV * db + u, qk_base);
+        }
+      }
+    };
+
     float x[32];
-    float mx;
     uint32_t pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // P' codes of the current tile
     {
       v16f sc[2];
-      qk(lds[0], sc);
+      qk(k_lds[0], sc);
 #pragma unroll
-      for (int w = 0; w < 8; ++w) scale_group(w, lds[0], sc, 0.0f, x);
+      for (int w = 0; w < 8; ++w) scale_group(w, f_lds[wave][0], sc, 0.0f, x);
     }
+    Chunk cq[QD];
+    // every wave's reads of K of tile t_first done before K of tile t_first + 3 is
+    // loaded into its slot
+    publish();
+
+    int kr = 0;  // K slot of tile t: (t - t_first) % kKSlots
+    int4 ids_v = tile_ids(t_first + 2);  // page ids of tile t + 2
     for (int t = t_first; t <= t_last; ++t) {
       const int rel = t - t_first;
-      const uint8_t* buf = lds[rel % kStages];
-      const uint8_t* nbuf = lds[(rel + 1) % kStages];  // past the last tile: unused
+      const int kr1 = kr == kKSlots - 1 ? 0 : kr + 1;
+      const int kr2 = kr1 == kKSlots - 1 ? 0 : kr1 + 1;
+      const uint8_t* kb1 = k_lds[kr1];            // K of tile t + 1
+      const uint8_t* kb2 = k_lds[kr2];            // K of tile t + 2 (published mid-way)
+      uint8_t* const kb3 = k_lds[kr];             // K of tile t + 3 goes here
+      const uint8_t* vb0 = v_lds[rel & 3];        // V of tile t
+      uint8_t* const vb1 = v_lds[(rel + 1) & 3];  // V of tile t + 1 (published mid-way)
+      uint8_t* const vb2 = v_lds[(rel + 2) & 3];  // V of tile t + 2 goes here
+      uint8_t* const fb0 = f_lds[wave][rel & 1];        // factors of tile t
+      uint8_t* const fb1 = f_lds[wave][(rel + 1) & 1];  // factors of tile t + 1
+      // V of tile t (published by the previous barrier) is first read in phase 1
+      if (rel > 0) scrub_v(t, v_lds[rel & 3]);
       const float vr = vref_run;  // v_ref after tile t (before tile t + 1 is derived)
-      // ---- operand queue: chunk c < NQK is S^T MFMA c (K operand of tile t + 1, P'
-      // factors of tile t), chunk NQK + db is P.V MFMA db (V operand of tile t,
-      // row-sum factors of tile t, score factors of tile t + 1).  Operands are read QD
-      // chunks ahead; the first QD are read here, before the rescale test runs, to
-      // cover their latency.
-      constexpr int NQK = 2 * KS;          // MFMAs of S^T per tile
-      constexpr int WQ = 8 / NQK;          // P' words per phase-1 chunk
-      constexpr int WV = 8 / DB;           // row-sum words / score groups per phase-2 chunk
-      constexpr int NCH = NQK + DB;
-      static_assert(PER_TILE + 1 <= NCH, "one load per chunk");
-      constexpr int MW = WQ > WV ? WQ : WV;
-      // queue depth (chunks read ahead)
-      constexpr int QD = 2;
-      auto k_operand = [&](int i) {        // chunk i: key block i % 2, dim step i / 2
-        const int off = k_addr[i / 2] + K_KB * (i % 2);
-        const uint4 x0 = lds_read<uint4>(nbuf, off);
-        const uint4 x1 = lds_read<uint4>(nbuf, off + 16);
-        return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      };
-      auto v_operand = [&](int db) {
-        const int off = v_lane + 16 * 32 * db;
-        const uint4 x0 = lds_read<uint4>(buf, off);
-        const uint4 x1 = lds_read<uint4>(buf, off + V_HI);
-        return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      };
-      // per-key factors of word / score group w (keys 32 (w / 4) + 16 grp + 4 (w % 4) ..)
-      auto factor = [&](const uint8_t* b, int region, int w, float uniform) {
-        if constexpr (kPTH) return lds_read<float4>(b, region + s_lane + 16 * (8 * (w / 4) + w % 4));
-        else return make_float4(uniform, uniform, uniform, uniform);
-      };
-      struct Chunk {
-        v8i op;
-        float4 f[MW], f2[MW];
-      };
-      auto load_chunk = [&](int c, Chunk& q) {
-        if (c < NQK) {
-          q.op = k_operand(c);
-          if constexpr (!kLateFactors) {
-#pragma unroll
-            for (int u = 0; u < WQ; ++u) q.f[u] = factor(buf, LY::FV_OFF, WQ * c + u, pmul);
-          }
-        } else {
-          const int db = c - NQK;
-          q.op = v_operand(db);
-          if constexpr (!kLateFactors) {
-#pragma unroll
-            for (int u = 0; u < WV; ++u) {
-              q.f[u] = factor(buf, LY::IF_OFF, WV * db + u, 1.0f);
-              q.f2[u] = factor(nbuf, LY::CF_OFF, WV * db + u, qk_base);
-            }
-          }
-        }
-      };
-      // factors of tile t + 1 (its scales were made resident by the previous
-      // iteration): scales read here, factors written in chunk 1 (before the first
-      // score-factor read) or, with fewer than 4 S^T chunks, right away
-      uint8_t* const dbuf = lds[(rel + 1) % kStages];  // past the last tile: unused
+      // scales of tile t + 1 (resident since the previous barrier): read here, factors
+      // written in chunk 1 (before the first read of them) or, with fewer than 4 S^T
+      // chunks, right away
       float dks = 0.0f, dvs = 0.0f;
-      if constexpr (kPTH) {
-        dks = reinterpret_cast<const float*>(dbuf + LY::KS_OFF)[lane];
-        dvs = reinterpret_cast<const float*>(dbuf + LY::VS_OFF)[lane];
-        if constexpr (NQK < 4) derive_finish(dbuf, dks, dvs);
-      }
-      Chunk cq[QD];
+      read_scales(kb1, dks, dvs);
+      if constexpr (kPTH && NQK < 4) derive(t + 1, fb1, dks, dvs);
 #pragma unroll
-      for (int c = 0; c < QD; ++c) load_chunk(c, cq[c]);
-
+      for (int c = 0; c < QD; ++c) load_chunk(c, kb1, vb0, fb0, fb1, cq[c]);
+      // P' factors and their reciprocals of tile t, lane i of row 2 grp + h holding key
+      // 32 kb + 16 grp + i in register kb: score register r of key block kb takes its
+      // factor from lane r of its row
+      float fvb[2] = {pmul, pmul}, ifb[2] = {1.0f, 1.0f};
+      if constexpr (kPTH) {
+        const float* fv = reinterpret_cast<const float*>(fb0 + LY::FV_OFF) + 16 * grp + lane % 16;
+        const float* fi = reinterpret_cast<const float*>(fb0 + LY::IF_OFF) + 16 * grp + lane % 16;
+        fvb[0] = fv[0];
+        fvb[1] = fv[32];
+        ifb[0] = fi[0];
+        ifb[1] = fi[32];
+      }
       if (rel % kIdTiles == 0) issue_ids(rel / kIdTiles + 1);
-      // loads of tile t + 3 (into tile t - 1's slot): issued one per chunk from chunk 1
-      // on, so that they overlap the matrix and vector work
-      const int4 ld_ids = tile_ids(t + kStages - 1);
-      const int ld_slot = (rel + kStages - 1) % kStages;
-      // masks and row maxima of tile t's scores (vector work that covers the latency
-      // of the operand reads above)
-      mx = mask_max(t, x);
+      const int4 ids_k = tile_ids(t + 3);
+      // masks and row maxima of tile t's scores
+      float mx = mask_max(t, x);
 
       // ---- rescale when v_ref grew or a score passed the reference by the slack ----
       float fo = 1.0f;  // factor for o
@@ -612,10 +684,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       }
 
       // ---- phase 1 (chunks 0 .. NQK - 1): S^T of tile t + 1 on the matrix cores; P' of
-      // tile t (e4m3, in the B-operand layout) on the vector unit.  Phase 2 (chunks
-      // NQK ..): O^T += V^T . P'^T on the matrix cores; the row sum of the rounded P'
-      // and the scaled scores of tile t + 1 (past the last tile: unused) on the
-      // vector unit.  Each chunk holds one MFMA and a share of the vector work;
+      // tile t (e4m3, in the B-operand layout) on the vector unit.  Barrier.  Phase 2
+      // (chunks NQK ..): O^T += V^T . P'^T on the matrix cores; the row sum of the
+      // rounded P' and the scaled scores of tile t + 1 (past the last tile: unused) on
+      // the vector unit.  Each chunk holds one MFMA and a share of the vector work;
       // scheduling barriers keep the chunks in order, so the matrix cores, the vector
       // unit and the LDS overlap.
       v16f sn[2] = {(v16f){}, (v16f){}};
@@ -624,24 +696,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const Chunk cur = cq[c % QD];
-        if (c + QD < NCH) load_chunk(c + QD, cq[c % QD]);
-        if (c >= 1 && c - 1 < PER_TILE) issue_load(c - 1, ld_slot, ld_ids);
+        if (c + QD < NCH) load_chunk(c + QD, kb1, vb0, fb0, fb1, cq[c % QD]);
+        if (c >= 1 && c < NQK) {
+#pragma unroll
+          for (int u = 0; u < LPC; ++u) {
+            const int k = (c - 1) * LPC + u;
+            if (k < PER_K) issue_k(k, kb3, ids_k);
+            else if (k < NLD) issue_v(k - PER_K, vb2, ids_v);
+          }
+        }
         if constexpr (kPTH && NQK >= 4)
-          if (c == 1) derive_finish(dbuf, dks, dvs);
+          if (c == 1) derive(t + 1, fb1, dks, dvs);
+        if (c == NQK) {
+          // K of tile t + 2 and V of tile t + 1 resident: wait for them (the loads of
+          // K of tile t + 3 and V of tile t + 2 may stay in flight), publish
+          wait_vmcnt<NLD>();
+          publish();
+        }
         if (c < NQK) {
           sn[c % 2] = mfma(cur.op, qb[c / 2], sn[c % 2]);
 #pragma unroll
           for (int u = 0; u < WQ; ++u) {
             const int w = WQ * c + u;
-            const float4 fu = kLateFactors ? factor(buf, LY::FV_OFF, w, pmul) : cur.f[u];
-            const float f[4] = {fu.x, fu.y, fu.z, fu.w};
-            float pq[4];
+            float pe[4], pq[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float p = __builtin_amdgcn_exp2f(x[4 * w + e]);
-              if constexpr (PM == 2) pq[e] = p;
-              else if constexpr (PM == 1) pq[e] = fminf(p * f[e], kE4m3Max);
-              else pq[e] = p * f[e];
+            for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(x[4 * w + e]);
+            if constexpr (PM == 2) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) pq[e] = pe[e];
+            } else {
+              if constexpr (kPTH) {
+                mul4_row_bcast(pq, fvb[w / 4], 4 * (w % 4), pe);
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pq[e] = pe[e] * pmul;
+              }
+              if constexpr (PM == 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pq[e] = fminf(pq[e], kE4m3Max);
+              }
             }
             // the two conversions fill bytes 0-1 and 2-3; the old contents are dead
             const uint32_t lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(pq[0], pq[1], pw[w], false);
@@ -659,15 +752,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
           for (int u = 0; u < WV; ++u) {
             const int w = WV * db + u;
-            const float4 fi = kLateFactors ? factor(buf, LY::IF_OFF, w, 1.0f) : cur.f[u];
-            const float4 fc = kLateFactors ? factor(nbuf, LY::CF_OFF, w, qk_base) : cur.f2[u];
+            const float4 fc = kLateFactors ? factor(fb1, LY::CF_OFF, w, qk_base) : cur.f2[u];
             if constexpr (kPTH) {
               const float2_t d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], false);
               const float2_t d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], true);
-              lam = fmaf(d01.x, fi.x, lam);
-              lam = fmaf(d01.y, fi.y, lam);
-              lam = fmaf(d23.x, fi.z, lam);
-              lam = fmaf(d23.y, fi.w, lam);
+              fmac4_row_bcast(lam, ifb[w / 4], 4 * (w % 4), d01.x, d01.y, d23.x, d23.y);
             } else {
               const half2_t h01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw[w], 1.0f, false);
               const half2_t h23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw[w], 1.0f, true);
@@ -684,20 +773,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-
-      // ---- tile t + 2 resident (issued two iterations ago): wait, scrub its unwritten
-      // slots.  One barrier per tile: it publishes every wave's
-      // loads of tile t + 2 and closes this iteration's reads of tile t's slot, which
-      // the next iteration's loads overwrite (those reads were all consumed, hence
-      // complete, before it).
-      if (t + 2 <= t_last) {
-        uint8_t* nb = lds[(rel + 2) % kStages];
-        wait_vmcnt<PER_TILE * (kStages - 3)>();
-        barrier_lds();
-        scrub_tile(t + 2, nb);
-      } else {
-        barrier_lds();
-      }
+      kr = kr1;
+      ids_v = ids_k;
     }
   };
   if (a.prob_scale < 256.0f / kE4m3Max) {
