@@ -291,13 +291,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const uint32_t v_voff = 16u * lane;
   // the four page ids of tile t (past the last tile: those of the last tile, whose
   // re-load is harmless), in one LDS read
-  auto tile_ids = [&](int t) {
+  auto tile_ids_raw = [&](int t) {
     const int rel = min(t, t_last) - t_first;
-    const int4 v = *reinterpret_cast<const int4*>(
+    return *reinterpret_cast<const int4*>(
         &ids_lds[(rel / kIdTiles) & 1][(rel % kIdTiles) * kTilePages]);
+  };
+  auto uniform_ids = [](const int4 v) {
     return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
                      __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
   };
+  auto tile_ids = [&](int t) { return uniform_ids(tile_ids_raw(t)); };
   // This wave's load instruction k of a tile with (uniform) page ids id4 (K and V pages of one head have the same size, 16 D bytes, hence the same
   // (page, head) byte offset).  K side: k < W covers K block k, then (per-token-head)
   // the scales; V side: V block k.
@@ -554,6 +557,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int WV = 8 / DB;           // row-sum words / score groups per phase-2 chunk
     constexpr int NCH = NQK + DB;
     constexpr int QD = 2;                // queue depth (chunks read ahead)
+    // head_dim 256 has the registers to carry the queue over the loop's back edge, so
+    // the next tile's first operand reads are issued at the end of this one (others
+    // issue them at the top of the iteration)
+    constexpr bool kCrossQueue = D == 256;
     static_assert(QD <= NQK && QD <= DB, "queue depth");
     // the loads in phase-1 chunks 1 .. NQK - 1 (chunk 0 would wait for the page-id
     // read), LPC per chunk: K of tile t + 3, then V of tile t + 2
@@ -607,12 +614,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       for (int w = 0; w < 8; ++w) scale_group(w, f_lds[wave][0], sc, 0.0f, x);
     }
     Chunk cq[QD];
+    if constexpr (kCrossQueue) {
+#pragma unroll
+      for (int c = 0; c < QD; ++c)
+        load_chunk(c, k_lds[1], v_lds[0], f_lds[wave][0], f_lds[wave][1], cq[c]);
+    }
     // every wave's reads of K of tile t_first done before K of tile t_first + 3 is
     // loaded into its slot
     publish();
 
     int kr = 0;  // K slot of tile t: (t - t_first) % kKSlots
-    int4 ids_v = tile_ids(t_first + 2);  // page ids of tile t + 2
+    int4 ids_v = tile_ids(t_first + 2);       // page ids of tile t + 2
+    int4 ids_k_raw = tile_ids_raw(t_first + 3);  // of tile t + 3, read one tile ahead
     for (int t = t_first; t <= t_last; ++t) {
       const int rel = t - t_first;
       const int kr1 = kr == kKSlots - 1 ? 0 : kr + 1;
@@ -634,8 +647,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       float dks = 0.0f, dvs = 0.0f;
       read_scales(kb1, dks, dvs);
       if constexpr (kPTH && NQK < 4) derive(t + 1, fb1, dks, dvs);
+      if constexpr (!kCrossQueue) {
 #pragma unroll
-      for (int c = 0; c < QD; ++c) load_chunk(c, kb1, vb0, fb0, fb1, cq[c]);
+        for (int c = 0; c < QD; ++c) load_chunk(c, kb1, vb0, fb0, fb1, cq[c]);
+      }
       // P' factors and their reciprocals of tile t, lane i of row 2 grp + h holding key
       // 32 kb + 16 grp + i in register kb: score register r of key block kb takes its
       // factor from lane r of its row
@@ -649,7 +664,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         ifb[1] = fi[32];
       }
       if (rel % kIdTiles == 0) issue_ids(rel / kIdTiles + 1);
-      const int4 ids_k = tile_ids(t + 3);
+      const int4 ids_k = uniform_ids(ids_k_raw);
       // masks and row maxima of tile t's scores
       float mx = mask_max(t, x);
 
@@ -696,7 +711,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const Chunk cur = cq[c % QD];
-        if (c + QD < NCH) load_chunk(c + QD, kb1, vb0, fb0, fb1, cq[c % QD]);
+        if (c + QD < NCH)
+          load_chunk(c + QD, kb1, vb0, fb0, fb1, cq[c % QD]);
+        else if constexpr (kCrossQueue)  // the next tile's: K of t + 2, factors of t + 1
+          load_chunk(c + QD - NCH, kb2, vb1, fb1, fb0, cq[c % QD]);
+        if (c == NCH - 1) ids_k_raw = tile_ids_raw(t + 4);
         if (c >= 1 && c < NQK) {
 #pragma unroll
           for (int u = 0; u < LPC; ++u) {
