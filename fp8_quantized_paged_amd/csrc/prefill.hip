@@ -281,14 +281,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // q covers page q / PI, 64-chunk block jj = q % PI of it (jj is the same for all of
   // a wave's instructions).  Per-lane offsets inside the page:
   const int jj = wave % LY::PI;
+  const int wpg = LY::PI == kWaves ? 0 : wave / LY::PI;  // first page of the wave
+  // per-lane byte offsets inside a page (block jj included)
   uint32_t k_voff;
   {
     const int o = 64 * jj + lane;  // chunk inside the K page
     const int t = o / LY::NC, r = o % LY::NC;
     const int c = 2 * ((r / 2) ^ LY::phi(t)) + r % 2;
-    k_voff = (uint32_t)((t - 64 * jj / LY::NC) * D + 16 * c);
+    k_voff = (uint32_t)((t - 64 * jj / LY::NC) * D + 16 * c + 1024 * jj);
   }
-  const uint32_t v_voff = 16u * lane;
+  const uint32_t v_voff = 16u * lane + 1024u * jj;
   // the four page ids of tile t (past the last tile: those of the last tile, whose
   // re-load is harmless), in one LDS read
   auto tile_ids_raw = [&](int t) {
@@ -301,18 +303,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                      __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
   };
   auto tile_ids = [&](int t) { return uniform_ids(tile_ids_raw(t)); };
-  // This wave's load instruction k of a tile with (uniform) page ids id4 (K and V pages of one head have the same size, 16 D bytes, hence the same
-  // (page, head) byte offset).  K side: k < W covers K block k, then (per-token-head)
-  // the scales; V side: V block k.
-  auto page_off = [&](int k, const int4 id4) {
-    const int pg = (kWaves / LY::PI) * k + wave / LY::PI;  // (wave + 4 k) / PI
-    const int id = pg == 0 ? id4.x : pg == 1 ? id4.y : pg == 2 ? id4.z : id4.w;
-    return (uint64_t)(uint32_t)(id * hkv + g) * (uint64_t)(16 * D) + (uint64_t)(1024 * jj);
+  // This wave's load instruction k of a tile covers block jj of page (kWaves / PI) k +
+  // wpg.  The byte offsets of those pages (the same in the K and V pools: their pages
+  // have one size, 16 D bytes) are computed once per tile, as independent scalar
+  // chains (a dependent chain per load would cost its latency on every load).
+  struct PageOffs {
+    uint64_t o[LY::W];
   };
-  auto issue_k = [&](int k, uint8_t* slot, const int4 id4) {
+  auto page_offsets = [&](const int4 id4) {
+    PageOffs p;
+#pragma unroll
+    for (int k = 0; k < LY::W; ++k) {
+      const int pg = (kWaves / LY::PI) * k + wpg;
+      const int id = pg == 0 ? id4.x : pg == 1 ? id4.y : pg == 2 ? id4.z : id4.w;
+      p.o[k] = (uint64_t)(uint32_t)(id * hkv + g) * (uint64_t)(16 * D);
+    }
+    return p;
+  };
+  // K side: k < W covers K block k, then (per-token-head) the scales of the tile with
+  // (uniform) page ids id4; V side: V block k.
+  auto issue_k = [&](int k, uint8_t* slot, const PageOffs& po, const int4 id4) {
     if (k < LY::W) {
-      const int pg = (kWaves / LY::PI) * k + wave / LY::PI;
-      lds_load16s(a.k_pages + page_off(k, id4), k_voff,
+      const int pg = (kWaves / LY::PI) * k + wpg;
+      lds_load16s(a.k_pages + po.o[k], k_voff,
                   lds_offset(slot + 16 * (pg * LY::KPC + 64 * jj)));
     } else if constexpr (kPTH) {  // waves 0/2: K scales, 1/3: V scales (2, 3 repeat)
       const int page = lane / kPage;
@@ -323,10 +336,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                 lds_offset(slot + (kside ? LY::KS_OFF : LY::VS_OFF)));
     }
   };
-  auto issue_v = [&](int k, uint8_t* slot, const int4 id4) {
-    const int pg = (kWaves / LY::PI) * k + wave / LY::PI;
-    lds_load16s(a.v_pages + page_off(k, id4), v_voff,
-                lds_offset(slot + 16 * (pg * D + 64 * jj)));
+  auto issue_v = [&](int k, uint8_t* slot, const PageOffs& po) {
+    const int pg = (kWaves / LY::PI) * k + wpg;
+    lds_load16s(a.v_pages + po.o[k], v_voff, lds_offset(slot + 16 * (pg * D + 64 * jj)));
   };
   // This wave's direct loads done, then every wave's (a compiler barrier on each side
   // keeps the LDS reads of the new contents after it).
@@ -520,20 +532,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   barrier_lds();
   {
     const int4 i0 = tile_ids(t_first), i1 = tile_ids(t_first + 1);
+    const PageOffs o0 = page_offsets(i0), o1 = page_offsets(i1);
 #pragma unroll
-    for (int k = 0; k < PER_K; ++k) issue_k(k, k_lds[0], i0);
+    for (int k = 0; k < PER_K; ++k) issue_k(k, k_lds[0], o0, i0);
 #pragma unroll
-    for (int k = 0; k < PER_K; ++k) issue_k(k, k_lds[1], i1);
+    for (int k = 0; k < PER_K; ++k) issue_k(k, k_lds[1], o1, i1);
 #pragma unroll
-    for (int k = 0; k < PER_V; ++k) issue_v(k, v_lds[0], i0);
+    for (int k = 0; k < PER_V; ++k) issue_v(k, v_lds[0], o0);
     wait_vmcnt<0>();
     publish();
     scrub_v(t_first, v_lds[0]);
     const int4 i2 = tile_ids(t_first + 2);
+    const PageOffs o2 = page_offsets(i2);
 #pragma unroll
-    for (int k = 0; k < PER_K; ++k) issue_k(k, k_lds[2], i2);
+    for (int k = 0; k < PER_K; ++k) issue_k(k, k_lds[2], o2, i2);
 #pragma unroll
-    for (int k = 0; k < PER_V; ++k) issue_v(k, v_lds[1], i1);
+    for (int k = 0; k < PER_V; ++k) issue_v(k, v_lds[1], o1);
   }
   {
     float ks = 0.0f, vs = 0.0f;
@@ -624,7 +638,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     publish();
 
     int kr = 0;  // K slot of tile t: (t - t_first) % kKSlots
-    int4 ids_v = tile_ids(t_first + 2);       // page ids of tile t + 2
+    PageOffs offs_v = page_offsets(tile_ids(t_first + 2));  // page offsets of tile t + 2
     int4 ids_k_raw = tile_ids_raw(t_first + 3);  // of tile t + 3, read one tile ahead
     for (int t = t_first; t <= t_last; ++t) {
       const int rel = t - t_first;
@@ -665,6 +679,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       }
       if (rel % kIdTiles == 0) issue_ids(rel / kIdTiles + 1);
       const int4 ids_k = uniform_ids(ids_k_raw);
+      const PageOffs offs_k = page_offsets(ids_k);
       // masks and row maxima of tile t's scores
       float mx = mask_max(t, x);
 
@@ -720,8 +735,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
           for (int u = 0; u < LPC; ++u) {
             const int k = (c - 1) * LPC + u;
-            if (k < PER_K) issue_k(k, kb3, ids_k);
-            else if (k < NLD) issue_v(k - PER_K, vb2, ids_v);
+            if (k < PER_K) issue_k(k, kb3, offs_k, ids_k);
+            else if (k < NLD) issue_v(k - PER_K, vb2, offs_v);
           }
         }
         if constexpr (kPTH && NQK >= 4)
@@ -793,7 +808,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         __builtin_amdgcn_sched_barrier(0);
       }
       kr = kr1;
-      ids_v = ids_k;
+      offs_v = offs_k;
     }
   };
   if (a.prob_scale < 256.0f / kE4m3Max) {
