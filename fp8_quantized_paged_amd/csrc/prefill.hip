@@ -127,10 +127,10 @@ __device__ __forceinline__ int tile_key(int i) {
 // (S^T of tile t + 1, P' of tile t), one workgroup barrier, then phase 2 (P.V of tile
 // t, row sum and scaled scores).  The barrier of iteration t publishes K of tile t + 2
 // and V of tile t + 1.  Phase 1 issues the loads of K of tile t + 3 (its slot held K of
-// tile t, last read before the previous barrier) and of V of tile t + 2 (its slot held
-// V of tile t - 2, likewise), so each load has one and a half iterations to land, and
-// the operand reads of phase 2's first chunks are issued before the barrier.
-constexpr int kKSlots = 3;
+// tile t - 1, last read before the previous barrier) and of V of tile t + 2 (its slot
+// held V of tile t - 2, likewise), so each load has one and a half iterations to land,
+// and the operand reads of phase 2's first chunks are issued before the barrier.
+constexpr int kKSlots = 4;  // power-of-two rings: slot = tile index & 3
 constexpr int kVSlots = 4;
 constexpr int kFSlots = 2;  // per-wave factor blocks: tiles t and t + 1
 // Block-table entries are fetched into LDS by direct loads, kIdTiles tiles' worth at a
@@ -272,6 +272,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                                 a.window + 1)
                    : 0);
 
+  // tiles every row of the wave sees whole: no key below w_lo_max, none above w_hi_min,
+  // none past the sequence end
+  const int t_clean_lo = (w_lo_max + kTile - 1) / kTile;
+  const int t_clean_hi = min(w_hi_min + 1, L) / kTile - 1;
+
   // ---- direct loads -----------------------------------------------------------------
   auto issue_ids = [&](int c) {  // page ids of id chunk c, one per thread
     const int idx = min((t_first + kIdTiles * c) * kTilePages + tid, npages - 1);
@@ -350,9 +355,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // Slots past the sequence end were never written (any bytes, NaN included): zero
   // the V bytes of a tile that ends past it before anyone reads them (its scales are
   // masked where they are read).
+  const int t_partial = L % kTile ? L / kTile : -1;  // the tile the sequence ends in
   auto scrub_v = [&](int t, uint8_t* st) {
+    if (t != t_partial) return;
     const int valid = L - t * kTile;  // keys of the tile below the sequence end
-    if (valid >= kTile) return;
     for (int ch = tid; ch < LY::VT_CHUNKS; ch += kThreads) {
       const int keep = min(max(valid - (ch / D) * kPage, 0), kPage);  // tokens kept
       if (keep < kPage) {
@@ -500,7 +506,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // Masks the keys of tile t a row must not see (-inf); returns the lane's maximum.
   auto mask_max = [&](int t, float (&x)[32]) {
     const int kbase = t * kTile;
-    if ((kbase + kTile - 1 > w_hi_min) || (kbase < w_lo_max) || (kbase + kTile > L)) {
+    if (t < t_clean_lo || t > t_clean_hi) {
       // visible keys relative to this lane's first key: element (kb, r) is key
       // 32 kb + r of that range.  The empty asm keeps the per-key tests inside this
       // (rarely taken) branch instead of hoisted into every tile.
@@ -633,20 +639,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       for (int c = 0; c < QD; ++c)
         load_chunk(c, k_lds[1], v_lds[0], f_lds[wave][0], f_lds[wave][1], cq[c]);
     }
-    // every wave's reads of K of tile t_first done before K of tile t_first + 3 is
-    // loaded into its slot
-    publish();
 
-    int kr = 0;  // K slot of tile t: (t - t_first) % kKSlots
     PageOffs offs_v = page_offsets(tile_ids(t_first + 2));  // page offsets of tile t + 2
     int4 ids_k_raw = tile_ids_raw(t_first + 3);  // of tile t + 3, read one tile ahead
     for (int t = t_first; t <= t_last; ++t) {
       const int rel = t - t_first;
-      const int kr1 = kr == kKSlots - 1 ? 0 : kr + 1;
-      const int kr2 = kr1 == kKSlots - 1 ? 0 : kr1 + 1;
-      const uint8_t* kb1 = k_lds[kr1];            // K of tile t + 1
-      const uint8_t* kb2 = k_lds[kr2];            // K of tile t + 2 (published mid-way)
-      uint8_t* const kb3 = k_lds[kr];             // K of tile t + 3 goes here
+      const uint8_t* kb1 = k_lds[(rel + 1) & 3];  // K of tile t + 1
+      const uint8_t* kb2 = k_lds[(rel + 2) & 3];  // K of tile t + 2 (published mid-way)
+      uint8_t* const kb3 = k_lds[(rel + 3) & 3];  // K of tile t + 3 goes here
       const uint8_t* vb0 = v_lds[rel & 3];        // V of tile t
       uint8_t* const vb1 = v_lds[(rel + 1) & 3];  // V of tile t + 1 (published mid-way)
       uint8_t* const vb2 = v_lds[(rel + 2) & 3];  // V of tile t + 2 goes here
@@ -807,7 +807,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      kr = kr1;
       offs_v = offs_k;
     }
   };
