@@ -54,8 +54,9 @@ def parse():
                     help=f"comma-separated subset of {LEGS}; 'decode' is the headline")
     ap.add_argument("--cpu-seqs", type=int, default=8,
                     help="sequences in the oracle's timed sample (0 = skip)")
-    ap.add_argument("--cpu-reps", type=int, default=2,
-                    help="repetitions of the oracle's timed sample")
+    ap.add_argument("--cpu-reps", type=int, default=8,
+                    help="repetitions of the oracle's timed sample (about 1.4 s each on "
+                         "16 host cores: the default is ~11 s of CPU work)")
     ap.add_argument("--copy-calib", action="store_true",
                     help=f"also run a plain {COPY_BYTES >> 20} MiB device copy (counter "
                          "calibration for the HBM traffic figures)")
@@ -213,7 +214,8 @@ def cpu_baseline(case, nseq, reps=1):
             "kind": "oracle", "seconds": round(dt, 4), "blas_threads": blas,
             "sample": f"{nseq} of {B} sequences of one decode step (same inputs: new-token "
                       f"cache write, q quantisation, cache read, float64 attention), mean "
-                      f"of {reps} runs; value = their algorithmic bytes / oracle seconds"}
+                      f"of {reps} runs ({dt * reps:.1f} s of CPU work in all); value = their "
+                      f"algorithmic bytes / oracle seconds per run"}
 
 
 # ---- attention-only inter-token latency over context length ---------------------------------
