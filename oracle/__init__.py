@@ -9,6 +9,8 @@ computes, written from the pages' description of vLLM's FP8 KV cache:
                 block table, GQA, sliding window
   scales.py     host scale resolution (sentinels, single kv scale) and the
                 sliding-window skip policy
+  logits.py     float64 paged query-key logits per query head (a sparse-attention
+                indexer's scores), through a block table, GQA, per-row visibility
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  It shares no code with the device path
@@ -22,7 +24,9 @@ every finite code, an exhaustive sweep over all 65,536 bf16 patterns at several
 scales against torch's saturating cast, and every midpoint between neighbouring
 codes; scales by closed form and invariants; attention by equal keys, a dominant
 key, lossless grid values, GQA grouping, windows, page permutation, prefill/decode
-agreement and a brute-force pure-Python softmax.
+agreement and a brute-force pure-Python softmax; logits by pure-Python dot products
+over slot-addressed rows, one-hot queries (a lookup), constant key heads (GQA closed
+form), visibility counts, page permutation and bilinearity.
 
 Parity unpinned: nothing in this package.  (The effect of quantising softmax
 probabilities to e4m3 inside the device's prefill kernel is not modelled here; the

@@ -208,6 +208,57 @@ def make_prefill_case(seed: int, ctx_lens, new_lens, num_q_heads: int,
                        num_kv_heads, head_dim, window)
 
 
+@dataclass
+class LogitsCase:
+    """Inputs of one paged-logits call: query rows q [R][Hq][D] grouped by request
+    (cu_rows [B+1]), each row seeing the first row_lens[r] keys of its request's cache;
+    k, v, token_* and slots cover every cached token as in DecodeCase."""
+    name: str
+    q: np.ndarray
+    cu_rows: np.ndarray
+    row_lens: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    token_seq: np.ndarray
+    token_pos: np.ndarray
+    slots: np.ndarray
+    block_table: np.ndarray
+    seq_lens: np.ndarray
+    num_pages: int
+    num_kv_heads: int
+    head_dim: int
+
+
+def make_logits_case(seed: int, seq_lens, rows_per_req, num_q_heads: int,
+                     num_kv_heads: int, head_dim: int, table: str = "perm",
+                     causal_rows: bool = True, std: float = 1.0, extra_pages: int = 0,
+                     name: str = "logits") -> LogitsCase:
+    """Requests with seq_lens cached tokens and rows_per_req query rows each; with
+    causal_rows row i of request b sees seq_lens[b] - rows_per_req[b] + i + 1 keys (the
+    rows are the request's last tokens), else every row sees the whole cache."""
+    rng = np.random.default_rng(seed)
+    seq_lens = np.asarray(seq_lens, np.int32)
+    rows = np.asarray(rows_per_req, np.int64)
+    B = len(seq_lens)
+    R = int(rows.sum())
+    T = int(seq_lens.sum())
+    q = normal_bf16(rng, (R, num_q_heads, head_dim))
+    k = normal_bf16(rng, (T, num_kv_heads, head_dim), std)
+    v = normal_bf16(rng, (T, num_kv_heads, head_dim), std)
+    lens = []
+    for b in range(B):
+        for i in range(int(rows[b])):
+            L = int(seq_lens[b])
+            lens.append(max(0, L - int(rows[b]) + i + 1) if causal_rows else L)
+    pages_per_seq = max(1, -(-int(seq_lens.max()) // PAGE_SIZE)) if B else 1
+    num_pages = B * pages_per_seq + extra_pages
+    bt = make_block_table(rng, B, pages_per_seq, table, num_pages)
+    ts, tp, slots = token_layout(seq_lens, bt)
+    cu = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    return LogitsCase(name, q, cu, np.asarray(lens, np.int32), k, v, ts, tp, slots, bt,
+                      seq_lens, num_pages, num_kv_heads, head_dim)
+
+
 # --------------------------------------------------------------------------------
 # The five named workloads.
 # --------------------------------------------------------------------------------
