@@ -13,6 +13,7 @@ physical page block_table[b][j // 16] at offset j % 16):
 
     logits[r][h][j] = q[r][h] . k_j[g]      for j < row_lens[r]
     logits[r][h][j] = -inf                  for row_lens[r] <= j < out_len
+(only keys j < out_len are represented: a narrower output holds a prefix).
 
 Readings where the page is silent: the scores stay per query head (the page does not
 say how the indexer's heads are combined, so that reduction and the top-k rule are
@@ -42,12 +43,12 @@ def paged_logits(q, cu_rows, row_lens, k_pool, block_table, out_len: int) -> np.
         r0, r1 = int(cu_rows[b]), int(cu_rows[b + 1])
         if r1 <= r0:
             continue
-        n_keys = int(row_lens[r0:r1].max())
+        n_keys = min(int(row_lens[r0:r1].max()), out_len)  # only keys j < out_len exist
         if n_keys <= 0:
             continue
         k = np.asarray(gather(k_pool, block_table[b], n_keys), np.float64)  # [L][Hkv][D]
         for r in range(r0, r1):
-            n = int(row_lens[r])
+            n = min(int(row_lens[r]), out_len)
             for h in range(Hq):
                 out[r, h, :n] = k[:n, h // group, :] @ q[r, h]
     return out

@@ -136,6 +136,15 @@ def test_visibility():
     pin_visibility()
 
 
+def test_narrow_output_is_a_prefix():
+    """An output narrower than the visible keys holds the first out_len of them."""
+    case = small_case(seed=15)
+    kp = pools_of(case)
+    wide = logits.paged_logits(case.q, case.cu_rows, case.row_lens, kp, case.block_table, 48)
+    narrow = logits.paged_logits(case.q, case.cu_rows, case.row_lens, kp, case.block_table, 20)
+    assert np.array_equal(narrow, wide[:, :, :20])
+
+
 def test_page_permutation():
     pin_page_permutation(logits.paged_logits)
 
