@@ -40,7 +40,8 @@ DECODE_KERNEL = "decode_kernel"
 COPY_BYTES = 1 << 30
 SETTLE_S = 0.1               # untimed steps after the warmup, before each timed region
 LEGS = ("decode", "bf16", "tiny", "long", "hybrid", "prefill")
-EXTRA_LEGS = ("prefill_d128", "prefill_d64", "per_kv_head", "prefill_bf16_window")
+EXTRA_LEGS = ("prefill_d128", "prefill_d64", "per_kv_head", "prefill_bf16_window",
+              "paged_logits")
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix throughput, AMD published
 
 
@@ -809,6 +810,55 @@ def main():
             "us_per_step": round(us2, 2), "bytes": nb2,
             "GB_s": round(nb2 / (us2 * 1e-6) / 1e9, 1),
             "frac_hbm": round(nb2 / (us2 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del cs
+        torch.cuda.empty_cache()
+
+    if "paged_logits" in legs:
+        # sparse-attention indexer scores: 32 requests x 20,000 cached tokens, one query
+        # row each, 4 query heads on one key head, D 128, fp8 per-token-head cache (the
+        # indexer shape of the pages' test, at a serving batch and context)
+        B3, L3 = 32, 20000
+        lc = workloads.make_logits_case(109, [L3] * B3, [1] * B3, 4, 1, 128, table="perm",
+                                        name="paged logits")
+        cs = [kvq.PagedCache(lc.num_pages, 1, 128, "fp8", "per_token_head")
+              for _ in range(args.rotate)]
+        for i in range(0, len(lc.k), 65536):
+            sl_ = slice(i, i + 65536)
+            kk, vv = to_dev(lc.k[sl_]), to_dev(lc.v[sl_])
+            ss = torch.from_numpy(lc.slots[sl_].astype(np.int64)).to(dev)
+            for c in cs:
+                kvq.cache_write(c, kk, vv, ss)
+        lq = to_dev(lc.q)
+        lcu, lrl = torch.from_numpy(lc.cu_rows).to(dev), torch.from_numpy(lc.row_lens).to(dev)
+        lbt, lsl = (torch.from_numpy(lc.block_table).to(dev),
+                    torch.from_numpy(lc.seq_lens).to(dev))
+        lout = torch.empty((B3, 4, L3), dtype=torch.float32, device=dev)
+
+        def lstep(i):
+            kvq.paged_logits(cs[i % len(cs)], lq, lcu, lrl, lbt, lsl, L3, ones, out=lout)
+        for i in range(args.warmup):
+            lstep(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            lstep(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us3 = e0.elapsed_time(e1) * 1e3 / args.steps
+        # K codes and per-token scales read, float32 logits written (query and block
+        # table are < 0.3%)
+        nb3 = B3 * L3 * 128 + B3 * L3 * 4 + B3 * 4 * L3 * 4
+        result["paged_logits"] = {
+            "workload": "indexer logits: 32 requests x 20,000 cached tokens, 1 query row "
+                        "each, 4 query heads / 1 key head, D 128, fp8 per-token-head; "
+                        "float32 [32][4][20,000] out",
+            "us_per_launch": round(us3, 2), "bytes": nb3,
+            "GB_s": round(nb3 / (us3 * 1e-6) / 1e9, 1),
+            "frac_hbm": round(nb3 / (us3 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "timing": "HIP events around a burst of back-to-back launches over rotating "
+                      "cache copies"}
         del cs
         torch.cuda.empty_cache()
 

@@ -9,6 +9,6 @@ from .binding import (  # noqa: F401
     SKIP_SLIDING_WINDOW, WARN_UNCALIBRATED_Q_OR_PROB, CacheDesc, KvqError, PagedCache, Scales, abi_version,
     cache_write, decode_attention, decode_step, decode_workspace, decode_workspace_bytes,
     exported, header_functions,
-    last_error, layer_kv_dtype, prefill_attention, quantize_fp8, resolve_scales,
+    last_error, layer_kv_dtype, paged_logits, prefill_attention, quantize_fp8, resolve_scales,
     status_string,
 )

@@ -103,6 +103,8 @@ _SIGS = {
     "kvq_prefill_attention": (ctypes.c_int, [_PD, _p, _p, _i32, _i32, _p, _i32, _p,
                                              _i32, ctypes.POINTER(Scales), _i32, _i32,
                                              _f32, _p, ctypes.c_int, _p]),
+    "kvq_paged_logits": (ctypes.c_int, [_PD, _p, _p, _i32, _i32, _p, _p, _i32, _p,
+                                        ctypes.POINTER(Scales), _p, _i32, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     if hasattr(_lib, _name):
@@ -336,4 +338,23 @@ def prefill_attention(cache: PagedCache, q, cu_q_lens, block_table, seq_lens,
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_q_len,
         ctypes.byref(scales), int(causal), window, softmax_scale, _ptr(out),
         _DTYPES[out_dtype], _stream(stream, q.device)), "prefill_attention")
+    return out
+
+
+def paged_logits(cache: PagedCache, q, cu_rows, row_lens, block_table, seq_lens,
+                 out_len: int, scales: Scales | None = None, out=None, stream=None):
+    """Query-key logits per query head: q bf16 [R][Hq][D]; cu_rows int32 [B+1];
+    row_lens int32 [R]; seq_lens int32 [B] -> float32 [R][Hq][out_len] (out_len a
+    multiple of 4), -inf past each row's visible length."""
+    torch = _torch()
+    R, Hq, D = q.shape
+    if scales is None:
+        scales = Scales(1.0, 1.0, 1.0, 1.0)
+    if out is None:
+        out = torch.empty((R, Hq, out_len), dtype=torch.float32, device=q.device)
+    d = cache.desc()
+    _check(_lib.kvq_paged_logits(
+        ctypes.byref(d), _ptr(q), _ptr(cu_rows), int(seq_lens.numel()), Hq, _ptr(row_lens),
+        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), ctypes.byref(scales),
+        _ptr(out), out.shape[2], _stream(stream, q.device)), "paged_logits")
     return out

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvq.so")
 ARCH = "gfx950"
 
-SOURCES = ["host.cpp", "cache_write.hip", "decode.hip", "prefill.hip", "prefill_bf16.hip"]
+SOURCES = ["host.cpp", "cache_write.hip", "decode.hip", "prefill.hip", "prefill_bf16.hip",
+           "logits.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -1,0 +1,296 @@
+// Paged query-key logits for a sparse-attention indexer: every cache token a query
+// row may see, scored against each of the row's query heads, from an FP8 (e4m3) or
+// bf16 paged cache ("vLLM Qwen3.8-Flash-Next: QSA Indexer ... FP8 support", section on
+// the reference test of the decode/prefill selection: the top-k selection reads
+// these scores, and with FP8 the scores are compared value by value, exact float32
+// accumulation expected).
+//
+// Arithmetic.  FP8 cache: the query is quantised to e4m3 with q_scale (as in
+// attention); codes are widened to f16 (exact: every e4m3 value is an f16 value) and
+// S^T = K . Q^T runs on v_mfma_f32_32x32x16_f16: exact products, float32 sums; the
+// result is scaled by q_scale * k_scale_j.  bf16 cache: q and k as bf16 on
+// v_mfma_f32_32x32x16_bf16 (exact products, float32 sums), unscaled.
+//
+// Work split.  A workgroup owns one (request, KV head) and kIters consecutive 128-key
+// tiles (each of its 4 waves 32 keys of a tile, one 32-key MFMA block); the request's
+// query rows times the group's query heads ("pairs") are the MFMA columns, 32 at a
+// time, staged once per chunk in LDS.  The tiles are software-pipelined: page ids two
+// tiles ahead and key rows one tile ahead are in flight while a tile is computed, so
+// the block-table -> key -> store chain of dependent memory round trips is paid once
+// per workgroup rather than once per tile.  The contraction index is assigned so that lane group hg (lanes
+// 32 hg ..) holds the contiguous half D/2 hg .. D/2 hg + D/2 - 1 of every key and
+// query row: step s, element e <-> dim D/2 hg + 8 s + e (both operands agree, which
+// is all a contraction needs), so each lane's operands are plain 16-byte loads.
+#include "kvq_device.h"
+#include "kvq_host.h"
+
+namespace kvq {
+namespace lg {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kTileKeys = kWaves * 32;  // keys per tile (32 per wave)
+constexpr int kIters = 4;               // tiles per workgroup
+
+struct LogitsArgs {
+  const uint16_t* q;          // bf16 [rows][Hq][D]
+  const int32_t* cu_rows;     // [B + 1]
+  const int32_t* row_lens;    // [rows]
+  const int32_t* seq_lens;    // [B]
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const uint8_t* k_pages;     // [P][Hkv][16][D] codes or bf16
+  const float* k_scales;      // per-token-head [P][Hkv][16], per-KV-head [Hkv], or null
+  int32_t num_kv_heads, num_q_heads, groups;  // groups: workgroups per (request, head)
+  float q_scale, k_scale;     // k_scale: per-tensor
+  float* out;                 // [rows][Hq][out_stride]
+  int32_t out_stride;
+};
+
+// 8 e4m3 codes (two words, byte order = element order) as 8 f16 values
+__device__ __forceinline__ half8_t codes_to_f16(uint32_t lo, uint32_t hi) {
+  const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return (half8_t){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// kMode: 0 per-tensor, 1 per-token-head, 2 per-KV-head (FP8 only)
+template <int D, bool kFp8, int kMode>
+__global__ __launch_bounds__(kThreads) void logits_kernel(const LogitsArgs a) {
+  constexpr int ES = kFp8 ? 1 : 2;       // bytes per element
+  constexpr int HB = D / 2 * ES;         // bytes of a lane group's half row
+  constexpr int NV = HB / 16;            // 16-byte loads per half row
+  constexpr int NS = D / 16;             // MFMA steps over D
+  constexpr int QS = D * ES + 16;        // LDS stride of a pair's query row (padded)
+  __shared__ __align__(16) uint8_t q_lds[32 * QS];
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  const int lane = (int)threadIdx.x % kWave;
+  const int col = lane % 32, hg = lane / 32;
+  const int H = a.num_kv_heads;
+  const int g = (int)(blockIdx.x % (unsigned)H);
+  const int rest = (int)(blockIdx.x / (unsigned)H);
+  const int grp0 = rest % a.groups;
+  const int b = rest / a.groups;
+  const int G = a.num_q_heads / H;
+  const int r0 = a.cu_rows[b];
+  const int npairs = (a.cu_rows[b + 1] - r0) * G;
+  if (npairs <= 0) return;               // whole workgroup: no barrier is skipped
+  const int L = a.seq_lens[b];
+  const int npages = (L + kPage - 1) / kPage;
+  const int* bt = a.block_table + (int64_t)b * a.bt_stride;
+  const int key_base = grp0 * kIters * kTileKeys + wave * 32;  // wave's key of tile 0
+
+  // per-tile loads of this wave: the page ids of its 2 pages (lanes 0 and 1), then its
+  // lane's half row of key key_base + 128 it + col and the scales of its output keys
+  // (keys 8 q + 4 hg + e of the block, register 4 q + e: 4 consecutive keys, one page)
+  struct Tile {
+    uint4 k[NV];
+    float4 sc[4];
+  };
+  auto page_id = [&](int it) {
+    const int kw = key_base + it * kTileKeys;
+    int pid = 0;
+    if (kw < a.out_stride && npages > 0) pid = bt[min(kw / kPage + (lane & 1), npages - 1)];
+    return pid;
+  };
+  auto load_tile = [&](int it, int pid, Tile& t) {
+    const int kw = key_base + it * kTileKeys;
+    const int pg[2] = {__builtin_amdgcn_readlane(pid, 0), __builtin_amdgcn_readlane(pid, 1)};
+    const int key = kw + col;
+    if (kw < a.out_stride && key < L) {
+      const int page = col < 16 ? pg[0] : pg[1];
+      const uint8_t* row = a.k_pages + ((((int64_t)page * H + g) * kPage + key % kPage) * D) * ES;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) t.k[v] = *reinterpret_cast<const uint4*>(row + HB * hg + 16 * v);
+    } else {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) t.k[v] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int k0 = kw + 8 * q4 + 4 * hg;
+      t.sc[q4] = make_float4(a.k_scale, a.k_scale, a.k_scale, a.k_scale);
+      if constexpr (kFp8 && kMode == 1) {
+        if (kw < a.out_stride && k0 < L)  // slots past L hold unwritten scales: masked
+          t.sc[q4] = *reinterpret_cast<const float4*>(
+              a.k_scales + ((int64_t)pg[q4 / 2] * H + g) * kPage + k0 % kPage);
+      } else if constexpr (kFp8 && kMode == 2) {
+        const float hs = a.k_scales[g];
+        t.sc[q4] = make_float4(hs, hs, hs, hs);
+      }
+    }
+  };
+
+  const bool unit_q = a.q_scale == 1.0f;
+  for (int p0 = 0; p0 < npairs; p0 += 32) {
+    // ---- the chunk's query rows into LDS (e4m3 codes for an FP8 cache, else bf16) ---
+    __syncthreads();  // the previous chunk's operand reads are done
+    for (int i = (int)threadIdx.x; i < 32 * (D / 8); i += kThreads) {
+      const int pp = i / (D / 8), c8 = i % (D / 8);  // pair, 8-element chunk
+      const int p = p0 + pp;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (p < npairs)
+        w = *reinterpret_cast<const uint4*>(
+            a.q + ((int64_t)(r0 + p / G) * a.num_q_heads + g * G + p % G) * D + 8 * c8);
+      if constexpr (kFp8) {
+        const uint32_t xs[4] = {w.x, w.y, w.z, w.w};
+        uint32_t c[2] = {0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = bf16_bits_to_float((xs[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+          const uint32_t code = unit_q ? e4m3_encode(x) : e4m3_quantize(x, a.q_scale);
+          c[e / 4] |= code << (8 * (e % 4));
+        }
+        *reinterpret_cast<uint2*>(q_lds + pp * QS + 8 * c8) = make_uint2(c[0], c[1]);
+      } else {
+        *reinterpret_cast<uint4*>(q_lds + pp * QS + 16 * c8) = w;
+      }
+    }
+    const int p = p0 + col;
+    const bool pair_ok = p < npairs;
+    const int pr = r0 + (pair_ok ? p / G : 0), ph = g * G + (pair_ok ? p % G : 0);
+    const int vis = pair_ok ? min(a.row_lens[pr], L) : 0;
+    float* orow = a.out + ((int64_t)pr * a.num_q_heads + ph) * a.out_stride;
+    int pid_next = page_id(0);
+    Tile cur;
+    load_tile(0, pid_next, cur);
+    pid_next = page_id(1);
+    __syncthreads();
+    // B operand of this lane (pair col): its half row, kept for all tiles
+    const uint8_t* qrow = q_lds + col * QS + HB * hg;
+    for (int it = 0; it < kIters; ++it) {
+      const int kw = key_base + it * kTileKeys;
+      if (kw >= a.out_stride) break;  // wave-uniform; later tiles start further on
+      Tile nxt;
+      if (it + 1 < kIters) {
+        load_tile(it + 1, pid_next, nxt);
+        pid_next = page_id(it + 2);
+      }
+      v16f acc = (v16f){};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if constexpr (kFp8) {
+          const uint2 qc = *reinterpret_cast<const uint2*>(qrow + 8 * s);
+          const uint4 kv = cur.k[s / 2];  // key bytes 8 s .. 8 s + 7 of the half row
+          const half8_t ka = (s & 1) ? codes_to_f16(kv.z, kv.w) : codes_to_f16(kv.x, kv.y);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, codes_to_f16(qc.x, qc.y), acc, 0, 0, 0);
+        } else {
+          const bf16x8_t qb =
+              __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + 16 * s));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur.k[s]),
+                                                        qb, acc, 0, 0, 0);
+        }
+      }
+      // ---- scale, mask (keys past the row's visible length -> -inf), store ---------
+      if (pair_ok) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int k0 = kw + 8 * q4 + 4 * hg;
+          if (k0 >= a.out_stride) continue;  // out_stride % 4 == 0: all 4 or none
+          const float sc[4] = {cur.sc[q4].x, cur.sc[q4].y, cur.sc[q4].z, cur.sc[q4].w};
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = k0 + e < vis ? acc[4 * q4 + e] * (kFp8 ? sc[e] * a.q_scale : 1.0f)
+                                : -INFINITY;
+          *reinterpret_cast<float4*>(orow + k0) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+      if (it + 1 < kIters) cur = nxt;
+    }
+  }
+}
+
+template <int D, bool kFp8>
+static void launch_mode(int mode, const LogitsArgs& args, unsigned blocks, hipStream_t st) {
+  if (!kFp8)
+    logits_kernel<D, false, 0><<<blocks, kThreads, 0, st>>>(args);
+  else if (mode == KVQ_SCALE_PER_TOKEN_HEAD)
+    logits_kernel<D, true, 1><<<blocks, kThreads, 0, st>>>(args);
+  else if (mode == KVQ_SCALE_PER_KV_HEAD)
+    logits_kernel<D, true, 2><<<blocks, kThreads, 0, st>>>(args);
+  else
+    logits_kernel<D, true, 0><<<blocks, kThreads, 0, st>>>(args);
+}
+
+template <int D>
+static void launch_dtype(const kvq_cache_desc* c, const LogitsArgs& args, unsigned blocks,
+                         hipStream_t st) {
+  if (c->dtype == KVQ_FP8_E4M3) launch_mode<D, true>(c->mode, args, blocks, st);
+  else launch_mode<D, false>(c->mode, args, blocks, st);
+}
+
+}  // namespace lg
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" kvq_status kvq_paged_logits(const kvq_cache_desc* cache, const void* q,
+                                       const int32_t* cu_rows, int32_t num_seqs,
+                                       int32_t num_q_heads, const int32_t* row_lens,
+                                       const int32_t* block_table, int32_t block_table_stride,
+                                       const int32_t* seq_lens, const kvq_scales* scales,
+                                       float* out, int32_t out_stride, void* stream) {
+  clear_error();
+  if (kvq_status s = check_cache(cache)) return s;
+  if (num_seqs < 0 || num_q_heads <= 0 || out_stride < 0)
+    return fail(KVQ_ERR_INVALID_ARG, "num_seqs %d num_q_heads %d out_stride %d", num_seqs,
+                num_q_heads, out_stride);
+  if (num_q_heads % cache->num_kv_heads)
+    return fail(KVQ_ERR_INVALID_ARG, "num_q_heads %d not a multiple of num_kv_heads %d",
+                num_q_heads, cache->num_kv_heads);
+  if (num_seqs == 0 || out_stride == 0) return KVQ_OK;
+  if (out_stride % 4)
+    return fail(KVQ_ERR_INVALID_ARG, "out_stride %d is not a multiple of 4", out_stride);
+  if (!q || !out || !cu_rows || !row_lens || !seq_lens || !block_table)
+    return fail(KVQ_ERR_INVALID_ARG, "q, out, cu_rows, row_lens, seq_lens or block_table is NULL");
+  if (((uintptr_t)q | (uintptr_t)out) & 15u)
+    return fail(KVQ_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (block_table_stride <= 0) return fail(KVQ_ERR_INVALID_ARG, "block_table_stride <= 0");
+  if (cache->dtype == KVQ_FP8_E4M3 && cache->mode == KVQ_SCALE_PER_TOKEN_HEAD &&
+      ((uintptr_t)cache->k_scales & 15u))
+    return fail(KVQ_ERR_INVALID_ARG, "k_scales must be 16-byte aligned");
+  lg::LogitsArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.cu_rows = cu_rows;
+  a.row_lens = row_lens;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.bt_stride = block_table_stride;
+  a.k_pages = static_cast<const uint8_t*>(cache->k_pages);
+  a.k_scales = cache->k_scales;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.groups = (out_stride + lg::kTileKeys * lg::kIters - 1) / (lg::kTileKeys * lg::kIters);
+  a.q_scale = 1.0f;
+  a.k_scale = 1.0f;
+  if (cache->dtype == KVQ_FP8_E4M3) {
+    if (!scales) return fail(KVQ_ERR_INVALID_ARG, "scales is NULL");
+    if (!(scales->q_scale > 0.0f))
+      return fail(KVQ_ERR_INVALID_ARG, "q_scale must be > 0");
+    if (cache->mode == KVQ_SCALE_PER_TENSOR && !(scales->k_scale > 0.0f))
+      return fail(KVQ_ERR_INVALID_ARG, "k_scale must be > 0");
+    a.q_scale = scales->q_scale;
+    a.k_scale = cache->mode == KVQ_SCALE_PER_TENSOR ? scales->k_scale : 1.0f;
+  }
+  a.out = out;
+  a.out_stride = out_stride;
+  const int64_t blocks = (int64_t)num_seqs * cache->num_kv_heads * a.groups;
+  if (blocks > 0x7FFFFFFF) return fail(KVQ_ERR_INVALID_ARG, "grid too large");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (cache->head_dim) {
+    case 64: lg::launch_dtype<64>(cache, a, (unsigned)blocks, st); break;
+    case 128: lg::launch_dtype<128>(cache, a, (unsigned)blocks, st); break;
+    case 256: lg::launch_dtype<256>(cache, a, (unsigned)blocks, st); break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "logits launch: %s", hipGetErrorString(e));
+  return KVQ_OK;
+}

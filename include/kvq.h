@@ -306,6 +306,37 @@ kvq_status kvq_prefill_attention(const kvq_cache_desc* cache, const void* q,
                                  int32_t causal, int32_t window, float softmax_scale,
                                  void* out, kvq_dtype out_dtype, void* stream);
 
+/*
+ * Paged query-key logits for a sparse-attention indexer ("vLLM Qwen3.8-Flash-Next: QSA
+ * Indexer ... FP8 support", section on the reference test of the decode/prefill
+ * selection: the indexer's top-k selection reads these scores from an FP8 or bf16
+ * paged cache, and FP8 scores are compared value by value).
+ *
+ * Request b owns query rows cu_rows[b] .. cu_rows[b+1]-1; row r sees the first
+ * min(row_lens[r], seq_lens[b]) keys of request b's cache (keys through the block
+ * table as in kvq_decode_attention).  For query head h (key head g = h / (Hq/Hkv)):
+ *   out[r][h][j] = (q codes . k codes) * q_scale * k_scale_j   (FP8 cache: q quantised
+ *                  to e4m3 with scales->q_scale; k_scale_j as in attention: per-token-
+ *                  head, cache->k_scales[g] per-KV-head, or scales->k_scale per-tensor)
+ *   out[r][h][j] = q . k_j                                     (bf16 cache, unscaled)
+ * for visible j, and -inf for the other j < out_stride.  Products are exact and sums
+ * float32 (e4m3 and bf16 values widened for the matrix cores); no softmax scale and
+ * no reduction over heads (the selection rule is the caller's).
+ * q [device] bf16 [total_rows][num_q_heads][D], 16-byte aligned; cu_rows [device]
+ * int32 [num_seqs+1]; row_lens [device] int32 [total_rows]; seq_lens [device] int32
+ * [num_seqs]; out [device] float32 [total_rows][num_q_heads][out_stride], 16-byte
+ * aligned, out_stride a multiple of 4; every entry is written.  Only the K pool (and
+ * K scales) of the cache is read.  Errors: INVALID_ARG for NULL pointers, misaligned
+ * q/out (16 bytes) or per-token-head k_scales (16 bytes), out_stride not a multiple of
+ * 4, Hq not a multiple of Hkv; HIP for a failed launch.  Supported: fp8 or bf16 cache,
+ * D in {64,128,256}, any group size.
+ */
+kvq_status kvq_paged_logits(const kvq_cache_desc* cache, const void* q, const int32_t* cu_rows,
+                            int32_t num_seqs, int32_t num_q_heads, const int32_t* row_lens,
+                            const int32_t* block_table, int32_t block_table_stride,
+                            const int32_t* seq_lens, const kvq_scales* scales, float* out,
+                            int32_t out_stride, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
