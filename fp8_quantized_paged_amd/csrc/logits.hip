@@ -11,8 +11,8 @@
 // result is scaled by q_scale * k_scale_j.  bf16 cache: q and k as bf16 on
 // v_mfma_f32_32x32x16_bf16 (exact products, float32 sums), unscaled.
 //
-// Work split.  A workgroup owns one (request, KV head) and kIters consecutive 128-key
-// tiles (each of its 4 waves 32 keys of a tile, one 32-key MFMA block); the request's
+// Work split.  A workgroup owns one (request, KV head) and `iters` consecutive 128-key
+// tiles (1 to 8, chosen so that the launch has some 640 workgroups) (each of its 4 waves 32 keys of a tile, one 32-key MFMA block); the request's
 // query rows times the group's query heads ("pairs") are the MFMA columns, 32 at a
 // time, staged once per chunk in LDS.  The tiles are software-pipelined: page ids two
 // tiles ahead and key rows one tile ahead are in flight while a tile is computed, so
@@ -21,6 +21,8 @@
 // 32 hg ..) holds the contiguous half D/2 hg .. D/2 hg + D/2 - 1 of every key and
 // query row: step s, element e <-> dim D/2 hg + 8 s + e (both operands agree, which
 // is all a contraction needs), so each lane's operands are plain 16-byte loads.
+#include <algorithm>
+
 #include "kvq_device.h"
 #include "kvq_host.h"
 
@@ -35,7 +37,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTileKeys = kWaves * 32;  // keys per tile (32 per wave)
-constexpr int kIters = 4;               // tiles per workgroup
+constexpr int kMaxIters = 8;            // tiles per workgroup, at most
+constexpr int kTargetGroups = 640;      // workgroups a launch aims for
 
 struct LogitsArgs {
   const uint16_t* q;          // bf16 [rows][Hq][D]
@@ -46,7 +49,8 @@ struct LogitsArgs {
   int32_t bt_stride;
   const uint8_t* k_pages;     // [P][Hkv][16][D] codes or bf16
   const float* k_scales;      // per-token-head [P][Hkv][16], per-KV-head [Hkv], or null
-  int32_t num_kv_heads, num_q_heads, groups;  // groups: workgroups per (request, head)
+  int32_t num_kv_heads, num_q_heads;
+  int32_t groups, iters;      // workgroups per (request, head), tiles per workgroup
   float q_scale, k_scale;     // k_scale: per-tensor
   float* out;                 // [rows][Hq][out_stride]
   int32_t out_stride;
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const LogitsArgs a) {
   const int L = a.seq_lens[b];
   const int npages = (L + kPage - 1) / kPage;
   const int* bt = a.block_table + (int64_t)b * a.bt_stride;
-  const int key_base = grp0 * kIters * kTileKeys + wave * 32;  // wave's key of tile 0
+  const int key_base = grp0 * a.iters * kTileKeys + wave * 32;  // wave's key of tile 0
 
   // per-tile loads of this wave: the page ids of its 2 pages (lanes 0 and 1), then its
   // lane's half row of key key_base + 128 it + col and the scales of its output keys
@@ -139,7 +143,10 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const LogitsArgs a) {
       if (p < npairs)
         w = *reinterpret_cast<const uint4*>(
             a.q + ((int64_t)(r0 + p / G) * a.num_q_heads + g * G + p % G) * D + 8 * c8);
-      if constexpr (kFp8) {
+      if (p >= npairs) {  // columns without a pair: zero operands, nothing to encode
+        if constexpr (kFp8) *reinterpret_cast<uint2*>(q_lds + pp * QS + 8 * c8) = make_uint2(0, 0);
+        else *reinterpret_cast<uint4*>(q_lds + pp * QS + 16 * c8) = w;
+      } else if constexpr (kFp8) {
         const uint32_t xs[4] = {w.x, w.y, w.z, w.w};
         uint32_t c[2] = {0, 0};
 #pragma unroll
@@ -165,11 +172,11 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const LogitsArgs a) {
     __syncthreads();
     // B operand of this lane (pair col): its half row, kept for all tiles
     const uint8_t* qrow = q_lds + col * QS + HB * hg;
-    for (int it = 0; it < kIters; ++it) {
+    for (int it = 0; it < a.iters; ++it) {
       const int kw = key_base + it * kTileKeys;
       if (kw >= a.out_stride) break;  // wave-uniform; later tiles start further on
       Tile nxt;
-      if (it + 1 < kIters) {
+      if (it + 1 < a.iters) {
         load_tile(it + 1, pid_next, nxt);
         pid_next = page_id(it + 2);
       }
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const LogitsArgs a) {
           *reinterpret_cast<float4*>(orow + k0) = make_float4(v[0], v[1], v[2], v[3]);
         }
       }
-      if (it + 1 < kIters) cur = nxt;
+      if (it + 1 < a.iters) cur = nxt;
     }
   }
 }
@@ -268,7 +275,13 @@ extern "C" kvq_status kvq_paged_logits(const kvq_cache_desc* cache, const void* 
   a.k_scales = cache->k_scales;
   a.num_kv_heads = cache->num_kv_heads;
   a.num_q_heads = num_q_heads;
-  a.groups = (out_stride + lg::kTileKeys * lg::kIters - 1) / (lg::kTileKeys * lg::kIters);
+  {
+    const int64_t tiles = (out_stride + lg::kTileKeys - 1) / lg::kTileKeys;
+    const int64_t total = (int64_t)num_seqs * cache->num_kv_heads * tiles;
+    a.iters = (int)std::min<int64_t>(lg::kMaxIters, std::max<int64_t>(
+        1, (total + lg::kTargetGroups - 1) / lg::kTargetGroups));
+    a.groups = (int)((tiles + a.iters - 1) / a.iters);
+  }
   a.q_scale = 1.0f;
   a.k_scale = 1.0f;
   if (cache->dtype == KVQ_FP8_E4M3) {
