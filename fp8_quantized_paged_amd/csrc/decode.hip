@@ -1145,6 +1145,10 @@ static int max_visible_pages(int32_t max_seq_len, int32_t window) {
 static int auto_pages_per_split(int32_t num_seqs, int32_t num_kv_heads, int max_pages) {
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
   if (units <= 0 || max_pages <= 0) return 2 * kWaves;
+  // a unit of at most four pages per wave (a sliding window, a short sequence) is one
+  // split: extra splits would add the merge's round trips to a latency-bound launch
+  // (gpt-oss-shaped window-128 layer, 9 pages: 2 splits -> 1)
+  if (max_pages <= 4 * kWaves) return max_pages;
   int64_t splits = (kTargetWorkgroups + units - 1) / units;
   if (splits > kMaxAutoSplits) splits = kMaxAutoSplits;
   if (splits < 1) splits = 1;
