@@ -576,12 +576,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int WQ = 8 / NQK;          // P' words per phase-1 chunk
     constexpr int WV = 8 / DB;           // row-sum words / score groups per phase-2 chunk
     constexpr int NCH = NQK + DB;
-    constexpr int QD = 2;                // queue depth (chunks read ahead)
+    // queue depth (chunks read ahead): an LDS read batch takes ~300 cycles to return
+    // under this load, more than two chunks cover; head_dim 256 has the registers for a
+    // deeper queue (8,192 new on 32,768, per-token-head: depth 2 1755 us, 4 1627 us)
+    constexpr int QD = D == 256 ? 4 : 2;
     // head_dim 256 has the registers to carry the queue over the loop's back edge, so
     // the next tile's first operand reads are issued at the end of this one (others
     // issue them at the top of the iteration)
     constexpr bool kCrossQueue = D == 256;
     static_assert(QD <= NQK && QD <= DB, "queue depth");
+    // across the back edge chunk c of the next tile is read from the slot it was loaded
+    // into, (c + NCH - QD) % QD, as c % QD: equal only when QD divides NCH
+    static_assert(NCH % QD == 0, "queue depth must divide the chunk count");
     // the loads in phase-1 chunks 1 .. NQK - 1 (chunk 0 would wait for the page-id
     // read), LPC per chunk: K of tile t + 3, then V of tile t + 2
     constexpr int NLD = PER_K + PER_V;
