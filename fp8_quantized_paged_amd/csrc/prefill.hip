@@ -724,8 +724,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       // (chunks NQK ..): O^T += V^T . P'^T on the matrix cores; the row sum of the
       // rounded P' and the scaled scores of tile t + 1 (past the last tile: unused) on
       // the vector unit.  Each chunk holds one MFMA and a share of the vector work;
-      // scheduling barriers keep the matrix work, exponentials and loads in chunk
-      // order, so the matrix cores, the vector unit and the LDS overlap.
+      // scheduling barriers keep the matrix work and the loads in chunk order, so the
+      // matrix cores, the vector unit and the LDS overlap.
       v16f sn[2] = {(v16f){}, (v16f){}};
       v8i pb;
       const float msafe = m == -INFINITY ? 0.0f : m;
@@ -809,12 +809,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[4 * w + e] = fmaf(sn[kb][4 * q4 + e], cc[e], -msafe);
           }
-          asm volatile("" : "+v"(lam));  // keeps the row sum in this chunk
         }
-        // chunk boundary: MFMAs, exponentials and global loads stay in chunk order;
-        // other vector, scalar and LDS instructions may cross it (8,192 new on 32,768,
-        // head_dim 256: per-token-head 1797 -> 1658 us, per-tensor 1499 -> 1292 us)
-        __builtin_amdgcn_sched_barrier(0x0002 | 0x0004 | 0x0080 | 0x0100 | 0x0200);
+        // chunk boundary: MFMAs and global loads stay in chunk order; vector (the
+        // exponentials included), scalar and LDS instructions may cross it (8,192 new on
+        // 32,768, head_dim 256, one box: per-token-head 1821 -> 1642 us against a full
+        // barrier at every boundary)
+        __builtin_amdgcn_sched_barrier(0x0002 | 0x0004 | 0x0080 | 0x0100 | 0x0200 | 0x0400);
       }
       offs_v = offs_k;
     }
