@@ -576,10 +576,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int WQ = 8 / NQK;          // P' words per phase-1 chunk
     constexpr int WV = 8 / DB;           // row-sum words / score groups per phase-2 chunk
     constexpr int NCH = NQK + DB;
-    // queue depth (chunks read ahead): an LDS read batch takes ~300 cycles to return
-    // under this load, more than two chunks cover; head_dim 256 has the registers for a
-    // deeper queue (8,192 new on 32,768, per-token-head: depth 2 1755 us, 4 1627 us)
-    constexpr int QD = D == 256 ? 4 : 2;
+    // queue depth (chunks read ahead): two.  With MFMAs free to move across chunk
+    // boundaries (below) the scheduler hoists the reads itself; a depth of 4 then only
+    // costs registers (8,192 new on 32,768, head_dim 256, per-token-head, one box:
+    // depth 4 1680 us, depth 2 1604 us)
+    constexpr int QD = 2;
     // head_dim 256 has the registers to carry the queue over the loop's back edge, so
     // the next tile's first operand reads are issued at the end of this one (others
     // issue them at the top of the iteration)
@@ -787,8 +788,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
           const int db = c - NQK;
           o[db] = mfma(cur.op, pb, o[db]);
           // keep the accumulator in AGPRs across iterations: the (rare) rescale then
-          // copies it out and back, instead of every iteration copying it to VGPRs
-          asm volatile("" : "+a"(o[db]));
+          // copies it out and back, instead of every iteration copying it to VGPRs.
+          // head_dim 256 leaves the choice to the register allocator: pinned, it holds
+          // back the MFMAs the scheduler would move (1662 -> 1604 us, same case)
+          if constexpr (D != 256) asm volatile("" : "+a"(o[db]));
 #pragma unroll
           for (int u = 0; u < WV; ++u) {
             const int w = WV * db + u;
@@ -810,11 +813,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
             for (int e = 0; e < 4; ++e) x[4 * w + e] = fmaf(sn[kb][4 * q4 + e], cc[e], -msafe);
           }
         }
-        // chunk boundary: MFMAs and global loads stay in chunk order; vector (the
+        // chunk boundary: global loads stay in chunk order; MFMAs, vector (the
         // exponentials included), scalar and LDS instructions may cross it (8,192 new on
-        // 32,768, head_dim 256, one box: per-token-head 1821 -> 1642 us against a full
-        // barrier at every boundary)
-        __builtin_amdgcn_sched_barrier(0x0002 | 0x0004 | 0x0080 | 0x0100 | 0x0200 | 0x0400);
+        // 32,768, head_dim 256, one box: per-token-head 1808 us with a full barrier at
+        // every boundary, 1604 us so; head_dim 64 per-tensor 2642 -> 2341 us)
+        __builtin_amdgcn_sched_barrier(0x0002 | 0x0004 | 0x0008 | 0x0080 | 0x0100 | 0x0200 |
+                                       0x0400);
       }
       offs_v = offs_k;
     }
