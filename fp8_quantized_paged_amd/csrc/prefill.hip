@@ -577,9 +577,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int WV = 8 / DB;           // row-sum words / score groups per phase-2 chunk
     constexpr int NCH = NQK + DB;
     // queue depth (chunks read ahead): two.  With MFMAs free to move across chunk
-    // boundaries (below) the scheduler hoists the reads itself; a depth of 4 then only
-    // costs registers (8,192 new on 32,768, head_dim 256, per-token-head, one box:
-    // depth 4 1680 us, depth 2 1604 us)
+    // boundaries (below) the scheduler hoists the reads itself; a depth of four measured
+    // the same (within 1%, builds timed round-robin) and costs registers
     constexpr int QD = 2;
     // head_dim 256 has the registers to carry the queue over the loop's back edge, so
     // the next tile's first operand reads are issued at the end of this one (others
@@ -789,8 +788,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
           o[db] = mfma(cur.op, pb, o[db]);
           // keep the accumulator in AGPRs across iterations: the (rare) rescale then
           // copies it out and back, instead of every iteration copying it to VGPRs.
-          // head_dim 256 leaves the choice to the register allocator: pinned, it holds
-          // back the MFMAs the scheduler would move (1662 -> 1604 us, same case)
+          // head_dim 256 leaves the choice to the register allocator, which has the
+          // registers to spare (pinned or not measured the same)
           if constexpr (D != 256) asm volatile("" : "+a"(o[db]));
 #pragma unroll
           for (int u = 0; u < WV; ++u) {
@@ -815,8 +814,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         }
         // chunk boundary: global loads stay in chunk order; MFMAs, vector (the
         // exponentials included), scalar and LDS instructions may cross it (8,192 new on
-        // 32,768, head_dim 256, one box: per-token-head 1808 us with a full barrier at
-        // every boundary, 1604 us so; head_dim 64 per-tensor 2642 -> 2341 us)
+        // 32,768, builds timed round-robin on one box, against a full barrier at every
+        // boundary: head_dim 256 per-tensor 1441 -> 1270 us, head_dim 64 3-4%, head_dim
+        // 256 per-token-head unchanged at ~1520 us)
         __builtin_amdgcn_sched_barrier(0x0002 | 0x0004 | 0x0008 | 0x0080 | 0x0100 | 0x0200 |
                                        0x0400);
       }
