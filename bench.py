@@ -715,6 +715,17 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
                          "kernel": "prefill_kernel"}}
+        # the two-level ablation: the same launch with level 2 as an explicit float32
+        # VALU flush per 64-key chunk instead of the MFMA's chained C operand
+        us_v = timer.run(lambda i: kvq.prefill_attention(c, pq, pcu, pbt, psl, n_new, ones,
+                                                         out=out, accumulation="valu_add"),
+                         10, 3, warm_ms=200.0)
+        tf_v = fl / (float(np.mean(us_v)) * 1e-6) / 1e12
+        result["prefill_hd256_valu_add"] = {
+            "workload": "the same prefill, level-2 accumulation as float32 VALU adds of a "
+                        "zeroed accumulator per 64-key chunk (kvq_prefill_attention_accum)",
+            **stats(us_v), "frac_fp8_peak": round(tf_v / FP8_PEAK_TFLOPS, 4),
+            "time_vs_mfma_chain": round(float(np.mean(us_v)) / float(np.mean(us)), 3)}
         del c
         torch.cuda.empty_cache()
 

@@ -29,6 +29,23 @@ except OSError as e:  # pragma: no cover - depends on the machine
     raise ImportError(f"cannot load {LIB_PATH}: {e}") from e
 
 
+def _stale_check() -> None:
+    """Refuse a library built from other sources than the tree's (a stale build)."""
+    from .build import source_hash
+    try:
+        built = ctypes.string_at(ctypes.addressof(
+            ctypes.c_char.in_dll(_lib, "kvq_build_source_hash"))).decode()
+    except ValueError:
+        built = "(no source hash recorded)"
+    want = source_hash()
+    if built != want:
+        raise ImportError(f"{LIB_PATH} is stale: built from sources {built}, the tree is "
+                          f"{want}; rebuild with python -m fp8_quantized_paged_amd.build")
+
+
+_stale_check()
+
+
 def _hip_runtimes_mapped() -> set:
     libs = set()
     with open("/proc/self/maps") as f:
@@ -51,9 +68,14 @@ PER_TENSOR, PER_TOKEN_HEAD, PER_KV_HEAD = 0, 1, 2
 WARN_UNCALIBRATED_Q_OR_PROB = 1
 SKIP_SLIDING_WINDOW = 1
 PAGE_SIZE = 16
+# fixed counter prefix of every decode workspace (include/kvq.h)
+DECODE_MAX_SPLIT_UNITS = 65536
+DECODE_COUNTER_BYTES = 4 * DECODE_MAX_SPLIT_UNITS
 _MODES = {"per_tensor": PER_TENSOR, "per_token_head": PER_TOKEN_HEAD,
           "per_kv_head": PER_KV_HEAD}
 _DTYPES = {"bf16": BF16, "fp8": FP8_E4M3, "f32": F32}
+ACCUM_MFMA_CHAIN, ACCUM_VALU_ADD = 0, 1
+ACCUMULATIONS = {"mfma_chain": ACCUM_MFMA_CHAIN, "valu_add": ACCUM_VALU_ADD}
 
 
 class Scales(ctypes.Structure):
@@ -103,6 +125,9 @@ _SIGS = {
     "kvq_prefill_attention": (ctypes.c_int, [_PD, _p, _p, _i32, _i32, _p, _i32, _p,
                                              _i32, ctypes.POINTER(Scales), _i32, _i32,
                                              _f32, _p, ctypes.c_int, _p]),
+    "kvq_prefill_attention_accum": (ctypes.c_int, [_PD, _p, _p, _i32, _i32, _p, _i32, _p,
+                                                   _i32, ctypes.POINTER(Scales), _i32, _i32,
+                                                   _f32, _p, ctypes.c_int, ctypes.c_int, _p]),
     "kvq_paged_logits": (ctypes.c_int, [_PD, _p, _p, _i32, _i32, _p, _p, _i32, _p,
                                         ctypes.POINTER(Scales), _p, _i32, _p]),
 }
@@ -323,8 +348,12 @@ def decode_step(cache: PagedCache, q, k_new, v_new, block_table, seq_lens, max_s
 def prefill_attention(cache: PagedCache, q, cu_q_lens, block_table, seq_lens,
                       max_q_len: int, scales: Scales | None = None, causal: bool = True,
                       window: int = 0, softmax_scale: float = 0.0, out=None,
-                      out_dtype: str = "bf16", stream=None):
-    """q bf16 [Nq][Hq][D]; cu_q_lens int32 [B+1]; seq_lens int32 [B] (incl. new)."""
+                      out_dtype: str = "bf16", accumulation: str | None = None,
+                      stream=None):
+    """q bf16 [Nq][Hq][D]; cu_q_lens int32 [B+1]; seq_lens int32 [B] (incl. new).
+
+    accumulation: None (kvq_prefill_attention) or "mfma_chain" / "valu_add"
+    (kvq_prefill_attention_accum with that level-2 form)."""
     torch = _torch()
     Nq, Hq, D = q.shape
     if scales is None:
@@ -333,11 +362,17 @@ def prefill_attention(cache: PagedCache, q, cu_q_lens, block_table, seq_lens,
         out = torch.empty((Nq, Hq, D), dtype=torch.bfloat16 if out_dtype == "bf16"
                           else torch.float32, device=q.device)
     d = cache.desc()
-    _check(_lib.kvq_prefill_attention(
-        ctypes.byref(d), _ptr(q), _ptr(cu_q_lens), int(seq_lens.numel()), Hq,
-        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_q_len,
-        ctypes.byref(scales), int(causal), window, softmax_scale, _ptr(out),
-        _DTYPES[out_dtype], _stream(stream, q.device)), "prefill_attention")
+    args = (ctypes.byref(d), _ptr(q), _ptr(cu_q_lens), int(seq_lens.numel()), Hq,
+            _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_q_len,
+            ctypes.byref(scales), int(causal), window, softmax_scale, _ptr(out),
+            _DTYPES[out_dtype])
+    if accumulation is None:
+        _check(_lib.kvq_prefill_attention(*args, _stream(stream, q.device)),
+               "prefill_attention")
+    else:
+        _check(_lib.kvq_prefill_attention_accum(*args, ACCUMULATIONS[accumulation],
+                                                _stream(stream, q.device)),
+               "prefill_attention_accum")
     return out
 
 

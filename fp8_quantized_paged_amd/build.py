@@ -5,6 +5,7 @@ instruction selection disabled, then linked into fp8_quantized_paged_amd/libkvq.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -18,8 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvq.so")
 ARCH = "gfx950"
 
-SOURCES = ["host.cpp", "cache_write.hip", "decode.hip", "prefill.hip", "prefill_bf16.hip",
-           "logits.hip"]
+SOURCES = ["host.cpp", "cache_write.hip", "decode.hip", "prefill.hip", "prefill_d64.hip",
+           "prefill_d128.hip", "prefill_d256.hip", "prefill_bf16.hip", "logits.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -31,6 +32,23 @@ COMMON_FLAGS = [
     "-mllvm", "-simplifycfg-sink-common=false",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+
+
+def source_hash() -> str:
+    """SHA-256 (first 32 hex digits) of everything the library is built from: the
+    sources, the public header and the compiler flags.  build() compiles it into the
+    library (symbol kvq_build_source_hash); the binding refuses a library whose
+    recorded hash differs from the tree's, i.e. a stale build."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            h.update(name.encode() + b"\0")
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    with open(os.path.join(INCLUDE, "kvq.h"), "rb") as f:
+        h.update(f.read())
+    h.update(" ".join(COMMON_FLAGS[:-2]).encode())  # the -I paths depend on the checkout
+    return h.hexdigest()[:32]
 
 
 def hipcc() -> str:
@@ -45,6 +63,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     cc = hipcc()
     procs = []
     objs = []
+    stamp = f'-DKVQ_SOURCE_HASH="{source_hash()}"'
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         if not os.path.exists(path):
@@ -52,6 +71,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmd = [cc, "-c", path, "-o", obj, *COMMON_FLAGS, *extra_flags]
+        if src == "host.cpp":
+            cmd.append(stamp)
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,

@@ -117,6 +117,7 @@ struct DecodeShape {
 struct DecodeArgs {
   const uint16_t* q;
   int32_t num_kv_heads, splits, pps;
+  int32_t max_len;  // the call's max_seq_len: longer device lengths are clamped to it
   const int32_t* block_table;
   int32_t bt_stride;
   const int32_t* seq_lens;
@@ -271,11 +272,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       qraw[u] = e < QW ? qsrc[e] : 0u;
     }
   }
-  const int L = a.seq_lens[b];
+  // A device length above the call's max_seq_len breaks the precondition the grid and
+  // the workspace were sized by: such a sequence is read only up to max_seq_len (no
+  // access past its block-table row, at most a.splits splits, so its merge still
+  // runs and its counter returns to zero) and its new token, if any, is not written.
+  const int L_dev = a.seq_lens[b];
+  const int L = min(L_dev, a.max_len);
   const int lo = a.window > 0 ? max(0, L - a.window) : 0;
   const int pfirst = lo / kPage;
   const int pend = (L + kPage - 1) / kPage;
-  const int ns = L > 0 ? (pend - pfirst + a.pps - 1) / a.pps : 0;  // splits of (b, g)
+  const int ns = L > 0 ? min((pend - pfirst + a.pps - 1) / a.pps, a.splits) : 0;  // splits of (b, g)
   if (s >= ns) {
     if (s == 0) {  // empty sequence: zero output rows
       for (int e = tid; e < G * D; e += kThreads) store_out(a.out, a.out_f32, row0 * D + e, 0.0f);
@@ -348,7 +354,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // only keep the compiler from moving loads above the stores, order the two.
   bool app_owner = false;
   int app_page = 0;
-  if (a.k_new != nullptr) {
+  if (a.k_new != nullptr && L_dev == L) {
     const int lp = (L - 1) / kPage;
     const int rel = lp - pb;
     app_owner = rel >= 0 && lp < pe && rel % kWaves == wave;
@@ -1161,14 +1167,16 @@ static int auto_pages_per_split(int32_t num_seqs, int32_t num_kv_heads, int max_
 struct DecodePlan {
   int pps;
   int splits;
-  size_t counter_bytes;  // completion counters, int32 [B][Hkv], 256-byte padded
-  size_t bytes;
+  size_t bytes;  // 0: one split everywhere, no workspace used
 };
 
-static size_t counter_area_bytes(int32_t num_seqs, int32_t num_kv_heads) {
-  const size_t n = (size_t)num_seqs * num_kv_heads * sizeof(int32_t);
-  return (n + 255) / 256 * 256;
-}
+// Workspace layout, the same for every call so that calls of any shape can share one
+// buffer: the completion counters of unit u = b * Hkv + g (int32) sit at a fixed
+// offset 4 u inside a fixed prefix of KVQ_DECODE_COUNTER_BYTES, and the split
+// partials follow it.  A call's partials therefore never overlap a counter, and the
+// counters a call leaves at zero stay zero for the next call, whatever its shape.
+constexpr size_t kCounterBytes = KVQ_DECODE_COUNTER_BYTES;
+static_assert(kCounterBytes == sizeof(int32_t) * KVQ_DECODE_MAX_SPLIT_UNITS, "counter prefix");
 
 static kvq_status plan_decode(const kvq_cache_desc* cache, int32_t num_seqs,
                               int32_t num_q_heads, int32_t max_seq_len, int32_t window,
@@ -1191,10 +1199,16 @@ static kvq_status plan_decode(const kvq_cache_desc* cache, int32_t num_seqs,
                               : auto_pages_per_split(num_seqs, cache->num_kv_heads, mp);
   // at least one split: an all-empty batch still needs its zero output rows
   plan->splits = mp > 0 ? (mp + plan->pps - 1) / plan->pps : 1;
-  plan->counter_bytes = counter_area_bytes(num_seqs, cache->num_kv_heads);
+  const int64_t units = (int64_t)num_seqs * cache->num_kv_heads;
+  if (plan->splits > 1 && units > KVQ_DECODE_MAX_SPLIT_UNITS)
+    return fail(KVQ_ERR_UNSUPPORTED,
+                "num_seqs * num_kv_heads = %lld > %d with %d splits (the workspace's "
+                "counter prefix holds %d units)",
+                (long long)units, KVQ_DECODE_MAX_SPLIT_UNITS, plan->splits,
+                KVQ_DECODE_MAX_SPLIT_UNITS);
   plan->bytes = plan->splits > 1
-                    ? plan->counter_bytes + (size_t)num_seqs * num_q_heads * plan->splits *
-                                                (cache->head_dim + 2) * sizeof(float)
+                    ? kCounterBytes + (size_t)num_seqs * num_q_heads * plan->splits *
+                                          (cache->head_dim + 2) * sizeof(float)
                     : 0;
   return KVQ_OK;
 }
@@ -1247,7 +1261,10 @@ extern "C" kvq_status kvq_decode_workspace_bytes(const kvq_cache_desc* cache,
   return KVQ_OK;
 }
 
-static kvq_status decode_impl(
+namespace kvq {
+
+// The decode entry points' common body (k_new == nullptr: plain decode).
+kvq_status decode_impl(
     const kvq_cache_desc* cache, const void* q, int32_t num_seqs, int32_t num_q_heads,
     const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
     int32_t max_seq_len, const kvq_scales* scales, int32_t window, float softmax_scale,
@@ -1280,6 +1297,7 @@ static kvq_status decode_impl(
                 pl.bytes);
   if (pl.bytes > 0 && ((uintptr_t)workspace & 15u))
     return fail(KVQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  auto st = static_cast<hipStream_t>(stream);
   const int D = cache->head_dim;
   const int G = num_q_heads / cache->num_kv_heads;
   const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)D);
@@ -1288,6 +1306,7 @@ static kvq_status decode_impl(
   args.num_kv_heads = cache->num_kv_heads;
   args.splits = pl.splits;
   args.pps = pl.pps;
+  args.max_len = max_seq_len;
   args.block_table = block_table;
   args.bt_stride = block_table_stride;
   args.seq_lens = seq_lens;
@@ -1303,7 +1322,7 @@ static kvq_status decode_impl(
   args.window = window;
   args.counters = pl.bytes ? static_cast<int32_t*>(workspace) : nullptr;
   args.o_part = pl.bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                    pl.counter_bytes)
+                                                    kCounterBytes)
                          : nullptr;
   args.ml_part = pl.bytes ? args.o_part + (size_t)num_seqs * num_q_heads * pl.splits * D
                           : nullptr;
@@ -1311,7 +1330,6 @@ static kvq_status decode_impl(
   args.out_f32 = out_dtype == KVQ_F32;
   args.k_new = static_cast<const uint16_t*>(k_new);
   args.v_new = static_cast<const uint16_t*>(v_new);
-  auto st = static_cast<hipStream_t>(stream);
   switch (D) {
     case 64: dispatch_group<64>(G, cache, args, num_seqs, pl, st); break;
     case 128: dispatch_group<128>(G, cache, args, num_seqs, pl, st); break;
@@ -1321,6 +1339,8 @@ static kvq_status decode_impl(
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return KVQ_OK;
 }
+
+}  // namespace kvq
 
 extern "C" kvq_status kvq_decode_attention(
     const kvq_cache_desc* cache, const void* q, int32_t num_seqs, int32_t num_q_heads,

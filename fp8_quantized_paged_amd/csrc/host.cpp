@@ -55,7 +55,16 @@ kvq_status check_cache(const kvq_cache_desc* c) {
 
 using namespace kvq;
 
+#ifndef KVQ_SOURCE_HASH
+#define KVQ_SOURCE_HASH "unstamped"
+#endif
+
 extern "C" {
+
+// Hash of the sources this library was built from (set by the build script); the
+// Python binding compares it with the tree's to refuse a stale library.
+extern __attribute__((visibility("default"))) const char kvq_build_source_hash[];
+const char kvq_build_source_hash[] = KVQ_SOURCE_HASH;
 
 int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
 

@@ -190,12 +190,20 @@ kvq_status kvq_cache_write(const kvq_cache_desc* cache, const void* k, const voi
 kvq_status kvq_quantize_fp8(const void* x, int64_t n, float scale, uint8_t* codes,
                             void* stream);
 
+/* Decode workspace layout, fixed for every call so that calls of any shape may share
+ * one buffer: bytes [0, KVQ_DECODE_COUNTER_BYTES) hold the int32 completion counter
+ * of each (sequence b, KV head g) at index b * num_kv_heads + g; the split-K partial
+ * results follow.  A call with more than one split supports at most
+ * KVQ_DECODE_MAX_SPLIT_UNITS (sequence, KV head) pairs (KVQ_ERR_UNSUPPORTED beyond). */
+#define KVQ_DECODE_MAX_SPLIT_UNITS 65536
+#define KVQ_DECODE_COUNTER_BYTES (4 * KVQ_DECODE_MAX_SPLIT_UNITS)
+
 /*
- * Workspace bytes needed by kvq_decode_attention for these arguments: completion
- * counters (int32 per (sequence, KV head), 256-byte padded) followed by the split-K
- * partial results; 0 when every sequence fits in one split (then no workspace is
- * read or written).  pages_per_split = 0 selects the library's choice, which
- * depends only on the arguments given here; otherwise 1..256.  bytes [host].
+ * Workspace bytes needed by kvq_decode_attention for these arguments: the counter
+ * prefix (KVQ_DECODE_COUNTER_BYTES) followed by the split-K partial results; 0 when
+ * every sequence fits in one split (then no workspace is read or written).
+ * pages_per_split = 0 selects the library's choice, which depends only on the
+ * arguments given here; otherwise 1..256.  bytes [host].
  */
 kvq_status kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t max_seq_len,
@@ -227,15 +235,20 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t num_s
  * block_table [device] int32 [num_seqs][block_table_stride]: physical page of each
  *   logical page.  seq_lens [device] int32 [num_seqs].
  * Preconditions: 0 <= seq_lens[b] <= max_seq_len; entries used are < num_pages.
+ *   (A device length above max_seq_len cannot be detected on the host; the kernel
+ *   then reads that sequence only up to max_seq_len -- no access past its block-table
+ *   row -- so its output is wrong but no memory outside the arguments is touched and
+ *   the workspace counters still return to zero.)
  * scales [host]: per-tensor values (q_scale and, in per-tensor mode, k/v scales;
  *   the per-KV-head mode takes k/v from the cache's scale arrays).
  * window: 0 = full attention, > 0 = the last `window` keys.
  * softmax_scale: 0 selects 1/sqrt(D).
  * pages_per_split: 0 = library choice; must match kvq_decode_workspace_bytes.
  * workspace [device], workspace_bytes: at least kvq_decode_workspace_bytes(...).
- *   Its counter area must be zero before the first call (allocate it zero-filled);
- *   every call leaves it zero again.  Calls that share one workspace must not
- *   overlap in time (same stream, or ordered by events).
+ *   Its counter prefix must be zero before the first call (allocate it zero-filled);
+ *   every call leaves it zero again, so one workspace, sized for the largest call,
+ *   serves calls of any shape.  Calls that share one workspace must not overlap in
+ *   time (same stream, or ordered by events).
  * Supported: D in {64,128,256}; num_q_heads / num_kv_heads in {1,2,4,8,16}.
  */
 kvq_status kvq_decode_attention(const kvq_cache_desc* cache, const void* q,
@@ -262,7 +275,8 @@ kvq_status kvq_decode_attention(const kvq_cache_desc* cache, const void* q,
  * k_new, v_new [device]: bf16 [num_seqs][num_kv_heads][D], contiguous, 16-byte
  * aligned.  The other arguments, their preconditions and the workspace rules are
  * those of kvq_decode_attention; the cache is written, so no other call may use it
- * concurrently.
+ * concurrently.  A sequence whose device length exceeds max_seq_len (a precondition
+ * violation) gets no new row written.
  */
 kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const void* k_new,
                            const void* v_new, int32_t num_seqs, int32_t num_q_heads,
@@ -284,11 +298,12 @@ kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const voi
  * > L - n_b + i - window).
  *   S = (q codes . k codes) on FP8 matrix cores, scaled by q_scale * k_scale_j *
  *   softmax_scale (k_scale_j: per-token-head scale, cache->k_scales[g] per-KV-head,
- *   or scales->k_scale per-tensor; V alike); online softmax in float32;
- *   probabilities quantised to e4m3 with
- *   prob_scale (per-token V scales folded in before rounding) and P.V on FP8
- *   matrix cores into a fresh float32 accumulator per key tile, added into the
- *   running float32 output (two-level accumulation).
+ *   or scales->k_scale per-tensor; V alike); online softmax in float32 against a
+ *   reference that puts the largest weight seen at 2^6 (at most 2^8); the weights
+ *   quantised to e4m3 with prob_scale (per-token V scales folded in before
+ *   rounding) and P.V on FP8 matrix cores, each 64-key chunk's sum added into the
+ *   running float32 output (two-level accumulation; the row sum uses the same
+ *   rounded weights, so the output is a convex combination of V rows).
  * q [device] bf16 [total_q][num_q_heads][D]; out [device] [total_q][num_q_heads][D].
  * cu_q_lens [device] int32 [num_seqs+1]; seq_lens [device] int32 [num_seqs];
  * block_table as for decode.  max_q_len >= every n_b.
@@ -305,6 +320,36 @@ kvq_status kvq_prefill_attention(const kvq_cache_desc* cache, const void* q,
                                  int32_t max_q_len, const kvq_scales* scales,
                                  int32_t causal, int32_t window, float softmax_scale,
                                  void* out, kvq_dtype out_dtype, void* stream);
+
+/* Level 2 of the FP8 prefill's two-level accumulation ("vLLM FP8 KV-Cache and Attention
+ * Quantization Update", section "Two-level accumulation": partial sums flushed to true
+ * FP32 registers every chunk; the page's recommendations table offers turning the
+ * scheme off for head_dim-256 prefill-heavy work). */
+typedef enum {
+  /* The matrix core's float32 C operand carries the running output: each 64-key
+   * chunk's MFMA adds into it (the default; kvq_prefill_attention). */
+  KVQ_ACCUM_MFMA_CHAIN = 0,
+  /* Explicit flush: each 64-key chunk's MFMA starts from zero and its result is added
+   * into the running output by float32 vector adds (16 extra adds per lane and
+   * output block per chunk). */
+  KVQ_ACCUM_VALU_ADD = 1
+} kvq_accumulation;
+
+/*
+ * kvq_prefill_attention with the level-2 accumulation form chosen by `accum` (an
+ * ablation of the two-level scheme; both forms keep the running output in float32).
+ * Arguments, layouts and errors as kvq_prefill_attention; additionally
+ * KVQ_ERR_INVALID_ARG for an unknown `accum` and KVQ_ERR_UNSUPPORTED for
+ * KVQ_ACCUM_VALU_ADD over a bf16 cache (its prefill has the chained form only).
+ */
+kvq_status kvq_prefill_attention_accum(const kvq_cache_desc* cache, const void* q,
+                                       const int32_t* cu_q_lens, int32_t num_seqs,
+                                       int32_t num_q_heads, const int32_t* block_table,
+                                       int32_t block_table_stride, const int32_t* seq_lens,
+                                       int32_t max_q_len, const kvq_scales* scales,
+                                       int32_t causal, int32_t window, float softmax_scale,
+                                       void* out, kvq_dtype out_dtype,
+                                       kvq_accumulation accum, void* stream);
 
 /*
  * Paged query-key logits for a sparse-attention indexer ("vLLM Qwen3.8-Flash-Next: QSA

@@ -29,6 +29,9 @@ over slot-addressed rows, one-hot queries (a lookup), constant key heads (GQA cl
 form), visibility counts, page permutation and bilinearity.
 
 Parity unpinned: nothing in this package.  (The effect of quantising softmax
-probabilities to e4m3 inside the device's prefill kernel is not modelled here; the
-device result is compared with the exact attention under a tolerance instead.)
+probabilities to e4m3 inside the device's prefill kernel is not emulated here -- it
+depends on the kernel's tiling; attention.attend_rows instead bounds the move of the
+renormalised output under given per-key relative weight errors, pinned by brute force
+over every corner of the error box, and the tests compare the device result with the
+exact attention within that bound.)
 """

@@ -31,6 +31,7 @@ import math
 import numpy as np
 
 PAGE_SIZE = 16
+LOG2E = 1.0 / math.log(2.0)
 
 
 def gather(pool, block_table_row, n_tokens: int) -> np.ndarray:
@@ -41,7 +42,8 @@ def gather(pool, block_table_row, n_tokens: int) -> np.ndarray:
     return pool[pages, :, j % PAGE_SIZE, :]
 
 
-def attend_rows(q, k, v, lo, hi, sm_scale: float, spread: bool = False):
+def attend_rows(q, k, v, lo, hi, sm_scale: float, spread: bool = False,
+                weight_error=None):
     """Softmax attention of query rows q [R][D] over rows k, v [L][D].
 
     Row r sees keys lo[r] .. hi[r] inclusive; an empty range gives zeros.
@@ -51,6 +53,14 @@ def attend_rows(q, k, v, lo, hi, sm_scale: float, spread: bool = False):
     which the output moves per unit of relative error in the weights (if every
     weight w_j becomes w_j (1 + e_j) with |e_j| <= r, renormalised, the output
     moves by at most r / (1 - r) times this).
+
+    With ``weight_error`` (a function of (gap, j) giving, for key j of a row whose
+    log2-domain score lies ``gap`` = (s_j - max_i s_i) * log2(e) <= 0 below the row's
+    largest, a bound e_j in [0, 1] on the relative error of that key's weight) the
+    second result is instead the largest move of the renormalised weighted mean under
+    those errors:  sum_j e_j w_j |v_j - o| / sum_j w_j (1 - e_j).  (Exact: with
+    w'_j = w_j (1 + d_j), o' - o = sum_j w_j d_j (v_j - o) / sum_j w'_j, because
+    sum_j w_j (v_j - o) = 0.)  Infinite when the denominator is not positive.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -58,7 +68,7 @@ def attend_rows(q, k, v, lo, hi, sm_scale: float, spread: bool = False):
     out = np.zeros((q.shape[0], v.shape[1]), np.float64)
     dev = np.zeros_like(out)
     if k.shape[0] == 0:
-        return (out, dev) if spread else out
+        return (out, dev) if (spread or weight_error is not None) else out
     s = (q @ k.T) * sm_scale                      # [R][L]
     j = np.arange(k.shape[0])[None, :]
     vis = (j >= np.asarray(lo)[:, None]) & (j <= np.asarray(hi)[:, None])
@@ -70,10 +80,17 @@ def attend_rows(q, k, v, lo, hi, sm_scale: float, spread: bool = False):
     l = p.sum(axis=1, keepdims=True)
     o = (p @ v) / np.where(l > 0, l, 1.0)
     out[ok] = o[ok]
-    if not spread:
+    if not spread and weight_error is None:
         return out
     for r in np.nonzero(ok)[0]:
-        dev[r] = (p[r] @ np.abs(v - o[r])) / l[r, 0]
+        if weight_error is None:
+            dev[r] = (p[r] @ np.abs(v - o[r])) / l[r, 0]
+            continue
+        js = np.nonzero(vis[r])[0]
+        gap = (s[r, js] - m[r, 0]) * LOG2E
+        e = np.clip(np.asarray(weight_error(gap, js), np.float64), 0.0, 1.0)
+        den = p[r, js] @ (1.0 - e)
+        dev[r] = ((p[r, js] * e) @ np.abs(v[js] - o[r])) / den if den > 0 else np.inf
     return out, dev
 
 
@@ -115,13 +132,16 @@ def decode(q, k_pool, v_pool, block_table, seq_lens, window: int = 0,
 
 def prefill(q, cu_q_lens, k_pool, v_pool, block_table, seq_lens, causal: bool = True,
             window: int = 0, sm_scale: float | None = None, rows=None,
-            spread: bool = False):
+            spread: bool = False, weight_error=None):
     """Chunked-prefill attention.  q [Nq][Hq][D] holds the new queries of all
     sequences back to back (sequence b owns rows cu_q_lens[b] .. cu_q_lens[b+1]-1).
 
     Returns float64 [Nq][Hq][D].  ``rows`` optionally restricts the work to a sorted
     list of query row indices (other rows stay zero).  With ``spread`` also returns
-    attend_rows' weighted mean absolute deviation of V, same shape.
+    attend_rows' weighted mean absolute deviation of V, same shape.  With
+    ``weight_error`` (a function of (b, g) returning attend_rows' per-key function for
+    sequence b, KV head g; keys j are the sequence's positions) the second result is
+    attend_rows' bound under those per-key weight errors instead.
     """
     q = np.asarray(q, np.float64)
     Nq, Hq, D = q.shape
@@ -147,9 +167,10 @@ def prefill(q, cu_q_lens, k_pool, v_pool, block_table, seq_lens, causal: bool = 
         v = gather(v_pool, block_table[b], L)
         for h in range(Hq):
             g = h // G
-            res = attend_rows(q[idx, h], k[:, g], v[:, g], lo, hi, sm, spread)
-            if spread:
+            we = None if weight_error is None else weight_error(b, g)
+            res = attend_rows(q[idx, h], k[:, g], v[:, g], lo, hi, sm, spread, we)
+            if spread or we is not None:
                 out[idx, h], dev[idx, h] = res
             else:
                 out[idx, h] = res
-    return (out, dev) if spread else out
+    return (out, dev) if (spread or weight_error is not None) else out

@@ -19,6 +19,9 @@ from oracle import attention, cache as ocache
 # the same dequantised cache: |o - O| <= ATOL + RTOL * |O| elementwise.
 ATOL = 5e-3
 RTOL = 2e-2
+# Second bar: against the float64 attention over the raw (unquantised) bf16 Q/K/V,
+# |o - O_bf16| <= BF16_TOL + BF16_TOL * |O_bf16| elementwise.
+BF16_TOL = 6e-2
 
 
 def log(*a):
@@ -105,3 +108,45 @@ def assert_close_to_oracle(got, want, what=""):
             f"{what}: {int(bad.sum())}/{bad.size} outside {ATOL}+{RTOL}|O|; worst at "
             f"{i}: got {got[i]!r} want {want[i]!r} (max abs err {err.max():.3g})")
     return float(err.max())
+
+
+def raw_pools_for_heads(case, b, kv_heads):
+    """Logical float64 K/V pools of sequence b's raw bf16 rows for some KV heads (other
+    entries zero): the inputs of the bf16-cache reference."""
+    sel = np.nonzero(case.token_seq == b)[0]
+    P, D = case.num_pages, case.head_dim
+    kp = np.zeros((P, case.num_kv_heads, 16, D))
+    vp = np.zeros_like(kp)
+    page, off = case.slots[sel] // 16, case.slots[sel] % 16
+    for g in kv_heads:
+        kp[page, g, off] = case.k[sel, g]
+        vp[page, g, off] = case.v[sel, g]
+    return kp, vp
+
+
+def check_bf16_bar(got, want_bf16, want_exact=None, what="", require=True):
+    """The second bar.  With require=False (a workload where the oracle's own exact
+    result already misses it) the device's distance to O_bf16 must instead stay
+    within the first bar of the oracle's own distance, element by element:
+    |o - O_bf16| <= |O_exact - O_bf16| + ATOL + RTOL * |O_exact|.  Returns the
+    fraction of elements within the bar for the device (and for the oracle)."""
+    err = np.abs(got - want_bf16)
+    lim = BF16_TOL + BF16_TOL * np.abs(want_bf16)
+    frac = float(np.mean(err <= lim))
+    frac_oracle = None
+    if want_exact is not None:
+        frac_oracle = float(np.mean(np.abs(want_exact - want_bf16) <= lim))
+    log(f"  {what}: within {BF16_TOL} of the bf16-cache result: device {frac:.4f}"
+        + ("" if frac_oracle is None else f", oracle's exact result {frac_oracle:.4f}"))
+    if require:
+        bad = err > lim
+        if bad.any():
+            i = np.unravel_index(np.argmax(err - lim), err.shape)
+            raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} outside {BF16_TOL} "
+                                 f"of the bf16 result; worst got {got[i]!r} "
+                                 f"want {want_bf16[i]!r}")
+    else:
+        assert want_exact is not None
+        slack = np.abs(want_exact - want_bf16) + ATOL + RTOL * np.abs(want_exact)
+        assert np.all(err <= slack), what
+    return frac, frac_oracle

@@ -8,7 +8,7 @@ import pytest
 
 from oracle import scales as oscales
 
-kvq = pytest.importorskip("fp8_quantized_paged_amd")
+import fp8_quantized_paged_amd as kvq  # noqa: E402  (a missing or stale library fails here)
 
 from test_oracle_cache import read_scale_cases  # noqa: E402
 
@@ -132,19 +132,28 @@ def test_decode_workspace_and_checks():
     L = _lib()
     n = ctypes.c_size_t()
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 32, 20000, 0, 0, ctypes.byref(n)) == 0
-    assert n.value > 256
-    assert (n.value - 256) % (8 * 32 * (128 + 2) * 4) == 0   # 256: counters for 8 x 8
+    C = kvq.DECODE_COUNTER_BYTES   # fixed counter prefix, whatever the shape
+    assert n.value > C
+    assert (n.value - C) % (8 * 32 * (128 + 2) * 4) == 0
     # explicit pages_per_split: splits = ceil(1250 / 10) = 125
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 32, 20000, 0, 10, ctypes.byref(n)) == 0
-    assert n.value == 256 + 8 * 32 * 125 * 130 * 4
+    assert n.value == C + 8 * 32 * 125 * 130 * 4
     # one long sequence: the automatic split count stops at 32 per (sequence, KV head)
     # (8,192 pages -> 256 pages per split)
     one = _desc(mode=kvq.PER_TENSOR)
     assert L.kvq_decode_workspace_bytes(ctypes.byref(one), 1, 32, 131072, 0, 0, ctypes.byref(n)) == 0
-    assert n.value == 256 + 1 * 32 * 32 * 130 * 4
+    assert n.value == C + 1 * 32 * 32 * 130 * 4
     # a window bounds the visible pages: 128 keys span at most 9 pages
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 32, 20000, 128, 4, ctypes.byref(n)) == 0
-    assert n.value == 256 + 8 * 32 * 3 * 130 * 4
+    assert n.value == C + 8 * 32 * 3 * 130 * 4
+    # more than KVQ_DECODE_MAX_SPLIT_UNITS (sequence, KV head) pairs only without splits
+    # (this descriptor has 2 KV heads: 32,769 sequences are 65,538 pairs)
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 32769, 32, 20000, 0, 0,
+                                        ctypes.byref(n)) == kvq.binding.ERR_UNSUPPORTED
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 32769, 32, 4096, 0, 0,
+                                        ctypes.byref(n)) == 0 and n.value == 0
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 32768, 32, 20000, 0, 0,
+                                        ctypes.byref(n)) == 0 and n.value > C
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 24, 20000, 0, 0, ctypes.byref(n)) == kvq.binding.ERR_UNSUPPORTED
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 33, 20000, 0, 0, ctypes.byref(n)) == kvq.binding.ERR_INVALID_ARG
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 32, 20000, 0, 257, ctypes.byref(n)) == kvq.binding.ERR_INVALID_ARG
@@ -152,7 +161,7 @@ def test_decode_workspace_and_checks():
     args = lambda ws, wsb, outdt=kvq.BF16, q=4096, scales=ctypes.byref(sc): (
         ctypes.byref(d), q, 8, 32, 4096, 1250, 4096, 20000, scales, 0, 0.0, 10, 4096,
         outdt, ws, wsb, None)
-    need = 256 + 8 * 32 * 125 * 130 * 4
+    need = C + 8 * 32 * 125 * 130 * 4
     assert L.kvq_decode_attention(*args(None, 0)) == kvq.binding.ERR_WORKSPACE
     assert L.kvq_decode_attention(*args(4096, need - 1)) == kvq.binding.ERR_WORKSPACE
     assert L.kvq_decode_attention(*args(4096, need, outdt=kvq.FP8_E4M3)) == kvq.binding.ERR_UNSUPPORTED

@@ -152,3 +152,37 @@ def test_cache_write_llama8b_sampled(kvq):
     rows = np.sort(rng.choice(len(case.k), size=4000, replace=False))
     want = oracle_pools(case, "per_token_head", rows=rows)
     _check_pools(read_pools(c), want, case.slots[rows])
+
+
+@pytest.mark.parametrize("which", ["long_context", "gptoss_full", "gptoss_window",
+                                   "hd256_prefill"])
+def test_cache_write_full_size_sampled(kvq, which):
+    """Codes and scales bit-exact on the other full-size workloads, written in the bulk
+    configuration: the 131,072-token cache (per-tensor scale 1.0, the planted key's row
+    included), a gpt-oss-shaped full-attention layer (fp8, per-tensor) and window layer
+    (bf16 copy), and the head_dim-256 prefill cache (per-token-head) with every one of
+    its 8,192 new tokens."""
+    rng = np.random.default_rng(11)
+    if which == "long_context":
+        case, dtype, mode = workloads.long_context_decode(), "fp8", "per_tensor"
+        extra = [case.meta["planted_pos"]]
+    elif which.startswith("gptoss"):
+        case = workloads.gptoss_hybrid_layer(0 if which == "gptoss_full" else 1)
+        dtype = kvq.layer_kv_dtype(case.window, kvq.SKIP_SLIDING_WINDOW)
+        mode, extra = "per_tensor", []
+    else:
+        case, dtype, mode = workloads.hd256_prefill(), "fp8", "per_token_head"
+        extra = list(case.new_token_rows())
+    log(f"cache_write {which} full ({dtype}, {mode})")
+    c = write_cache(kvq, case, dtype, mode, chunk=1 << 24)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([rng.choice(len(case.k), size=4000, replace=False),
+                                     np.asarray(extra, np.int64)]))
+    got = read_pools(c)
+    if dtype == "bf16":
+        page, off = case.slots[rows] // 16, case.slots[rows] % 16
+        assert np.array_equal(got["k"][page, :, off], case.k[rows])
+        assert np.array_equal(got["v"][page, :, off], case.v[rows])
+        return
+    want = oracle_pools(case, mode, rows=rows)
+    _check_pools(got, want, case.slots[rows])

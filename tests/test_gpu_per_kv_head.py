@@ -100,5 +100,5 @@ def test_prefill(kvq, D, Hq, Hkv):
     log(f"per-KV-head prefill D={D}")
     c = write_cache(kvq, case, "fp8", "per_kv_head", ks, vs)
     got = run_prefill(kvq, c, case)
-    want, spread = oracle_prefill(case, "per_kv_head", 1.0, ks, vs, spread=True)
-    assert_close_with_p_rounding(got, want, spread, f"per-KV-head prefill D={D}")
+    want, bound = oracle_prefill(case, "per_kv_head", 1.0, ks, vs, p_bound=True)
+    assert_close_with_p_rounding(got, want, bound, f"per-KV-head prefill D={D}")

@@ -282,6 +282,56 @@ def test_spread_brute_force_and_special_cases():
                        atol=1e-14, rtol=0)
 
 
+def test_weight_error_bound_brute_force():
+    """attend_rows' bound under per-key weight errors: for tiny rows, every corner of
+    the box of relative errors (each weight scaled by 1 - e_j or 1 + e_j, then the
+    mean renormalised) moves the output by at most the bound, and the worst corner
+    comes within second order of it; zero errors give zero, a constant error r gives
+    r / (1 - r) times the spread, and the gap handed to the function is the key's
+    log2-domain distance below the row maximum."""
+    import itertools
+    rng = np.random.default_rng(9)
+    for trial in range(6):
+        n = 5
+        q = rng.standard_normal((1, 4))
+        k = rng.standard_normal((n, 4))
+        v = rng.standard_normal((n, 4))
+        e = rng.uniform(0.0, 0.02, n) if trial % 2 else rng.uniform(0.0, 0.3, n)
+        seen = {}
+
+        def fn(gap, js):
+            seen["gap"], seen["js"] = np.array(gap), np.array(js)
+            return e[np.asarray(js)]
+        out, bound = attention.attend_rows(q, k, v, [0], [n - 1], 0.7, weight_error=fn)
+        s = 0.7 * (q[0] @ k.T)
+        assert np.allclose(seen["gap"], (s - s.max()) / math.log(2.0), atol=1e-12)
+        assert list(seen["js"]) == list(range(n))
+        w = np.exp(s - s.max())
+        worst = np.zeros(4)
+        for signs in itertools.product((-1.0, 1.0), repeat=n):
+            w2 = w * (1.0 + np.array(signs) * e)
+            worst = np.maximum(worst, np.abs(w2 @ v / w2.sum() - out[0]))
+        assert np.all(worst <= bound[0] + 1e-15)
+        # the numerator's worst case is one corner (signs of v_j - o per channel);
+        # only the denominator's 1 - e_j is not attained at the same time
+        assert np.all(worst >= bound[0] * (1.0 - e.max()) / (1.0 + e.max()) - 1e-15)
+    # special cases
+    q = rng.standard_normal((2, 4))
+    k = rng.standard_normal((7, 4))
+    v = rng.standard_normal((7, 4))
+    _, z = attention.attend_rows(q, k, v, [0, 0], [6, 3], 1.0,
+                                 weight_error=lambda g, j: np.zeros(len(j)))
+    assert np.all(z == 0.0)
+    r = 0.05
+    _, b = attention.attend_rows(q, k, v, [0, 0], [6, 3], 1.0,
+                                 weight_error=lambda g, j: np.full(len(j), r))
+    _, sp = attention.attend_rows(q, k, v, [0, 0], [6, 3], 1.0, spread=True)
+    assert np.allclose(b, r / (1.0 - r) * sp, rtol=1e-12, atol=0)
+    _, inf = attention.attend_rows(q, k, v, [0, 0], [6, 3], 1.0,
+                                   weight_error=lambda g, j: np.ones(len(j)))
+    assert np.all(np.isinf(inf))
+
+
 # ---- mutation tests -------------------------------------------------------------
 
 def test_mutants_are_caught():

@@ -13,8 +13,8 @@ outlier channels, planted position, block-table permutation):
     once and shared by all tokens, whose values are multiplied by 20 before the
     bfloat16 rounding;
   * "planted key": at one seeded position, in every KV head g, the key row is
-    8 * q / |q| with q the query of the group's first head (h = g * G), rounded to
-    bfloat16;
+    8 * q / |q| with q the query of the group's first head (h = g * G) -- the decode
+    query, or the last new row of a prefill chunk -- rounded to bfloat16;
   * block tables: identity (sequence b owns pages b*P .. b*P+P-1) or a seeded
     permutation of all pages reshaped to [B][P], as the pages' tests build them.
 """
@@ -188,7 +188,10 @@ class PrefillCase:
 def make_prefill_case(seed: int, ctx_lens, new_lens, num_q_heads: int,
                       num_kv_heads: int, head_dim: int, table: str = "identity",
                       std: float = 1.0, window: int = 0, extra_pages: int = 0,
-                      name: str = "prefill") -> PrefillCase:
+                      planted_below: int = 0, name: str = "prefill") -> PrefillCase:
+    """planted_below > 0: a planted key at a seeded position below planted_below (and
+    below every sequence's context), in every KV head g of every sequence, equal to
+    8 * q / |q| for q the query of head g * G at the sequence's LAST new row."""
     rng = np.random.default_rng(seed)
     ctx_lens = np.asarray(ctx_lens, np.int64)
     new_lens = np.asarray(new_lens, np.int64)
@@ -199,13 +202,25 @@ def make_prefill_case(seed: int, ctx_lens, new_lens, num_q_heads: int,
     q = normal_bf16(rng, (Nq, num_q_heads, head_dim))
     k = normal_bf16(rng, (T, num_kv_heads, head_dim), std)
     v = normal_bf16(rng, (T, num_kv_heads, head_dim), std)
+    meta = {}
+    if planted_below > 0:
+        G = num_q_heads // num_kv_heads
+        pos = int(rng.integers(0, min(planted_below, int(ctx_lens.min()))))
+        meta["planted_pos"] = pos
+        starts = np.concatenate([[0], np.cumsum(seq_lens)[:-1]])
+        ends = np.cumsum(new_lens) - 1
+        for b in range(B):
+            for g in range(num_kv_heads):
+                qv = q[ends[b], g * G].astype(np.float64)
+                k[starts[b] + pos, g] = bf16_round(
+                    (8.0 * qv / np.linalg.norm(qv)).astype(np.float32))
     pages_per_seq = max(1, -(-int(seq_lens.max()) // PAGE_SIZE))
     num_pages = B * pages_per_seq + extra_pages
     bt = make_block_table(rng, B, pages_per_seq, table, num_pages)
     ts, tp, slots = token_layout(seq_lens, bt)
     cu = np.concatenate([[0], np.cumsum(new_lens)]).astype(np.int32)
     return PrefillCase(name, q, cu, k, v, ts, tp, slots, bt, seq_lens, num_pages,
-                       num_kv_heads, head_dim, window)
+                       num_kv_heads, head_dim, window, meta)
 
 
 @dataclass
@@ -303,3 +318,12 @@ def hd256_prefill(seed: int = 105, ctx: int = 32768, new: int = 8192) -> Prefill
     cache, 8 q / 4 KV heads, causal, identity table, N(0,1) bf16."""
     return make_prefill_case(seed, [ctx], [new], 8, 4, 256, table="identity",
                              name="hd256_prefill")
+
+
+def long_context_prefill(seed: int = 106, ctx: int = 130944, new: int = 128) -> PrefillCase:
+    """Accumulation stress for the FP8-MFMA prefill: 128 new queries at the end of a
+    131,072-token sequence, 32 q / 8 KV heads, head_dim 128, K/V N(0, 0.5) bf16 with a
+    planted key 8 q / |q| (q of the last new row, first head of each group) at a seeded
+    position in the first 16,384 tokens, so that nearly every key is read after it."""
+    return make_prefill_case(seed, [ctx], [new], 32, 8, 128, table="identity", std=0.5,
+                             planted_below=16384, name="long_context_prefill")
