@@ -71,6 +71,7 @@ PAGE_SIZE = 16
 # fixed counter prefix of every decode workspace (include/kvq.h)
 DECODE_MAX_SPLIT_UNITS = 65536
 DECODE_COUNTER_BYTES = 4 * DECODE_MAX_SPLIT_UNITS
+DECODE_SCRATCH_BYTES = 32 * 1024 * 1024
 _MODES = {"per_tensor": PER_TENSOR, "per_token_head": PER_TOKEN_HEAD,
           "per_kv_head": PER_KV_HEAD}
 _DTYPES = {"bf16": BF16, "fp8": FP8_E4M3, "f32": F32}
@@ -119,6 +120,9 @@ _SIGS = {
     "kvq_decode_attention": (ctypes.c_int, [_PD, _p, _i32, _i32, _p, _i32, _p, _i32,
                                             ctypes.POINTER(Scales), _i32, _f32, _i32,
                                             _p, ctypes.c_int, _p, _sz, _p]),
+    "kvq_decode_attention_noalloc": (ctypes.c_int, [_PD, _p, _i32, _i32, _p, _i32, _p, _i32,
+                                                    ctypes.POINTER(Scales), _i32, _f32, _i32,
+                                                    _p, ctypes.c_int, _p]),
     "kvq_decode_step": (ctypes.c_int, [_PD, _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32,
                                        ctypes.POINTER(Scales), _i32, _f32, _i32,
                                        _p, ctypes.c_int, _p, _sz, _p]),
@@ -317,6 +321,28 @@ def decode_attention(cache: PagedCache, q, block_table, seq_lens, max_seq_len: i
         _ptr(seq_lens), max_seq_len, ctypes.byref(scales), window, softmax_scale,
         pages_per_split, _ptr(out), _DTYPES[out_dtype], _ptr(workspace),
         workspace.numel(), _stream(stream, q.device)), "decode_attention")
+    return out
+
+
+def decode_attention_noalloc(cache: PagedCache, q, block_table, seq_lens, max_seq_len: int,
+                             scales: Scales | None = None, window: int = 0,
+                             softmax_scale: float = 0.0, pages_per_split: int = 0, out=None,
+                             out_dtype: str = "bf16", stream=None):
+    """decode_attention on the library's own device scratch (no workspace).  With
+    ``out`` given, the call allocates nothing."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    if scales is None:
+        scales = Scales(1.0, 1.0, 1.0, 1.0)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16 if out_dtype == "bf16"
+                          else torch.float32, device=q.device)
+    d = cache.desc()
+    _check(_lib.kvq_decode_attention_noalloc(
+        ctypes.byref(d), _ptr(q), B, Hq, _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), max_seq_len, ctypes.byref(scales), window, softmax_scale,
+        pages_per_split, _ptr(out), _DTYPES[out_dtype], _stream(stream, q.device)),
+        "decode_attention_noalloc")
     return out
 
 

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvq.so")
 ARCH = "gfx950"
 
-SOURCES = ["host.cpp", "cache_write.hip", "decode.hip", "prefill.hip", "prefill_d64.hip",
+SOURCES = ["host.cpp", "cache_write.hip", "decode.hip", "decode_noalloc.hip", "prefill.hip", "prefill_d64.hip",
            "prefill_d128.hip", "prefill_d256.hip", "prefill_bf16.hip", "logits.hip"]
 
 COMMON_FLAGS = [

@@ -260,6 +260,33 @@ kvq_status kvq_decode_attention(const kvq_cache_desc* cache, const void* q,
                                 void* out, kvq_dtype out_dtype, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* Size of the device scratch behind kvq_decode_attention_noalloc (per GPU). */
+#define KVQ_DECODE_SCRATCH_BYTES (32 * 1024 * 1024)
+
+/*
+ * kvq_decode_attention without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  It calls no allocating routine: the split-K partials and the
+ * completion counters live in a library-owned device array of KVQ_DECODE_SCRATCH_BYTES
+ * per GPU (the workspace layout above: counter prefix, then partials), held until the
+ * process ends.  The first call on a device (the calling thread's current device,
+ * which must own `stream`) looks the array up and clears its counters with a small
+ * kernel on `stream`.  Every call on one GPU shares that array: calls that overlap in
+ * time on one GPU (different streams, or another thread) race and give wrong results;
+ * order them on one stream.  Arguments, results and preconditions are those of
+ * kvq_decode_attention; KVQ_ERR_WORKSPACE when kvq_decode_workspace_bytes(...) for
+ * these arguments exceeds KVQ_DECODE_SCRATCH_BYTES (split the batch or raise
+ * pages_per_split).
+ */
+kvq_status kvq_decode_attention_noalloc(const kvq_cache_desc* cache, const void* q,
+                                        int32_t num_seqs, int32_t num_q_heads,
+                                        const int32_t* block_table,
+                                        int32_t block_table_stride, const int32_t* seq_lens,
+                                        int32_t max_seq_len, const kvq_scales* scales,
+                                        int32_t window, float softmax_scale,
+                                        int32_t pages_per_split, void* out,
+                                        kvq_dtype out_dtype, void* stream);
+
 /*
  * Decode step: the cache write of each sequence's new token and the decode attention
  * of kvq_decode_attention, in one launch.  For every sequence b with L = seq_lens[b]
