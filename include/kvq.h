@@ -326,7 +326,7 @@ kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const voi
  *   S = (q codes . k codes) on FP8 matrix cores, scaled by q_scale * k_scale_j *
  *   softmax_scale (k_scale_j: per-token-head scale, cache->k_scales[g] per-KV-head,
  *   or scales->k_scale per-tensor; V alike); online softmax in float32 against a
- *   reference that puts the largest weight seen at 2^6 (at most 2^8); the weights
+ *   reference that puts the largest weight seen at 2^4 (at most 2^8); the weights
  *   quantised to e4m3 with prob_scale (per-token V scales folded in before
  *   rounding) and P.V on FP8 matrix cores, each 64-key chunk's sum added into the
  *   running float32 output (two-level accumulation; the row sum uses the same

@@ -6,13 +6,13 @@ the sum of the same rounded weights, so its output is the exact attention with e
 weight w_j carrying a relative error d_j, renormalised.  The bound on |d_j| follows
 from the kernel's stated invariants (prefill_kernel.h, "Softmax"): the weight handed to
 the rounding is P_j = 2^(x_j - m) f_j, where x_j is the key's log2-domain score, the
-reference m is at most the row's largest score minus 6 (so P_j >= 2^(gap_j + 6) f_j,
+reference m is at most the row's largest score minus 4 (so P_j >= 2^(gap_j + 4) f_j,
 gap_j = x_j - max x <= 0), and f_j = v_scale_j / (v_ref prob_scale) with v_ref at most
 the largest V scale of the sequence's KV head (per-tensor and per-KV-head modes:
 f_j = 1 / prob_scale).  Round-to-nearest e4m3 errs by at most 2^-4 P (normal values,
 3 mantissa bits) or 2^-10 (the subnormal grid 2^-9, values below 2^-6; below 2^-10
 the weight may flush to zero), and a non-negative weight cannot err by more than
-itself: |d_j| <= min(1, max(2^-4, 2^-10 / (2^(gap_j + 6) f_j))).  The oracle turns
+itself: |d_j| <= min(1, max(2^-4, 2^-10 / (2^(gap_j + 4) f_j))).  The oracle turns
 those per-key bounds into the largest move of the renormalised mean (attend_rows'
 weight_error), which the tests add to the plain 5e-3 + 2e-2 |O| bar.  The full-size
 head_dim-256 workload and the 131,072-key stress test are held to the plain bar.
@@ -40,7 +40,7 @@ def kvq():
 
 
 # The kernel's reference puts a row's largest weight at 2^REF_TOP or above.
-REF_TOP = 6.0
+REF_TOP = 4.0
 
 
 def p_rounding_error(case, pools, mode, prob_scale=1.0):
