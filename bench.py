@@ -15,9 +15,12 @@ Infinity Cache cannot serve a step from the previous one.  `value` = algorithmic
 fused launches, on the stream they run on).  Further legs, each timed the same way, are
 reported beside it: the bf16-cache baseline of the same layer, the tiny decode, the 131,072-token decode,
 the 24-layer gpt-oss-20b-shaped hybrid step (12 fp8 full layers + 12 bf16 window-128
-layers, cache writes included) and the head_dim-256 chunked prefill (FP8 matrix cores,
-`roofline` against the dense FP8 peak).  `cpu_baseline` times the CPU oracle (float64)
-on the headline step's inputs.
+layers, cache writes included), the head_dim-256 chunked prefill (FP8 matrix cores,
+`roofline` against the dense FP8 peak, and its level-2 accumulation ablation), the bulk
+quantising cache write (GB/s), and a compact inter-token-latency sweep (decode step of
+whole models at 4k / 32k / 128k contexts, fp8 vs bf16 vs the bf16 window-layer skip
+path: slopes, slope ratios, break-even contexts).  `cpu_baseline` times the CPU oracle
+(float64) on the headline step's inputs.
 """
 from __future__ import annotations
 
@@ -39,7 +42,8 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_llama8b_traffic.json")
 DECODE_KERNEL = "decode_kernel"
 COPY_BYTES = 1 << 30
 SETTLE_S = 0.1               # untimed steps after the warmup, before each timed region
-LEGS = ("decode", "bf16", "tiny", "long", "hybrid", "prefill")
+LEGS = ("decode", "bf16", "tiny", "long", "hybrid", "prefill", "cache_write", "itl")
+ITL_CONTEXTS = (4096, 32768, 131072)   # the default line's compact sweep
 EXTRA_LEGS = ("prefill_d128", "prefill_d64", "per_kv_head", "prefill_bf16_window",
               "paged_logits")
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix throughput, AMD published
@@ -222,6 +226,12 @@ def cpu_baseline(case, nseq, reps=1):
 # ---- attention-only inter-token latency over context length ---------------------------------
 
 def run_itl(args):
+    """--itl: the sweep at --itl-contexts, printed as its own JSON line."""
+    res = itl_sweep([int(x) for x in args.itl_contexts.split(",") if x])
+    print(json.dumps(res), flush=True)
+
+
+def itl_sweep(contexts):
     """Per decode step, the attention of every layer of a model (fused new-token write +
     decode, one HIP graph replay per step), over context lengths: Llama-3.1-8B-shaped
     (32 layers, 8 sequences, 32/8 heads, D 128) with an fp8 (per-token-head) or a bf16
@@ -243,7 +253,6 @@ def run_itl(args):
     ones = kvq.Scales(1.0, 1.0, 1.0, 1.0)
     gen = torch.Generator(device=dev)
     gen.manual_seed(20240607)
-    contexts = [int(x) for x in args.itl_contexts.split(",") if x]
 
     def make_layer(B, L, Hq, Hkv, D, dtype, window):
         """One layer's cache holding L tokens per sequence (N(0,1) bf16 rows through the
@@ -354,7 +363,7 @@ def run_itl(args):
             di = v["intercept_us"] - mres["bf16"]["intercept_us"]
             v["break_even_ctx_vs_bf16"] = round(di / ds * 1e3) if ds > 0 and di > 0 else 0
         res["models"][mname] = mres
-    print(json.dumps(res), flush=True)
+    return res
 
 
 # ---- GPU legs -------------------------------------------------------------------------------
@@ -882,6 +891,34 @@ def main():
                       "cache copies"}
         del cs
         torch.cuda.empty_cache()
+
+    if "cache_write" in legs:
+        # the quantising cache write in its bulk form: the Llama-shaped layer's whole
+        # cache (160,000 tokens x 8 KV heads, D 128, per-token-head scales) and the
+        # head_dim-256 prefill chunk's 8,192 new tokens (4 KV heads, per-token-head)
+        cw = {}
+        for name, (T, Hkv_, D_) in (("llama8b_fill", (160000, 8, 128)),
+                                     ("hd256_new_tokens", (8192, 4, 256))):
+            P_ = (T + 15) // 16
+            c = kvq.PagedCache(P_, Hkv_, D_, "fp8", "per_token_head")
+            kk = dev_normal((T, Hkv_, D_), 1.0, 7000 + D_)
+            vv = dev_normal((T, Hkv_, D_), 1.0, 7100 + D_)
+            sl_ = torch.arange(T, dtype=torch.int64, device=dev)
+            us = timer.run(lambda i: kvq.cache_write(c, kk, vv, sl_), 20, 3, warm_ms=100.0)
+            nb = write_bytes(T, Hkv_, D_, 1, 8) + T * 8   # + the slot mapping
+            cw[name] = {"tokens": T, "kv_heads": Hkv_, "head_dim": D_, **stats(us),
+                        "bytes": nb, "GB_s": round(nb / (float(np.mean(us)) * 1e-6) / 1e9, 1),
+                        "frac_hbm": round(nb / (float(np.mean(us)) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            del c, kk, vv
+            torch.cuda.empty_cache()
+        result["cache_write"] = {
+            "workload": "quantising cache write, per-token-head scales, slots in page order "
+                        "(bulk fill); bytes = bf16 K/V read + e4m3 codes and scales written "
+                        "+ slot mapping", **cw}
+
+    if "itl" in legs:
+        log("bench: inter-token-latency sweep")
+        result["itl_sweep"] = itl_sweep(list(ITL_CONTEXTS))
 
     if args.copy_calib:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)

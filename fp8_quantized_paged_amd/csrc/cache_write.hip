@@ -8,37 +8,44 @@
 // optimizations": per-KV-head mode quantises head h with its own layer scale.
 // Scale = amax / 448, code = clamp(round_rne(v / scale), +-448).
 //
-// Work split: one row = one (token, KV head) of D bf16 values; D/8 lanes own a
-// row, 8 consecutive values (one 16-byte load) each.  The row maximum is reduced
-// across those lanes; every lane then quantises its 8 values.  K rows are stored
-// token-major (8 codes = one 8-byte store per lane), V rows dim-major (one byte per
-// channel row of the page tile).
+// Work split: a workgroup owns 16 consecutive tokens of the call and one KV head;
+// D/8 lanes own a (token, head) row, 8 consecutive values (one 16-byte load) each.
+// The row maximum is reduced across those lanes; every lane then quantises its 8
+// values.  K rows go token-major (8 codes = one 8-byte store per lane).  V rows go
+// dim-major: when the 16 tokens fill one page in order (slots 16 p .. 16 p + 15, the
+// usual bulk fill) the codes are transposed through LDS and every channel row of the
+// page tile is written with one 16-byte store (32 bytes for bf16); otherwise each
+// lane stores its bytes where they belong (one byte per channel row).
 #include "kvq_device.h"
 #include "kvq_host.h"
 
 namespace kvq {
 
+constexpr int kWriteTokens = 16;  // tokens per workgroup: one page when aligned
+
 template <int D, bool kFp8, bool kPerTokenHead>
-__global__ __launch_bounds__(256) void cache_write_kernel(
+__global__ __launch_bounds__(2 * D) void cache_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t token_stride,
     const int64_t* __restrict__ slots, int32_t num_tokens, int32_t num_heads,
     uint8_t* __restrict__ k_pages, uint8_t* __restrict__ v_pages,
     float* __restrict__ k_scales, float* __restrict__ v_scales, float k_scale,
     float v_scale) {
   constexpr int kLanesPerRow = D / 8;
-  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
+  constexpr int EB = kFp8 ? 1 : 2;  // bytes per stored element
+  // V codes of the 16 tokens, channel-major: [d][token] (a page tile's layout)
+  __shared__ __align__(16) uint8_t vt[D * kWriteTokens * EB];
   const int c = threadIdx.x % kLanesPerRow;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
-  if (row >= (int64_t)num_tokens * num_heads) return;  // whole rows exit together
-  const int t = (int)(row / num_heads);
-  const int h = (int)(row % num_heads);
-  const int64_t slot = slots[t];
-  if (slot < 0) return;
-  const int64_t page = slot >> 4;
-  const int off = (int)(slot & 15);
-  const int64_t tile = page * num_heads + h;  // (page, head) tile index
-
-  const int64_t src = (int64_t)t * token_stride + (int64_t)h * D;
+  const int i = threadIdx.x / kLanesPerRow;  // token of the workgroup
+  // head fastest: neighbouring workgroups read the neighbouring pieces of the same
+  // token rows and write neighbouring (page, head) tiles
+  const int h = (int)(blockIdx.x % (unsigned)num_heads);
+  const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)num_heads) * kWriteTokens;
+  const int64_t t = t0 + i;
+  const int64_t slot = t < num_tokens ? slots[t] : -1;
+  // whole-page fast path: 16 tokens present, slots 16 p + i in order
+  const int64_t slot0 = t0 + kWriteTokens <= num_tokens ? slots[t0] : -1;
+  const bool page_run = __syncthreads_and(slot0 >= 0 && (slot0 & 15) == 0 &&
+                                          slot == slot0 + i);
   // per-KV-head mode: k_scales / v_scales hold one scale per head (per-tensor: null)
   float ks = k_scale, vs = v_scale;
   if constexpr (kFp8 && !kPerTokenHead) {
@@ -47,8 +54,78 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
       vs = v_scales[h];
     }
   }
-  store_token_row<D, kFp8, kPerTokenHead>(k + src, v + src, c, tile, off, k_pages, v_pages,
-                                          k_scales, v_scales, ks, vs);
+  if (!page_run) {
+    // any slot pattern: every (token, head) row on its own (rows of skipped tokens
+    // simply do nothing; whole rows of lanes agree)
+    if (slot >= 0) {
+      const int64_t src = t * token_stride + (int64_t)h * D;
+      store_token_row<D, kFp8, kPerTokenHead>(k + src, v + src, c, (slot >> 4) * num_heads + h,
+                                              (int)(slot & 15), k_pages, v_pages, k_scales,
+                                              v_scales, ks, vs);
+    }
+    return;
+  }
+  const int64_t tile = (slot0 >> 4) * num_heads + h;  // the page's (page, head) tile
+  const int64_t src = t * token_stride + (int64_t)h * D;
+  const uint4 kw = *reinterpret_cast<const uint4*>(k + src + c * 8);
+  const uint4 vw = *reinterpret_cast<const uint4*>(v + src + c * 8);
+  if constexpr (!kFp8) {
+    // bf16 cache: K row copied, V values transposed through LDS
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(k_pages) + (tile * kPage + i) * D +
+                              c * 8) = kw;
+    const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
+    uint16_t* vt16 = reinterpret_cast<uint16_t*>(vt);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vt16[(c * 8 + 2 * j) * kWriteTokens + i] = (uint16_t)(vv[j] & 0xFFFFu);
+      vt16[(c * 8 + 2 * j + 1) * kWriteTokens + i] = (uint16_t)(vv[j] >> 16);
+    }
+  } else {
+    const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
+    const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
+    float kf[8], vf[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kf[2 * j] = bf16_bits_to_float(kk[j] & 0xFFFFu);
+      kf[2 * j + 1] = bf16_bits_to_float(kk[j] >> 16);
+      vf[2 * j] = bf16_bits_to_float(vv[j] & 0xFFFFu);
+      vf[2 * j + 1] = bf16_bits_to_float(vv[j] >> 16);
+    }
+    if constexpr (kPerTokenHead) {
+      uint32_t ka = 0, va = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ka = max(ka, abs_bits(kf[j]));
+        va = max(va, abs_bits(vf[j]));
+      }
+#pragma unroll
+      for (int o = kLanesPerRow / 2; o >= 1; o >>= 1) {
+        ka = max(ka, (uint32_t)__shfl_xor((int)ka, o));
+        va = max(va, (uint32_t)__shfl_xor((int)va, o));
+      }
+      ks = scale_from_amax_bits(ka);
+      vs = scale_from_amax_bits(va);
+      if (c == 0) {
+        k_scales[tile * kPage + i] = ks;
+        v_scales[tile * kPage + i] = vs;
+      }
+    }
+    *reinterpret_cast<uint2*>(k_pages + (tile * kPage + i) * D + c * 8) =
+        make_uint2(e4m3_quantize4(kf, ks), e4m3_quantize4(kf + 4, ks));
+    const uint32_t vlo = e4m3_quantize4(vf, vs), vhi = e4m3_quantize4(vf + 4, vs);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      vt[(c * 8 + j) * kWriteTokens + i] = (uint8_t)((j < 4 ? vlo : vhi) >> (8 * (j % 4)));
+  }
+  __syncthreads();
+  // one channel row of the V tile per thread: 16 codes (16 bytes) or 16 bf16 (32 bytes)
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    const uint4* rowp = reinterpret_cast<const uint4*>(vt + d * kWriteTokens * EB);
+    uint4* dst = reinterpret_cast<uint4*>(v_pages + (tile * D + d) * kPage * EB);
+#pragma unroll
+    for (int w = 0; w < EB; ++w) dst[w] = rowp[w];
+  }
 }
 
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x,
@@ -59,45 +136,46 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
     const uint4 w = reinterpret_cast<const uint4*>(x)[i];
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-    uint32_t lo = 0, hi = 0;
+    float f[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      lo |= e4m3_quantize(bf16_bits_to_float(ww[j] & 0xFFFFu), scale) << (16 * j);
-      lo |= e4m3_quantize(bf16_bits_to_float(ww[j] >> 16), scale) << (16 * j + 8);
-      hi |= e4m3_quantize(bf16_bits_to_float(ww[2 + j] & 0xFFFFu), scale) << (16 * j);
-      hi |= e4m3_quantize(bf16_bits_to_float(ww[2 + j] >> 16), scale) << (16 * j + 8);
+    for (int j = 0; j < 4; ++j) {
+      f[2 * j] = bf16_bits_to_float(ww[j] & 0xFFFFu);
+      f[2 * j + 1] = bf16_bits_to_float(ww[j] >> 16);
     }
-    reinterpret_cast<uint2*>(codes)[i] = make_uint2(lo, hi);
+    reinterpret_cast<uint2*>(codes)[i] = make_uint2(e4m3_quantize4(f, scale),
+                                                    e4m3_quantize4(f + 4, scale));
   }
   // tail
   const int64_t i = nvec * 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) codes[i] = (uint8_t)e4m3_quantize(bf16_bits_to_float(x[i]), scale);
+  if (i < n) {
+    const float f = bf16_bits_to_float(x[i]);
+    codes[i] = (uint8_t)(e4m3_quantize2(f, f, scale) & 0xFFu);
+  }
 }
 
 template <int D>
 static void launch_cache_write(const kvq_cache_desc* c, const void* k, const void* v,
                                int64_t stride, const int64_t* slots, int32_t n,
                                float ks, float vs, hipStream_t st) {
-  constexpr int kRowsPerBlock = 256 / (D / 8);
-  const int64_t rows = (int64_t)n * c->num_kv_heads;
-  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  const dim3 grid((unsigned)(((int64_t)n + kWriteTokens - 1) / kWriteTokens * c->num_kv_heads));
+  constexpr int kThreads = 2 * D;  // 16 tokens x D / 8 lanes
   auto* kk = static_cast<const uint16_t*>(k);
   auto* vv = static_cast<const uint16_t*>(v);
   auto* kp = static_cast<uint8_t*>(c->k_pages);
   auto* vp = static_cast<uint8_t*>(c->v_pages);
   if (c->dtype == KVQ_BF16)
-    cache_write_kernel<D, false, false><<<grid, 256, 0, st>>>(
+    cache_write_kernel<D, false, false><<<grid, kThreads, 0, st>>>(
         kk, vv, stride, slots, n, c->num_kv_heads, kp, vp, nullptr, nullptr, 1.f, 1.f);
   else if (c->mode == KVQ_SCALE_PER_TOKEN_HEAD)
-    cache_write_kernel<D, true, true><<<grid, 256, 0, st>>>(
+    cache_write_kernel<D, true, true><<<grid, kThreads, 0, st>>>(
         kk, vv, stride, slots, n, c->num_kv_heads, kp, vp, c->k_scales, c->v_scales,
         1.f, 1.f);
   else if (c->mode == KVQ_SCALE_PER_KV_HEAD)
-    cache_write_kernel<D, true, false><<<grid, 256, 0, st>>>(
+    cache_write_kernel<D, true, false><<<grid, kThreads, 0, st>>>(
         kk, vv, stride, slots, n, c->num_kv_heads, kp, vp, c->k_scales, c->v_scales,
         1.f, 1.f);
   else
-    cache_write_kernel<D, true, false><<<grid, 256, 0, st>>>(
+    cache_write_kernel<D, true, false><<<grid, kThreads, 0, st>>>(
         kk, vv, stride, slots, n, c->num_kv_heads, kp, vp, nullptr, nullptr, ks, vs);
 }
 
@@ -131,6 +209,9 @@ extern "C" kvq_status kvq_cache_write(const kvq_cache_desc* cache, const void* k
                 (double)k_scale, (double)v_scale);
   if (cache->num_pages == 0)
     return fail(KVQ_ERR_INVALID_ARG, "cache has no pages");
+  if (((int64_t)num_tokens + kWriteTokens - 1) / kWriteTokens * cache->num_kv_heads > 0x7FFFFFFF)
+    return fail(KVQ_ERR_INVALID_ARG, "num_tokens %d x num_kv_heads %d: grid too large",
+                num_tokens, cache->num_kv_heads);
   auto st = static_cast<hipStream_t>(stream);
   switch (cache->head_dim) {
     case 64: launch_cache_write<64>(cache, k, v, token_stride, slot_mapping, num_tokens, k_scale, v_scale, st); break;
