@@ -1036,15 +1036,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   __syncthreads();
   if (!last_lds) return;
 
-  // Level-3 merge over the ns splits, by the last workgroup: wave w takes splits w,
-  // w + 4, ... (in order), lane l the float4 groups l, l + 64, ... of the G x D
-  // outputs; batches of MB splits have all their loads in flight at once.  The four
-  // waves' (M, L, O) then combine in a fixed tree through LDS.
+  // Level-3 merge over the ns splits, by the last workgroup; lane l takes the float4
+  // groups l, l + 64, ... of the G x D outputs, and batches of MB splits have all their
+  // loads in flight at once.  When every split fits in one batch, wave 0 folds them all
+  // in split order and the other waves leave (one round trip, no LDS tree); otherwise
+  // wave w takes splits w, w + 4, ... (in order) and the four waves' (M, L, O) combine
+  // in a fixed tree through LDS.  Only splits that exist are loaded.
   constexpr int E4L = (NE4 + kWave - 1) / kWave;
   // splits per batch (its loads all in flight); kernels held to three waves per SIMD
   // keep the batch small to stay within their register budget
   constexpr int MB_REGS = decode_waves_per_eu<D, G, kFp8, kPTH>() >= 3 ? 4 : 16;
   constexpr int MB = MB_REGS / E4L > 1 ? MB_REGS / E4L : 1;
+  const bool solo = ns <= MB;  // workgroup-uniform
+  if (solo && wave != 0) return;
+  const int jfirst = solo ? 0 : wave;
+  const int jstep = solo ? 1 : kWaves;
   float Mx[E4L], Ls[E4L];
   float4 Os[E4L];
 #pragma unroll
@@ -1065,56 +1071,60 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     l0 = l0 * fa + l1 * fb;
     m0 = mn;
   };
-  for (int j0 = wave; j0 < ns; j0 += kWaves * MB) {
+  for (int j0 = jfirst; j0 < ns; j0 += jstep * MB) {
     float4 ov[MB][E4L];
     float2 mlv[MB][E4L];
 #pragma unroll
     for (int u = 0; u < MB; ++u) {
-      const int j = min(j0 + kWaves * u, ns - 1);
+      const int j = j0 + jstep * u;
+      if (j < ns) {
 #pragma unroll
-      for (int k = 0; k < E4L; ++k) {
-        const int e4 = min(lane + kWave * k, NE4 - 1);
-        const float* op = a.o_part + (prow + j) * G * D + 4 * e4;
-        const float2 lo2 = load_agent2(op), hi2 = load_agent2(op + 2);
-        ov[u][k] = make_float4(lo2.x, lo2.y, hi2.x, hi2.y);
-        mlv[u][k] = load_agent2(a.ml_part + ((prow + j) * G + (4 * e4) / D) * 2);
+        for (int k = 0; k < E4L; ++k) {
+          const int e4 = min(lane + kWave * k, NE4 - 1);
+          const float* op = a.o_part + (prow + j) * G * D + 4 * e4;
+          const float2 lo2 = load_agent2(op), hi2 = load_agent2(op + 2);
+          ov[u][k] = make_float4(lo2.x, lo2.y, hi2.x, hi2.y);
+          mlv[u][k] = load_agent2(a.ml_part + ((prow + j) * G + (4 * e4) / D) * 2);
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < MB; ++u)
 #pragma unroll
       for (int k = 0; k < E4L; ++k)
-        if (j0 + kWaves * u < ns) combine(Mx[k], Ls[k], Os[k], mlv[u][k].x, mlv[u][k].y, ov[u][k]);
+        if (j0 + jstep * u < ns) combine(Mx[k], Ls[k], Os[k], mlv[u][k].x, mlv[u][k].y, ov[u][k]);
   }
   // tree over the waves: waves [h, 2h) hand their (M, L, O) to waves [0, h)
   float* mslot = merge_lds;                        // [2][NE4] M, L pairs
   float4* oslot = reinterpret_cast<float4*>(merge_lds + 4 * NE4);  // [2][NE4]
+  if (!solo) {
 #pragma unroll
-  for (int half = kWaves / 2; half >= 1; half /= 2) {
-    if (wave >= half && wave < 2 * half) {
+    for (int half = kWaves / 2; half >= 1; half /= 2) {
+      if (wave >= half && wave < 2 * half) {
 #pragma unroll
-      for (int k = 0; k < E4L; ++k) {
-        const int e4 = lane + kWave * k;
-        if (e4 < NE4) {
-          const int i = (wave - half) * NE4 + e4;
-          mslot[2 * i] = Mx[k];
-          mslot[2 * i + 1] = Ls[k];
-          oslot[i] = Os[k];
+        for (int k = 0; k < E4L; ++k) {
+          const int e4 = lane + kWave * k;
+          if (e4 < NE4) {
+            const int i = (wave - half) * NE4 + e4;
+            mslot[2 * i] = Mx[k];
+            mslot[2 * i + 1] = Ls[k];
+            oslot[i] = Os[k];
+          }
         }
       }
-    }
-    __syncthreads();
-    if (wave < half) {
+      __syncthreads();
+      if (wave < half) {
 #pragma unroll
-      for (int k = 0; k < E4L; ++k) {
-        const int e4 = lane + kWave * k;
-        if (e4 < NE4) {
-          const int i = wave * NE4 + e4;
-          combine(Mx[k], Ls[k], Os[k], mslot[2 * i], mslot[2 * i + 1], oslot[i]);
+        for (int k = 0; k < E4L; ++k) {
+          const int e4 = lane + kWave * k;
+          if (e4 < NE4) {
+            const int i = wave * NE4 + e4;
+            combine(Mx[k], Ls[k], Os[k], mslot[2 * i], mslot[2 * i + 1], oslot[i]);
+          }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
   if (wave == 0) {
 #pragma unroll
