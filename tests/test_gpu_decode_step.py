@@ -147,3 +147,14 @@ def test_decode_step_window_fp8(kvq):
                                       window=128)
     log("decode step fp8 window 128")
     check_step(kvq, case, "fp8", "per_token_head", steps=3)
+
+
+@pytest.mark.parametrize("D,Hq,mode", [(128, 32, "per_token_head"), (64, 64, "per_tensor")])
+def test_decode_step_eight_sequences(kvq, D, Hq, mode):
+    """8 sequences x 8 KV heads (the Llama- and gpt-oss-shaped head layouts), ragged:
+    several splits per sequence, two steps in a row."""
+    case = workloads.make_decode_case(431 + D, [1, 16, 17, 333, 1029, 2048, 40, 700], Hq, 8,
+                                      D, table="perm")
+    ks, vs = (1.0, 1.0) if mode == "per_token_head" else (0.05, 0.04)
+    log(f"decode step 8 sequences {mode} D={D} Hq={Hq}")
+    check_step(kvq, case, "fp8", mode, k_scale=ks, v_scale=vs, steps=2)
