@@ -219,9 +219,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr bool kMfma = decode_uses_mfma<D, G, kFp8>();
   constexpr int QW = G * D / 2;                  // query as bf16 pairs
   constexpr int NE4 = G * D / 4;                 // float4 groups of a (b, g) output
+  // One-pass wave merge: every wave's G x D result fits an LDS slot of its own (32 KB for
+  // the four), so one barrier separates the writes from a combine that all four waves
+  // share; larger outputs take a tree through two slots.
+  constexpr bool kOnePass = kWaves * G * D * 4 <= 32768;
   // wave-merge slots (floats): the waves' partial outputs, later the split merge's
   // (M, L, O) per float4 group of two waves
-  constexpr int MERGE = (kWaves / 2) * G * D > 12 * NE4 ? (kWaves / 2) * G * D : 12 * NE4;
+  constexpr int SLOTS = (kOnePass ? kWaves : kWaves / 2) * G * D;
+  constexpr int MERGE = SLOTS > 12 * NE4 ? SLOTS : 12 * NE4;
   __shared__ uint32_t q_lds_all[kWaves][QW];
   __shared__ uint32_t w_lds_all[kWaves][S::W_WORDS];
   __shared__ float ml_lds[kWaves][G][2];
@@ -634,6 +639,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       lw[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                              __builtin_bit_cast(int, lt), hh));
     }
+    if constexpr (kOnePass) {
+      // the wave's result, scaled per head, straight into its slot ([G][D] layout):
+      // accumulator row 4 qg + rr is head 4 qg + rr, channel 16 blk + n
+      float fh[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+        fh[hh] = !kPTH ? v_scale_g
+                       : (m_all[hh] == -INFINITY ? 0.0f
+                                                 : __builtin_amdgcn_exp2f(mv_all[hh] - m_all[hh]));
+      float* slot = merge_lds + wave * G * D;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int hr = 4 * qg + rr;
+        float f = 0.0f;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) f = hr == hh ? fh[hh] : f;
+        if (hr < G) {
+#pragma unroll
+          for (int blk = 0; blk < NBLK; ++blk) slot[hr * D + 16 * blk + n] = acc_o[blk][rr] * f;
+        }
+      }
+    } else {
     // two waves at a time through merge_lds (room for two G x D blocks)
 #pragma unroll
     for (int round = 0; round < 2; ++round) {
@@ -658,6 +685,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       }
       __syncthreads();
     }
+    }  // two-round conversion
   } else {
   // One page's inputs for this lane: K rows of its token slots, V rows of its
   // channels, and the per-token scales of the scores it will hold.
@@ -943,14 +971,94 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   }  // vector-ALU path
 
   // ---- this wave's result relative to m_all: o = acc * f, l ------------------------
+  // (the one-pass matrix-core form has already written its scaled result to LDS)
+  if constexpr (!(kOnePass && kMfma)) {
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    float f = kFp8 && !kPTH ? v_scale_g : 1.0f;
-    if constexpr (kFp8 && kPTH)
-      f = m_all[hh] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv_all[hh] - m_all[hh]);
+    for (int hh = 0; hh < G; ++hh) {
+      float f = kFp8 && !kPTH ? v_scale_g : 1.0f;
+      if constexpr (kFp8 && kPTH)
+        f = m_all[hh] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv_all[hh] - m_all[hh]);
 #pragma unroll
-    for (int dd = 0; dd < S::DPL; ++dd) acc[hh][dd] *= f;
+      for (int dd = 0; dd < S::DPL; ++dd) acc[hh][dd] *= f;
+    }
   }
+
+  const int64_t prow = (int64_t)ug * a.splits;  // split partial rows of (b, g)
+  if constexpr (kOnePass) {
+    // ---- merge the four waves in one pass (level 3, fixed order) ------------------
+    // Element e = 64 w + l + 256 k of the G x D output (head e / D, the same for every
+    // lane of wave w since D >= 64) is the sum over waves v = 0..3 of slot_v[e] scaled
+    // from v's reference to the common one; wave w combines and stores its elements.
+    if constexpr (!kMfma) {
+      float* slot = merge_lds + wave * G * D;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int dd = 0; dd < S::DPL; ++dd) slot[hh * D + lane + kWave * dd] = acc[hh][dd];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        ml_lds[wave][hh][0] = m_all[hh];
+        ml_lds[wave][hh][1] = lw[hh];
+      }
+    }
+    __syncthreads();
+    constexpr int EPW = (G * D + kThreads - 1) / kThreads;  // elements per lane
+    static_assert(D >= kWave, "one head per wave and element group");
+    float val[EPW];
+    float Mh[EPW], Lh[EPW];
+#pragma unroll
+    for (int k = 0; k < EPW; ++k) {
+      const int e0 = kWave * wave + kThreads * k;   // wave-uniform
+      const int hh = e0 < G * D ? e0 / D : 0;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) mx = fmaxf(mx, ml_lds[v][hh][0]);
+      float sum = 0.0f, ls = 0.0f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        const float mv = ml_lds[v][hh][0];
+        const float c = mv == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv - mx);
+        ls += ml_lds[v][hh][1] * c;
+        if (e0 < G * D) sum += merge_lds[v * G * D + e0 + lane] * c;
+      }
+      val[k] = sum;
+      Mh[k] = mx;
+      Lh[k] = ls;
+    }
+    if (ns == 1) {  // the only split: normalise and store directly
+#pragma unroll
+      for (int k = 0; k < EPW; ++k) {
+        const int e0 = kWave * wave + kThreads * k;
+        if (e0 < G * D)
+          store_out(a.out, a.out_f32, row0 * D + e0 + lane, Lh[k] > 0.0f ? val[k] / Lh[k] : 0.0f);
+      }
+      return;
+    }
+#pragma unroll
+    for (int k = 0; k < EPW; ++k) {
+      const int e0 = kWave * wave + kThreads * k;
+      if (e0 < G * D) {
+        store_agent(a.o_part + (prow + s) * G * D + e0 + lane, val[k]);
+        // one (M, L) pair per head, by the lane holding the head's first channel
+        if ((e0 + lane) % D == 0)
+          store_agent2(a.ml_part + ((prow + s) * G + (e0 + lane) / D) * 2, Mh[k], Lh[k]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (wave == 0) {
+      int done = 0;
+      if (lane == 0)
+        done = __hip_atomic_fetch_add(&a.counters[ug], 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      done = __builtin_amdgcn_readfirstlane(done);
+      if (lane == 0) last_lds = done == ns - 1;
+    }
+    __syncthreads();
+    if (!last_lds) return;
+  } else {
 
   // ---- merge the four waves (level 3, fixed order) --------------------------------
   if (lane == 0) {
@@ -1016,7 +1124,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // Partials are stored with agent-scope atomics, i.e. written through to the device
   // coherence point; the wave waits until they are performed before it counts itself
   // done, and the last workgroup reads them back with agent-scope loads.
-  const int64_t prow = (int64_t)ug * a.splits;  // partial rows of (b, g)
   if (wave == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -1035,6 +1142,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   }
   __syncthreads();
   if (!last_lds) return;
+  }  // wave merge and split partial
 
   // Level-3 merge over the ns splits, by the last workgroup; lane l takes the float4
   // groups l, l + 64, ... of the G x D outputs, and batches of MB splits have all their
@@ -1043,9 +1151,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // wave w takes splits w, w + 4, ... (in order) and the four waves' (M, L, O) combine
   // in a fixed tree through LDS.  Only splits that exist are loaded.
   constexpr int E4L = (NE4 + kWave - 1) / kWave;
-  // splits per batch (its loads all in flight); kernels held to three waves per SIMD
-  // keep the batch small to stay within their register budget
-  constexpr int MB_REGS = decode_waves_per_eu<D, G, kFp8, kPTH>() >= 3 ? 4 : 16;
+  // splits per batch (its loads all in flight; the page loop's registers are free here)
+  constexpr int MB_REGS = 16;
   constexpr int MB = MB_REGS / E4L > 1 ? MB_REGS / E4L : 1;
   const bool solo = ns <= MB;  // workgroup-uniform
   if (solo && wave != 0) return;
