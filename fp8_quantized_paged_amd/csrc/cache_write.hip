@@ -11,7 +11,9 @@
 // Work split: a workgroup owns 16 consecutive tokens of the call and one KV head;
 // D/8 lanes own a (token, head) row, 8 consecutive values (one 16-byte load) each.
 // The row maximum is reduced across those lanes; every lane then quantises its 8
-// values.  K rows go token-major (8 codes = one 8-byte store per lane).  V rows go
+// values (per-token-head rows: the quotient from one reciprocal per row and two fused
+// multiply-adds per value, whose codes equal those of the division -- see
+// e4m3_quantize4_row).  K rows go token-major (8 codes = one 8-byte store per lane).  V rows go
 // dim-major: when the 16 tokens fill one page in order (slots 16 p .. 16 p + 15, the
 // usual bulk fill) the codes are transposed through LDS and every channel row of the
 // page tile is written with one 16-byte store (32 bytes for bf16); otherwise each
@@ -42,12 +44,21 @@ __global__ __launch_bounds__(2 * D) void cache_write_kernel(
   const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)num_heads) * kWriteTokens;
   const int64_t t = t0 + i;
   const int64_t slot = t < num_tokens ? slots[t] : -1;
+  // the rows do not depend on the slots: their loads go out with the slot loads
+  const int64_t src = t * token_stride + (int64_t)h * D;
+  uint4 kw = make_uint4(0u, 0u, 0u, 0u), vw = kw;
+  if (t < num_tokens) {
+    kw = *reinterpret_cast<const uint4*>(k + src + c * 8);
+    vw = *reinterpret_cast<const uint4*>(v + src + c * 8);
+  }
   // whole-page fast path: 16 tokens present, slots 16 p + i in order
   const int64_t slot0 = t0 + kWriteTokens <= num_tokens ? slots[t0] : -1;
   const bool page_run = __syncthreads_and(slot0 >= 0 && (slot0 & 15) == 0 &&
                                           slot == slot0 + i);
   // per-KV-head mode: k_scales / v_scales hold one scale per head (per-tensor: null)
   float ks = k_scale, vs = v_scale;
+  float kr = 0.0f, vr = 0.0f;  // per-token-head: 1 / scale for the fast quotient
+  bool kfast = false, vfast = false;
   if constexpr (kFp8 && !kPerTokenHead) {
     if (k_scales != nullptr) {
       ks = k_scales[h];
@@ -58,7 +69,6 @@ __global__ __launch_bounds__(2 * D) void cache_write_kernel(
     // any slot pattern: every (token, head) row on its own (rows of skipped tokens
     // simply do nothing; whole rows of lanes agree)
     if (slot >= 0) {
-      const int64_t src = t * token_stride + (int64_t)h * D;
       store_token_row<D, kFp8, kPerTokenHead>(k + src, v + src, c, (slot >> 4) * num_heads + h,
                                               (int)(slot & 15), k_pages, v_pages, k_scales,
                                               v_scales, ks, vs);
@@ -66,9 +76,6 @@ __global__ __launch_bounds__(2 * D) void cache_write_kernel(
     return;
   }
   const int64_t tile = (slot0 >> 4) * num_heads + h;  // the page's (page, head) tile
-  const int64_t src = t * token_stride + (int64_t)h * D;
-  const uint4 kw = *reinterpret_cast<const uint4*>(k + src + c * 8);
-  const uint4 vw = *reinterpret_cast<const uint4*>(v + src + c * 8);
   if constexpr (!kFp8) {
     // bf16 cache: K row copied, V values transposed through LDS
     *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(k_pages) + (tile * kPage + i) * D +
@@ -109,10 +116,15 @@ __global__ __launch_bounds__(2 * D) void cache_write_kernel(
         k_scales[tile * kPage + i] = ks;
         v_scales[tile * kPage + i] = vs;
       }
+      kfast = row_quot_fast(ka);
+      vfast = row_quot_fast(va);
+      if (kfast) kr = 1.0f / ks;
+      if (vfast) vr = 1.0f / vs;
     }
     *reinterpret_cast<uint2*>(k_pages + (tile * kPage + i) * D + c * 8) =
-        make_uint2(e4m3_quantize4(kf, ks), e4m3_quantize4(kf + 4, ks));
-    const uint32_t vlo = e4m3_quantize4(vf, vs), vhi = e4m3_quantize4(vf + 4, vs);
+        make_uint2(e4m3_quantize4_row(kf, ks, kr, kfast), e4m3_quantize4_row(kf + 4, ks, kr, kfast));
+    const uint32_t vlo = e4m3_quantize4_row(vf, vs, vr, vfast);
+    const uint32_t vhi = e4m3_quantize4_row(vf + 4, vs, vr, vfast);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       vt[(c * 8 + j) * kWriteTokens + i] = (uint8_t)((j < 4 ? vlo : vhi) >> (8 * (j % 4)));

@@ -62,12 +62,7 @@ __host__ __device__ __forceinline__ uint32_t e4m3_quantize(float x, float s) {
 // an MI355X), so the codes equal e4m3_quantize's; it does two values in one instruction
 // where the integer encoder takes about a dozen per value.  x / 1 is x, so a unit scale
 // skips the division.
-__device__ __forceinline__ uint32_t e4m3_quantize2(float x0, float x1, float s) {
-  float q0 = x0, q1 = x1;
-  if (s != 1.0f) {
-    q0 = x0 / s;
-    q1 = x1 / s;
-  }
+__device__ __forceinline__ uint32_t e4m3_codes2(float q0, float q1, float x0, float x1) {
   const float c0 = __builtin_amdgcn_fmed3f(q0, -448.0f, 448.0f);
   const float c1 = __builtin_amdgcn_fmed3f(q1, -448.0f, 448.0f);
   uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false) & 0xFFFFu;
@@ -75,9 +70,37 @@ __device__ __forceinline__ uint32_t e4m3_quantize2(float x0, float x1, float s) 
   if (q1 != q1) w = (w & 0x00FFu) | ((0x7Fu | ((__float_as_uint(x1) >> 24) & 0x80u)) << 8);
   return w;
 }
+__device__ __forceinline__ uint32_t e4m3_quantize2(float x0, float x1, float s) {
+  if (s == 1.0f) return e4m3_codes2(x0, x1, x0, x1);
+  return e4m3_codes2(x0 / s, x1 / s, x0, x1);
+}
 // Four codes (bytes 0..3) of x[0..3] / s.
 __device__ __forceinline__ uint32_t e4m3_quantize4(const float* x, float s) {
   return e4m3_quantize2(x[0], x[1], s) | (e4m3_quantize2(x[2], x[3], s) << 16);
+}
+
+// x / s for the values of one per-token-head row, s = fl32(amax / 448), from r = 1 / s
+// (IEEE, once per row) and two fused multiply-adds per value: q0 = x r, e = x - q0 s
+// (exact), q = q0 + e r (Markstein's correction step), with the sign of x so that -0
+// stays -0.  Where it is used -- 2^-100 <= amax < inf, |x| <= amax -- its e4m3 code
+// equals that of the IEEE quotient for every bf16 x and every bf16 amax (all such pairs
+// checked on an MI355X; the quotients themselves differ in about 0.1% of them, never
+// across an e4m3 rounding boundary).  Rows with smaller, infinite or NaN maxima take the
+// division (row_quot_fast false).
+__device__ __forceinline__ bool row_quot_fast(uint32_t amax_bits) {
+  return amax_bits >= 0x0D800000u && amax_bits < 0x7F800000u;  // [2^-100, inf)
+}
+__device__ __forceinline__ float row_quot(float x, float s, float r) {
+  const float q0 = x * r;
+  return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0), x);
+}
+// Four codes (bytes 0..3) of a per-token-head row's x[0..3] / s (r = 1 / s when fast).
+__device__ __forceinline__ uint32_t e4m3_quantize4_row(const float* x, float s, float r,
+                                                       bool fast) {
+  if (!fast) return e4m3_quantize4(x, s);
+  const uint32_t lo = e4m3_codes2(row_quot(x[0], s, r), row_quot(x[1], s, r), x[0], x[1]);
+  const uint32_t hi = e4m3_codes2(row_quot(x[2], s, r), row_quot(x[3], s, r), x[2], x[3]);
+  return lo | (hi << 16);
 }
 
 // |x| maximum that propagates NaN (integer max of the magnitude bit patterns).
@@ -250,6 +273,8 @@ __device__ __forceinline__ void store_token_row(const uint16_t* k, const uint16_
       vf[2 * i + 1] = bf16_bits_to_float(vv[i] >> 16);
     }
     float ks = k_scale, vs = v_scale;
+    float kr = 0.0f, vr = 0.0f;     // per-token-head: 1 / scale for the fast quotient
+    bool kfast = false, vfast = false;
     if constexpr (kPerTokenHead) {
       uint32_t ka = 0, va = 0;
 #pragma unroll
@@ -268,10 +293,15 @@ __device__ __forceinline__ void store_token_row(const uint16_t* k, const uint16_
         k_scales[tile * kPage + off] = ks;
         v_scales[tile * kPage + off] = vs;
       }
+      kfast = row_quot_fast(ka);
+      vfast = row_quot_fast(va);
+      if (kfast) kr = 1.0f / ks;
+      if (vfast) vr = 1.0f / vs;
     }
     *reinterpret_cast<uint2*>(k_pages + (tile * kPage + off) * D + c * 8) =
-        make_uint2(e4m3_quantize4(kf, ks), e4m3_quantize4(kf + 4, ks));
-    const uint32_t vlo = e4m3_quantize4(vf, vs), vhi = e4m3_quantize4(vf + 4, vs);
+        make_uint2(e4m3_quantize4_row(kf, ks, kr, kfast), e4m3_quantize4_row(kf + 4, ks, kr, kfast));
+    const uint32_t vlo = e4m3_quantize4_row(vf, vs, vr, vfast);
+    const uint32_t vhi = e4m3_quantize4_row(vf + 4, vs, vr, vfast);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       v_pages[(tile * D + c * 8 + i) * kPage + off] = (uint8_t)((i < 4 ? vlo : vhi) >> (8 * (i % 4)));

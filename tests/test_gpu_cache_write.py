@@ -186,3 +186,50 @@ def test_cache_write_full_size_sampled(kvq, which):
         return
     want = oracle_pools(case, mode, rows=rows)
     _check_pools(got, want, case.slots[rows])
+
+
+def _rows_for_maxima(maxima, D):
+    """Per-token-head rows: each row's maximum magnitude is one of ``maxima`` (its first
+    value, signs alternating between rows), the other D - 1 values run through every
+    finite bf16 x with |x| <= that maximum, so every (x, row maximum) pair of the list
+    occurs.  Returns float32 [rows][D]."""
+    allx = all_bf16()
+    rows = []
+    for k, a in enumerate(maxima):
+        xs = allx[np.isfinite(allx) & (np.abs(allx) <= a)]
+        for i in range(0, len(xs), D - 1):
+            r = np.zeros(D, np.float32)
+            chunk = xs[i:i + D - 1]
+            r[1:1 + len(chunk)] = chunk
+            r[0] = a if (len(rows) + k) % 2 == 0 else -a
+            rows.append(r)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("ordered", [True, False])
+def test_cache_write_per_token_head_row_maxima(kvq, ordered):
+    """Per-token-head codes are bit-exact over every bf16 value against a set of row
+    maxima: the ends of the fast-quotient range (2^-100 and the bf16 values beside it,
+    the largest finite bf16), a subnormal maximum (division path), 1 and 448, and 40
+    seeded maxima across the exponent range.  ordered: slots in page order (the
+    whole-page LDS path); otherwise scattered slots (the single-row path)."""
+    D, H = 128, 8
+    rng = np.random.default_rng(77)
+    bits = [0x0D80, 0x0D7F, 0x0D81, 0x0001, 0x3F80, 0x43E0, 0x7F7F]
+    bits += list(rng.integers(0x0080, 0x7F7F, size=40))
+    maxima = (np.array(bits, dtype=np.uint32) << 16).view(np.float32)
+    rows = _rows_for_maxima(maxima, D)
+    T = (len(rows) + H - 1) // H
+    pad = np.zeros((T * H - len(rows), D), np.float32)
+    x = np.concatenate([rows, pad]).reshape(T, H, D)
+    v = x[::-1].copy()                       # V: the same rows, other tokens
+    P = (T + 15) // 16
+    slots = np.arange(T, dtype=np.int64)
+    if not ordered:
+        slots = rng.permutation(P * 16)[:T].astype(np.int64)
+    log(f"per-token-head row maxima: {len(rows)} rows, ordered={ordered}")
+    c = kvq.PagedCache(P, H, D, "fp8", "per_token_head")
+    kvq.cache_write(c, dev_bf16(x), dev_bf16(v), dev(slots))
+    pools = ocache.new_pools(P, H, D)
+    ocache.cache_write(pools, x, v, slots, "per_token_head", 1.0, 1.0)
+    _check_pools(read_pools(c), pools, slots)
