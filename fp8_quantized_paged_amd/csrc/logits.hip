@@ -12,7 +12,8 @@
 // v_mfma_f32_32x32x16_bf16 (exact products, float32 sums), unscaled.
 //
 // Work split.  A workgroup owns one (request, KV head) and `iters` consecutive 128-key
-// tiles (1 to 8, chosen so that the launch has some 640 workgroups) (each of its 4 waves 32 keys of a tile, one 32-key MFMA block); the request's
+// tiles (1 to 8, chosen so that the launch has about three workgroups per CU), each of
+// its 4 waves 32 keys of a tile (one 32-key MFMA block); the request's
 // query rows times the group's query heads ("pairs") are the MFMA columns, 32 at a
 // time, staged once per chunk in LDS.  The tiles are software-pipelined: page ids two
 // tiles ahead and key rows one tile ahead are in flight while a tile is computed, so
@@ -38,7 +39,11 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTileKeys = kWaves * 32;  // keys per tile (32 per wave)
 constexpr int kMaxIters = 8;            // tiles per workgroup, at most
-constexpr int kTargetGroups = 640;      // workgroups a launch aims for
+// Workgroups a launch aims for: three per CU, what the kernel's registers keep resident
+// (124 VGPRs) -- the busiest CUs then hold the fewest tiles.  Indexer shape (32 x 20,000
+// keys, D 128, 5,024 tiles): 736 workgroups of 7 tiles 26.2 us; 640 of 8 (up to 24 tiles
+// on a CU) 28.5 us; 512 of 10 29.4 us; 1,024 33.5 us (more than stay resident).
+constexpr int kTargetGroups = 768;
 
 struct LogitsArgs {
   const uint16_t* q;          // bf16 [rows][Hq][D]
