@@ -12,14 +12,15 @@
 // v_mfma_f32_32x32x16_bf16 (exact products, float32 sums), unscaled.
 //
 // Work split.  A workgroup owns one (request, KV head) and `iters` consecutive 128-key
-// tiles (1 to 8, chosen so that the launch has about three workgroups per CU), each of
+// tiles (1 to 12, chosen so that the launch has about two workgroups per CU), each of
 // its 4 waves 32 keys of a tile (one 32-key MFMA block); the request's
 // query rows times the group's query heads ("pairs") are the MFMA columns, 32 at a
-// time, staged once per chunk in LDS.  The tiles are software-pipelined: page ids two
-// tiles ahead and key rows one tile ahead are in flight while a tile is computed, so
-// the block-table -> key -> store chain of dependent memory round trips is paid once
-// per workgroup rather than once per tile.  The contraction index is assigned so that lane group hg (lanes
-// 32 hg ..) holds the contiguous half D/2 hg .. D/2 hg + D/2 - 1 of every key and
+// time, staged once per chunk in LDS.  The tiles are software-pipelined: a wave loads
+// all its page ids at once, then keeps two tiles' key rows in flight (a three-buffer
+// register ring) while one is computed, so the block-table -> key -> store chain of
+// dependent memory round trips is paid once per workgroup rather than once per tile.
+// The contraction index is assigned so that lane group hg (lanes 32 hg ..) holds the
+// contiguous half D/2 hg .. D/2 hg + D/2 - 1 of every key and
 // query row: step s, element e <-> dim D/2 hg + 8 s + e (both operands agree, which
 // is all a contraction needs), so each lane's operands are plain 16-byte loads.
 #include <algorithm>
@@ -38,12 +39,14 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTileKeys = kWaves * 32;  // keys per tile (32 per wave)
-constexpr int kMaxIters = 8;            // tiles per workgroup, at most
-// Workgroups a launch aims for: three per CU, what the kernel's registers keep resident
-// (124 VGPRs) -- the busiest CUs then hold the fewest tiles.  Indexer shape (32 x 20,000
-// keys, D 128, 5,024 tiles): 736 workgroups of 7 tiles 26.2 us; 640 of 8 (up to 24 tiles
-// on a CU) 28.5 us; 512 of 10 29.4 us; 1,024 33.5 us (more than stay resident).
-constexpr int kTargetGroups = 768;
+constexpr int kMaxIters = 12;           // tiles per workgroup, at most (2 page ids per lane pair)
+// Workgroups a launch aims for: two per CU, all resident at once (two waves per SIMD),
+// each keeping two tiles' keys in flight per wave (the kernel is bound per CU by the
+// loads it has in flight, so the CU holding the most tiles sets the time).  Indexer
+// shape (32 x 20,000 keys, D 128, 5,024 tiles), round-robin A/B: 512 workgroups of 10
+// tiles, tile ring of three 22.2 us; one tile in flight: 736 workgroups of 7 tiles 26.2
+// us, 640 of 8 28.5 us; the ring at three workgroups per CU 28.4 us.
+constexpr int kTargetGroups = 512;
 
 struct LogitsArgs {
   const uint16_t* q;          // bf16 [rows][Hq][D]
@@ -71,8 +74,11 @@ __device__ __forceinline__ half8_t codes_to_f16(uint32_t lo, uint32_t hi) {
 }
 
 // kMode: 0 per-tensor, 1 per-token-head, 2 per-KV-head (FP8 only)
+// Two waves per SIMD: a launch's workgroups (two per CU) stay resident at once.  (A
+// three-wave budget spilled the ring at head_dim 128.)
 template <int D, bool kFp8, int kMode>
-__global__ __launch_bounds__(kThreads) void logits_kernel(const LogitsArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
+logits_kernel(const LogitsArgs a) {
   constexpr int ES = kFp8 ? 1 : 2;       // bytes per element
   constexpr int HB = D / 2 * ES;         // bytes of a lane group's half row
   constexpr int NV = HB / 16;            // 16-byte loads per half row
@@ -96,24 +102,35 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const LogitsArgs a) {
   const int* bt = a.block_table + (int64_t)b * a.bt_stride;
   const int key_base = grp0 * a.iters * kTileKeys + wave * 32;  // wave's key of tile 0
 
-  // per-tile loads of this wave: the page ids of its 2 pages (lanes 0 and 1), then its
-  // lane's half row of key key_base + 128 it + col and the scales of its output keys
-  // (keys 8 q + 4 hg + e of the block, register 4 q + e: 4 consecutive keys, one page)
+  // All of the wave's page ids at once (lane j: page j % 2 of tile j / 2, j < 2 iters),
+  // so no block-table round trip sits between one tile and the next.
+  int pid_all = 0;
+  {
+    const int kw = key_base + (lane / 2) * kTileKeys;
+    if (lane < 2 * a.iters && kw < a.out_stride && npages > 0)
+      pid_all = bt[min(kw / kPage + (lane & 1), npages - 1)];
+  }
+  // per-tile loads of this wave: its lane's half row of key key_base + 128 it + col and
+  // (per-token-head) the scale of key col of the wave's 32; the scales an output lane
+  // needs (keys 8 q + 4 hg + e, register 4 q + e) come from those lanes at the store.
+  // Tiles past the workgroup's range (it >= iters) load nothing.
   struct Tile {
     uint4 k[NV];
-    float4 sc[4];
+    float sc;
   };
-  auto page_id = [&](int it) {
+  auto load_tile = [&](int it, Tile& t) {
     const int kw = key_base + it * kTileKeys;
-    int pid = 0;
-    if (kw < a.out_stride && npages > 0) pid = bt[min(kw / kPage + (lane & 1), npages - 1)];
-    return pid;
-  };
-  auto load_tile = [&](int it, int pid, Tile& t) {
-    const int kw = key_base + it * kTileKeys;
-    const int pg[2] = {__builtin_amdgcn_readlane(pid, 0), __builtin_amdgcn_readlane(pid, 1)};
+    const bool tile_ok = it < a.iters && kw < a.out_stride;
+    const int pi = 2 * min(it, kMaxIters - 1);
+    const int pg[2] = {__builtin_amdgcn_readlane(pid_all, pi),
+                       __builtin_amdgcn_readlane(pid_all, pi + 1)};
     const int key = kw + col;
-    if (kw < a.out_stride && key < L) {
+    t.sc = 0.0f;
+    if constexpr (kFp8 && kMode == 1) {
+      if (tile_ok && key < L)  // slots past L hold unwritten scales: never read
+        t.sc = a.k_scales[((int64_t)pg[col / 16] * H + g) * kPage + key % kPage];
+    }
+    if (tile_ok && key < L) {
       const int page = col < 16 ? pg[0] : pg[1];
       const uint8_t* row = a.k_pages + ((((int64_t)page * H + g) * kPage + key % kPage) * D) * ES;
 #pragma unroll
@@ -122,20 +139,10 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const LogitsArgs a) {
 #pragma unroll
       for (int v = 0; v < NV; ++v) t.k[v] = make_uint4(0, 0, 0, 0);
     }
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int k0 = kw + 8 * q4 + 4 * hg;
-      t.sc[q4] = make_float4(a.k_scale, a.k_scale, a.k_scale, a.k_scale);
-      if constexpr (kFp8 && kMode == 1) {
-        if (kw < a.out_stride && k0 < L)  // slots past L hold unwritten scales: masked
-          t.sc[q4] = *reinterpret_cast<const float4*>(
-              a.k_scales + ((int64_t)pg[q4 / 2] * H + g) * kPage + k0 % kPage);
-      } else if constexpr (kFp8 && kMode == 2) {
-        const float hs = a.k_scales[g];
-        t.sc[q4] = make_float4(hs, hs, hs, hs);
-      }
-    }
   };
+  // per-tensor / per-KV-head: one K scale for the head
+  float k_scale_h = a.k_scale;
+  if constexpr (kFp8 && kMode == 2) k_scale_h = a.k_scales[g];
 
   const bool unit_q = a.q_scale == 1.0f;
   for (int p0 = 0; p0 < npairs; p0 += 32) {
@@ -170,53 +177,61 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const LogitsArgs a) {
     const int pr = r0 + (pair_ok ? p / G : 0), ph = g * G + (pair_ok ? p % G : 0);
     const int vis = pair_ok ? min(a.row_lens[pr], L) : 0;
     float* orow = a.out + ((int64_t)pr * a.num_q_heads + ph) * a.out_stride;
-    int pid_next = page_id(0);
-    Tile cur;
-    load_tile(0, pid_next, cur);
-    pid_next = page_id(1);
+    // Ring of kRing tile buffers, fully unrolled so every buffer stays a named register
+    // set: kRing - 1 tiles' key rows are in flight while one is computed.
+    constexpr int kRing = 3;
+    Tile ring[kRing];
+#pragma unroll
+    for (int r = 0; r < kRing - 1; ++r) load_tile(r, ring[r]);
     __syncthreads();
     // B operand of this lane (pair col): its half row, kept for all tiles
     const uint8_t* qrow = q_lds + col * QS + HB * hg;
-    for (int it = 0; it < a.iters; ++it) {
+    // this wave's tiles: it < nt (a.iters, fewer where the row ends first)
+    const int nt = min(a.iters, max(0, (a.out_stride - key_base + kTileKeys - 1) / kTileKeys));
+    auto compute_store = [&](int it, const Tile& t) {
       const int kw = key_base + it * kTileKeys;
-      if (kw >= a.out_stride) break;  // wave-uniform; later tiles start further on
-      Tile nxt;
-      if (it + 1 < a.iters) {
-        load_tile(it + 1, pid_next, nxt);
-        pid_next = page_id(it + 2);
-      }
       v16f acc = (v16f){};
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         if constexpr (kFp8) {
           const uint2 qc = *reinterpret_cast<const uint2*>(qrow + 8 * s);
-          const uint4 kv = cur.k[s / 2];  // key bytes 8 s .. 8 s + 7 of the half row
+          const uint4 kv = t.k[s / 2];  // key bytes 8 s .. 8 s + 7 of the half row
           const half8_t ka = (s & 1) ? codes_to_f16(kv.z, kv.w) : codes_to_f16(kv.x, kv.y);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, codes_to_f16(qc.x, qc.y), acc, 0, 0, 0);
         } else {
           const bf16x8_t qb =
               __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + 16 * s));
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur.k[s]),
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, t.k[s]),
                                                         qb, acc, 0, 0, 0);
         }
       }
-      // ---- scale, mask (keys past the row's visible length -> -inf), store ---------
-      if (pair_ok) {
+      // ---- scale, mask (keys past the row's visible length -> -inf), store -----------
+      // (every lane takes part in the scale permutes; only pair lanes store)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int k0 = kw + 8 * q4 + 4 * hg;
-          if (k0 >= a.out_stride) continue;  // out_stride % 4 == 0: all 4 or none
-          const float sc[4] = {cur.sc[q4].x, cur.sc[q4].y, cur.sc[q4].z, cur.sc[q4].w};
-          float v[4];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int k0 = kw + 8 * q4 + 4 * hg;
+        float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = k0 + e < vis ? acc[4 * q4 + e] * (kFp8 ? sc[e] * a.q_scale : 1.0f)
-                                : -INFINITY;
-          *reinterpret_cast<float4*>(orow + k0) = make_float4(v[0], v[1], v[2], v[3]);
+        for (int e = 0; e < 4; ++e) {
+          float sc = k_scale_h;
+          if constexpr (kFp8 && kMode == 1) sc = __shfl(t.sc, 8 * q4 + 4 * hg + e);
+          v[e] = k0 + e < vis ? acc[4 * q4 + e] * (kFp8 ? sc * a.q_scale : 1.0f) : -INFINITY;
         }
+        if (pair_ok && k0 < a.out_stride)  // out_stride % 4 == 0: all 4 or none
+          *reinterpret_cast<float4*>(orow + k0) = make_float4(v[0], v[1], v[2], v[3]);
       }
-      if (it + 1 < a.iters) cur = nxt;
+    };
+    int i0 = 0;
+    for (; i0 + kRing <= nt; i0 += kRing) {
+#pragma unroll
+      for (int r = 0; r < kRing; ++r) {
+        load_tile(i0 + r + kRing - 1, ring[(r + kRing - 1) % kRing]);
+        compute_store(i0 + r, ring[r]);
+      }
     }
+#pragma unroll
+    for (int r = 0; r < kRing - 1; ++r)
+      if (i0 + r < nt) compute_store(i0 + r, ring[r]);
   }
 }
 
