@@ -10,10 +10,10 @@
 //
 // Work split: a workgroup owns 16 consecutive tokens of the call and one KV head;
 // D/8 lanes own a (token, head) row, 8 consecutive values (one 16-byte load) each.
-// The row maximum is reduced across those lanes; every lane then quantises its 8
-// values (per-token-head rows: the quotient from one reciprocal per row and two fused
-// multiply-adds per value, whose codes equal those of the division -- see
-// e4m3_quantize4_row).  K rows go token-major (8 codes = one 8-byte store per lane).  V rows go
+// The row maxima of K and V are reduced across those lanes together (row_amax_bf16_kv);
+// every lane then quantises its 8 values (per-token-head rows: the scale and a
+// reciprocal once per row and two fused multiply-adds per value, whose codes equal
+// those of the division -- see row_scale and e4m3_quantize4_row).  K rows go token-major (8 codes = one 8-byte store per lane).  V rows go
 // dim-major: when the 16 tokens fill one page in order (slots 16 p .. 16 p + 15, the
 // usual bulk fill) the codes are transposed through LDS and every channel row of the
 // page tile is written with one 16-byte store (32 bytes for bf16); otherwise each
@@ -99,27 +99,19 @@ __global__ __launch_bounds__(2 * D) void cache_write_kernel(
       vf[2 * j + 1] = bf16_bits_to_float(vv[j] >> 16);
     }
     if constexpr (kPerTokenHead) {
-      uint32_t ka = 0, va = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        ka = max(ka, abs_bits(kf[j]));
-        va = max(va, abs_bits(vf[j]));
-      }
-#pragma unroll
-      for (int o = kLanesPerRow / 2; o >= 1; o >>= 1) {
-        ka = max(ka, (uint32_t)__shfl_xor((int)ka, o));
-        va = max(va, (uint32_t)__shfl_xor((int)va, o));
-      }
-      ks = scale_from_amax_bits(ka);
-      vs = scale_from_amax_bits(va);
+      const uint32_t kv = row_amax_bf16_kv<kLanesPerRow>(kw, vw);
+      const uint32_t ka = kv << 16, va = kv & 0xFFFF0000u;  // float32 magnitude bits
+      const RowScale krs = row_scale(ka), vrs = row_scale(va);
+      ks = krs.s;
+      vs = vrs.s;
+      kr = krs.r;
+      vr = vrs.r;
+      kfast = krs.fast;
+      vfast = vrs.fast;
       if (c == 0) {
         k_scales[tile * kPage + i] = ks;
         v_scales[tile * kPage + i] = vs;
       }
-      kfast = row_quot_fast(ka);
-      vfast = row_quot_fast(va);
-      if (kfast) kr = 1.0f / ks;
-      if (vfast) vr = 1.0f / vs;
     }
     *reinterpret_cast<uint2*>(k_pages + (tile * kPage + i) * D + c * 8) =
         make_uint2(e4m3_quantize4_row(kf, ks, kr, kfast), e4m3_quantize4_row(kf + 4, ks, kr, kfast));

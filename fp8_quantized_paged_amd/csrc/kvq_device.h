@@ -79,39 +79,90 @@ __device__ __forceinline__ uint32_t e4m3_quantize4(const float* x, float s) {
   return e4m3_quantize2(x[0], x[1], s) | (e4m3_quantize2(x[2], x[3], s) << 16);
 }
 
-// x / s for the values of one per-token-head row, s = fl32(amax / 448), from r = 1 / s
-// (IEEE, once per row) and two fused multiply-adds per value: q0 = x r, e = x - q0 s
-// (exact), q = q0 + e r (Markstein's correction step), with the sign of x so that -0
-// stays -0.  Where it is used -- 2^-100 <= amax < inf, |x| <= amax -- its e4m3 code
-// equals that of the IEEE quotient for every bf16 x and every bf16 amax (all such pairs
-// checked on an MI355X; the quotients themselves differ in about 0.1% of them, never
-// across an e4m3 rounding boundary).  Rows with smaller, infinite or NaN maxima take the
+// x / s for the values of one per-token-head row, s = fl32(amax / 448), from a
+// reciprocal r of s (once per row) and two fused multiply-adds per value: q0 = x r, the residual
+// e = q0 s - x (exact), q = q0 - e r (Markstein's correction step).  Negating the
+// residual rather than the product keeps the sign of zero: a residual that vanishes is
+// +0, and q0 - (+0) r leaves q0 (-0 for x = -0) unchanged; otherwise it is exactly the
+// negated residual x - q0 s.  Where it is used -- 2^-100 <= amax < inf, |x| <= amax --
+// its e4m3 code equals that of the IEEE quotient for every bf16 x and every bf16 amax,
+// with r = RN(1 / s) and with r from the hardware reciprocal (all such pairs checked on
+// an MI355X; the quotients themselves differ in about 0.1% of them, never across an
+// e4m3 rounding boundary).  Rows with smaller, infinite or NaN maxima take the
 // division (row_quot_fast false).
 __device__ __forceinline__ bool row_quot_fast(uint32_t amax_bits) {
   return amax_bits >= 0x0D800000u && amax_bits < 0x7F800000u;  // [2^-100, inf)
 }
 __device__ __forceinline__ float row_quot(float x, float s, float r) {
   const float q0 = x * r;
-  return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0), x);
+  return __builtin_fmaf(-__builtin_fmaf(q0, s, -x), r, q0);
 }
-// Four codes (bytes 0..3) of a per-token-head row's x[0..3] / s (r = 1 / s when fast).
+// Four codes (bytes 0..3) of a per-token-head row's x[0..3] / s (r from row_scale when
+// fast).  On a fast row every quotient is finite with |q| <= 448 (1 + 2^-22), below 464,
+// up to which the converter rounds to +-448 (checked for every float in [448, 464] of
+// both signs): no clamp and no NaN fix-up.
 __device__ __forceinline__ uint32_t e4m3_quantize4_row(const float* x, float s, float r,
                                                        bool fast) {
   if (!fast) return e4m3_quantize4(x, s);
-  const uint32_t lo = e4m3_codes2(row_quot(x[0], s, r), row_quot(x[1], s, r), x[0], x[1]);
-  const uint32_t hi = e4m3_codes2(row_quot(x[2], s, r), row_quot(x[3], s, r), x[2], x[3]);
-  return lo | (hi << 16);
+  float q[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q[j] = row_quot(x[j], s, r);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)lo, true);
 }
 
-// |x| maximum that propagates NaN (integer max of the magnitude bit patterns).
-__device__ __forceinline__ uint32_t abs_bits(float x) {
-  return __float_as_uint(x) & 0x7FFFFFFFu;
+// Row maxima of |x| for a per-token-head row of K and one of V, held by `lanes`
+// consecutive lanes (8 bf16 values of each per lane, power-of-two lanes): as bf16
+// magnitude bit patterns, K in bits 0-15 and V in bits 16-31, reduced with packed 16-bit
+// integer maxima (magnitude bits order like the values, NaN above infinity, so a NaN
+// propagates), one shuffle chain for both.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                __builtin_bit_cast(u16x2_t, b)));
+}
+template <int kLanes>
+__device__ __forceinline__ uint32_t row_amax_bf16_kv(uint4 kw, uint4 vw) {
+  constexpr uint32_t kMag = 0x7FFF7FFFu;
+  const uint32_t mk = pk_max_u16(pk_max_u16(kw.x & kMag, kw.y & kMag), pk_max_u16(kw.z & kMag, kw.w & kMag));
+  const uint32_t mv = pk_max_u16(pk_max_u16(vw.x & kMag, vw.y & kMag), pk_max_u16(vw.z & kMag, vw.w & kMag));
+  // (K lo, V lo) and (K hi, V hi) pairs, then their maximum
+  uint32_t m = pk_max_u16(__builtin_amdgcn_perm(mv, mk, 0x05040100u),
+                          __builtin_amdgcn_perm(mv, mk, 0x07060302u));
+#pragma unroll
+  for (int o = kLanes / 2; o >= 1; o >>= 1) m = pk_max_u16(m, (uint32_t)__shfl_xor((int)m, o));
+  return m;
 }
 
 // Per-token-head scale from the magnitude bits of the row maximum.
 __device__ __forceinline__ float scale_from_amax_bits(uint32_t amax_bits) {
   if (amax_bits == 0u) return 1.0f;
   return __uint_as_float(amax_bits) / 448.0f;
+}
+// A row's scale s = fl32(amax / 448) and, on fast rows, the reciprocal r for row_quot.
+// Fast rows take s from one Markstein step around k = RN(1 / 448) and r from the
+// hardware reciprocal: on an MI355X, that s equals the IEEE quotient for every bf16
+// amax in [2^-100, inf), and with that r the codes of row_quot equal those of the IEEE
+// quotient x / s for every bf16 x with |x| <= amax (all pairs checked).  Other rows
+// divide.
+struct RowScale {
+  float s, r;
+  bool fast;
+};
+__device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
+  RowScale o;
+  o.fast = row_quot_fast(amax_bits);
+  if (o.fast) {
+    constexpr float k = 1.0f / 448.0f;
+    const float a = __uint_as_float(amax_bits);
+    const float q0 = a * k;
+    o.s = __builtin_fmaf(-__builtin_fmaf(q0, 448.0f, -a), k, q0);
+    o.r = __builtin_amdgcn_rcpf(o.s);
+  } else {
+    o.s = scale_from_amax_bits(amax_bits);
+    o.r = 0.0f;
+  }
+  return o;
 }
 
 // Two e4m3 codes (bytes 0,1 or 2,3 of w) -> two exact bf16 values.
@@ -276,27 +327,19 @@ __device__ __forceinline__ void store_token_row(const uint16_t* k, const uint16_
     float kr = 0.0f, vr = 0.0f;     // per-token-head: 1 / scale for the fast quotient
     bool kfast = false, vfast = false;
     if constexpr (kPerTokenHead) {
-      uint32_t ka = 0, va = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ka = max(ka, abs_bits(kf[i]));
-        va = max(va, abs_bits(vf[i]));
-      }
-#pragma unroll
-      for (int o = kLanesPerRow / 2; o >= 1; o >>= 1) {
-        ka = max(ka, (uint32_t)__shfl_xor((int)ka, o));
-        va = max(va, (uint32_t)__shfl_xor((int)va, o));
-      }
-      ks = scale_from_amax_bits(ka);
-      vs = scale_from_amax_bits(va);
+      const uint32_t kv = row_amax_bf16_kv<kLanesPerRow>(kw, vw);
+      const uint32_t ka = kv << 16, va = kv & 0xFFFF0000u;  // float32 magnitude bits
+      const RowScale krs = row_scale(ka), vrs = row_scale(va);
+      ks = krs.s;
+      vs = vrs.s;
+      kr = krs.r;
+      vr = vrs.r;
+      kfast = krs.fast;
+      vfast = vrs.fast;
       if (c == 0) {
         k_scales[tile * kPage + off] = ks;
         v_scales[tile * kPage + off] = vs;
       }
-      kfast = row_quot_fast(ka);
-      vfast = row_quot_fast(va);
-      if (kfast) kr = 1.0f / ks;
-      if (vfast) vr = 1.0f / vs;
     }
     *reinterpret_cast<uint2*>(k_pages + (tile * kPage + off) * D + c * 8) =
         make_uint2(e4m3_quantize4_row(kf, ks, kr, kfast), e4m3_quantize4_row(kf + 4, ks, kr, kfast));
