@@ -15,9 +15,10 @@
 // reciprocal once per row and two fused multiply-adds per value, whose codes equal
 // those of the division -- see row_scale and e4m3_quantize4_row).  K rows go token-major (8 codes = one 8-byte store per lane).  V rows go
 // dim-major: when the 16 tokens fill one page in order (slots 16 p .. 16 p + 15, the
-// usual bulk fill) the codes are transposed through LDS and every channel row of the
-// page tile is written with one 16-byte store (32 bytes for bf16); otherwise each
-// lane stores its bytes where they belong (one byte per channel row).
+// usual bulk fill; every wave checks the block's 16 slots itself with scalar loads) the
+// codes are transposed through LDS and every channel row of the page tile is written
+// with one 16-byte store (32 bytes for bf16); otherwise each lane stores its bytes
+// where they belong (one byte per channel row).
 #include "kvq_device.h"
 #include "kvq_host.h"
 
@@ -51,10 +52,18 @@ __global__ __launch_bounds__(2 * D) void cache_write_kernel(
     kw = *reinterpret_cast<const uint4*>(k + src + c * 8);
     vw = *reinterpret_cast<const uint4*>(v + src + c * 8);
   }
-  // whole-page fast path: 16 tokens present, slots 16 p + i in order
-  const int64_t slot0 = t0 + kWriteTokens <= num_tokens ? slots[t0] : -1;
-  const bool page_run = __syncthreads_and(slot0 >= 0 && (slot0 & 15) == 0 &&
-                                          slot == slot0 + i);
+  // whole-page fast path: 16 tokens present, slots 16 p + j in order.  The block's 16
+  // slots are read at uniform addresses (scalar loads), so every wave reaches the same
+  // decision on its own, without a workgroup vote.
+  int64_t slot0 = -1;
+  bool page_run = false;
+  if (t0 + kWriteTokens <= num_tokens) {
+    slot0 = slots[t0];
+    bool in_order = slot0 >= 0 && (slot0 & 15) == 0;
+#pragma unroll
+    for (int j = 1; j < kWriteTokens; ++j) in_order &= slots[t0 + j] == slot0 + j;
+    page_run = in_order;
+  }
   // per-KV-head mode: k_scales / v_scales hold one scale per head (per-tensor: null)
   float ks = k_scale, vs = v_scale;
   float kr = 0.0f, vr = 0.0f;  // per-token-head: 1 / scale for the fast quotient
