@@ -144,30 +144,47 @@ logits_kernel(const LogitsArgs a) {
   float k_scale_h = a.k_scale;
   if constexpr (kFp8 && kMode == 2) k_scale_h = a.k_scales[g];
 
-  const bool unit_q = a.q_scale == 1.0f;
+  // 16-byte query pieces per thread and chunk (32 pairs x D / 8 pieces)
+  constexpr int QI = (32 * (D / 8) + kThreads - 1) / kThreads;
   for (int p0 = 0; p0 < npairs; p0 += 32) {
-    // ---- the chunk's query rows into LDS (e4m3 codes for an FP8 cache, else bf16) ---
-    __syncthreads();  // the previous chunk's operand reads are done
-    for (int i = (int)threadIdx.x; i < 32 * (D / 8); i += kThreads) {
+    // The chunk's query rows are loaded first, then the first tiles' key rows, so the
+    // key loads stay in flight while the query is encoded (memory operations complete
+    // in order for the wait counter: a query load issued after them would wait for
+    // them too).
+    uint4 qw[QI];
+#pragma unroll
+    for (int u = 0; u < QI; ++u) {
+      const int i = (int)threadIdx.x + kThreads * u;
       const int pp = i / (D / 8), c8 = i % (D / 8);  // pair, 8-element chunk
       const int p = p0 + pp;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (p < npairs)
-        w = *reinterpret_cast<const uint4*>(
+      qw[u] = make_uint4(0, 0, 0, 0);
+      if (i < 32 * (D / 8) && p < npairs)
+        qw[u] = *reinterpret_cast<const uint4*>(
             a.q + ((int64_t)(r0 + p / G) * a.num_q_heads + g * G + p % G) * D + 8 * c8);
-      if (p >= npairs) {  // columns without a pair: zero operands, nothing to encode
-        if constexpr (kFp8) *reinterpret_cast<uint2*>(q_lds + pp * QS + 8 * c8) = make_uint2(0, 0);
-        else *reinterpret_cast<uint4*>(q_lds + pp * QS + 16 * c8) = w;
-      } else if constexpr (kFp8) {
-        const uint32_t xs[4] = {w.x, w.y, w.z, w.w};
-        uint32_t c[2] = {0, 0};
+    }
+    // Ring of kRing tile buffers, fully unrolled so every buffer stays a named register
+    // set: kRing - 1 tiles' key rows are in flight while one is computed.
+    constexpr int kRing = 3;
+    Tile ring[kRing];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = bf16_bits_to_float((xs[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
-          const uint32_t code = unit_q ? e4m3_encode(x) : e4m3_quantize(x, a.q_scale);
-          c[e / 4] |= code << (8 * (e % 4));
-        }
-        *reinterpret_cast<uint2*>(q_lds + pp * QS + 8 * c8) = make_uint2(c[0], c[1]);
+    for (int r = 0; r < kRing - 1; ++r) load_tile(r, ring[r]);
+    // ---- the chunk's query rows into LDS (e4m3 codes for an FP8 cache, else bf16) ---
+    __syncthreads();  // the previous chunk's operand reads are done
+#pragma unroll
+    for (int u = 0; u < QI; ++u) {
+      const int i = (int)threadIdx.x + kThreads * u;
+      if (i >= 32 * (D / 8)) break;
+      const int pp = i / (D / 8), c8 = i % (D / 8);
+      const uint4 w = qw[u];  // zero for columns without a pair
+      if constexpr (kFp8) {
+        // e4m3 codes of x / q_scale on the hardware converter (e4m3_quantize4: the same
+        // codes as the integer encoder, NaN included; zero words give zero codes)
+        const uint32_t xs[4] = {w.x, w.y, w.z, w.w};
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = bf16_bits_to_float((xs[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+        *reinterpret_cast<uint2*>(q_lds + pp * QS + 8 * c8) =
+            make_uint2(e4m3_quantize4(f, a.q_scale), e4m3_quantize4(f + 4, a.q_scale));
       } else {
         *reinterpret_cast<uint4*>(q_lds + pp * QS + 16 * c8) = w;
       }
@@ -177,12 +194,6 @@ logits_kernel(const LogitsArgs a) {
     const int pr = r0 + (pair_ok ? p / G : 0), ph = g * G + (pair_ok ? p % G : 0);
     const int vis = pair_ok ? min(a.row_lens[pr], L) : 0;
     float* orow = a.out + ((int64_t)pr * a.num_q_heads + ph) * a.out_stride;
-    // Ring of kRing tile buffers, fully unrolled so every buffer stays a named register
-    // set: kRing - 1 tiles' key rows are in flight while one is computed.
-    constexpr int kRing = 3;
-    Tile ring[kRing];
-#pragma unroll
-    for (int r = 0; r < kRing - 1; ++r) load_tile(r, ring[r]);
     __syncthreads();
     // B operand of this lane (pair col): its half row, kept for all tiles
     const uint8_t* qrow = q_lds + col * QS + HB * hg;
