@@ -233,3 +233,65 @@ def test_cache_write_per_token_head_row_maxima(kvq, ordered):
     pools = ocache.new_pools(P, H, D)
     ocache.cache_write(pools, x, v, slots, "per_token_head", 1.0, 1.0)
     _check_pools(read_pools(c), pools, slots)
+
+
+def _mixed_block_slots():
+    """Slots for 10 blocks of 16 tokens plus a 7-token tail, each block a different case
+    of the whole-page test the write takes per block: whole pages in order (the LDS
+    path), in order but one slot off the page boundary, one swapped pair, a skipped
+    token (-1) inside a page, a page in reverse, scattered slots; the partial tail is in
+    order but shorter than a page (the single-row path)."""
+    rng = np.random.default_rng(2024)
+    pages = iter(rng.permutation(64)[:40].tolist())  # distinct pages, no slot written twice
+    blocks = []
+    p = next(pages); blocks.append(16 * p + np.arange(16))                      # run
+    p = next(pages); next(pages); blocks.append(16 * p + 1 + np.arange(16))    # off by one
+    b = 16 * next(pages) + np.arange(16); b[[5, 6]] = b[[6, 5]]; blocks.append(b)  # swap
+    b = 16 * next(pages) + np.arange(16); b[7] = -1; blocks.append(b)          # skip inside
+    p = next(pages); blocks.append(16 * p + np.arange(16))                      # run
+    blocks.append(16 * next(pages) + np.arange(15, -1, -1))                     # reversed
+    p = next(pages); blocks.append(16 * p + np.arange(16))                      # run
+    scat = np.array([16 * next(pages) + int(o) for o in rng.integers(0, 16, 16)])
+    blocks.append(scat)                                                         # scattered
+    blocks.append(16 * next(pages) + np.arange(16))                             # run
+    blocks.append(16 * next(pages) + np.arange(16))                             # run
+    blocks.append(16 * next(pages) + np.arange(7))                              # tail
+    return np.concatenate(blocks).astype(np.int64)
+
+
+@pytest.mark.parametrize("mode", ["per_token_head", "per_tensor", "bf16"])
+def test_cache_write_mixed_page_blocks(kvq, mode):
+    """One call whose 16-token blocks alternate between whole pages in order and the
+    near misses of that test; every written row bit-exact to the oracle, no other slot
+    touched."""
+    H, D, P = 2, 128, 64
+    slots = _mixed_block_slots()
+    T = len(slots)
+    rng = np.random.default_rng(5)
+    k = workloads.bf16_round(rng.standard_normal((T, H, D)).astype(np.float32) * 3)
+    v = workloads.bf16_round(rng.standard_normal((T, H, D)).astype(np.float32) * 3)
+    log(f"cache_write mixed page blocks {mode}: {T} tokens")
+    dtype = "bf16" if mode == "bf16" else "fp8"
+    c = kvq.PagedCache(P, H, D, dtype, "per_tensor" if mode == "bf16" else mode)
+    c.k_pages.view(torch.uint8).fill_(0x5A)   # a marker in every byte: untouched slots keep it
+    c.v_pages.view(torch.uint8).fill_(0x5A)
+    kvq.cache_write(c, dev_bf16(k), dev_bf16(v), dev(slots), 0.5, 0.25)
+    got = read_pools(c)
+    keep = slots >= 0
+    page, off = slots[keep] // 16, slots[keep] % 16
+    if mode == "bf16":
+        assert np.array_equal(got["k"][page, :, off], k[keep])
+        assert np.array_equal(got["v"][page, :, off], v[keep])
+    else:
+        want = ocache.new_pools(P, H, D)
+        ocache.cache_write(want, k, v, slots, mode, 0.5, 0.25)
+        _check_pools(got, want, slots[keep])
+    # every slot no token was written to still holds the marker
+    written = np.zeros(P * 16, bool)
+    written[slots[keep]] = True
+    untouched = np.nonzero(~written)[0]
+    eb = 2 if mode == "bf16" else 1
+    kraw = c.k_pages.view(torch.uint8).cpu().numpy().reshape(P, H, 16, D * eb)
+    vraw = c.v_pages.view(torch.uint8).cpu().numpy().reshape(P, H, D, 16, eb)
+    assert (kraw[untouched // 16, :, untouched % 16] == 0x5A).all()
+    assert (vraw[untouched // 16, :, :, untouched % 16] == 0x5A).all()
