@@ -659,18 +659,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 
     PageOffs offs_v = page_offsets(tile_ids(t_first + 2));  // page offsets of tile t + 2
     int4 ids_k_raw = tile_ids_raw(t_first + 3);  // of tile t + 3, read one tile ahead
-    for (int t = t_first; t <= t_last; ++t) {
+    // One tile step.  R = (t - t_first) & 3, the tile's place in the four-slot rings,
+    // is a compile-time constant: the loop below is unrolled by hand over the ring
+    // period (the compiler does not unroll a loop with a barrier in it), so every slot
+    // address is a constant.
+    auto step = [&](auto r_tag, const int t) {
+      constexpr int R = decltype(r_tag)::value;
       const int rel = t - t_first;
-      const uint8_t* kb1 = k_lds[(rel + 1) & 3];  // K of tile t + 1
-      const uint8_t* kb2 = k_lds[(rel + 2) & 3];  // K of tile t + 2 (published mid-way)
-      uint8_t* const kb3 = k_lds[(rel + 3) & 3];  // K of tile t + 3 goes here
-      const uint8_t* vb0 = v_lds[rel & 3];        // V of tile t
-      uint8_t* const vb1 = v_lds[(rel + 1) & 3];  // V of tile t + 1 (published mid-way)
-      uint8_t* const vb2 = v_lds[(rel + 2) & 3];  // V of tile t + 2 goes here
-      uint8_t* const fb0 = f_lds[wave][rel & 1];        // factors of tile t
-      uint8_t* const fb1 = f_lds[wave][(rel + 1) & 1];  // factors of tile t + 1
+      const uint8_t* kb1 = k_lds[(R + 1) & 3];  // K of tile t + 1
+      const uint8_t* kb2 = k_lds[(R + 2) & 3];  // K of tile t + 2 (published mid-way)
+      uint8_t* const kb3 = k_lds[(R + 3) & 3];  // K of tile t + 3 goes here
+      const uint8_t* vb0 = v_lds[R];            // V of tile t
+      uint8_t* const vb1 = v_lds[(R + 1) & 3];  // V of tile t + 1 (published mid-way)
+      uint8_t* const vb2 = v_lds[(R + 2) & 3];  // V of tile t + 2 goes here
+      uint8_t* const fb0 = f_lds[wave][R & 1];        // factors of tile t
+      uint8_t* const fb1 = f_lds[wave][(R + 1) & 1];  // factors of tile t + 1
       // V of tile t (published by the previous barrier) is first read in phase 1
-      if (rel > 0) scrub_v(t, v_lds[rel & 3]);
+      if (rel > 0) scrub_v(t, v_lds[R]);
       const float vr = vref_run;  // v_ref after tile t (before tile t + 1 is derived)
       // scales of tile t + 1 (resident since the previous barrier): read here, factors
       // written in chunk 1 (before the first read of them) or, with fewer than 4 S^T
@@ -694,7 +699,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         ifb[0] = fi[0];
         ifb[1] = fi[32];
       }
-      if (rel % kIdTiles == 0) issue_ids(rel / kIdTiles + 1);
+      if (R == 0 && rel % kIdTiles == 0) issue_ids(rel / kIdTiles + 1);  // kIdTiles % 4 == 0
       const int4 ids_k = uniform_ids(ids_k_raw);
       const PageOffs offs_k = page_offsets(ids_k);
       // masks and row maxima of tile t's scores
@@ -845,8 +850,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                                        0x0400);
       }
       offs_v = offs_k;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    int t = t_first;
+    for (; t + 3 <= t_last; t += 4) {
+      step(I0{}, t);
+      step(I1{}, t + 1);
+      step(I2{}, t + 2);
+      step(I3{}, t + 3);
     }
+    // the last (up to three) tiles: t - t_first is a multiple of 4 here
+    if (t <= t_last) step(I0{}, t);
+    if (t + 1 <= t_last) step(I1{}, t + 1);
+    if (t + 2 <= t_last) step(I2{}, t + 2);
   };
+  static_assert(kIdTiles % 4 == 0, "page-id chunks start at ring position 0");
   if (a.prob_scale < 256.0f / kE4m3Max) {
     // P' = p * v_scale_j / (v_ref * prob_scale) can pass 448 only when prob_scale <
     // 2^8 / 448 (p <= 2^8, v_scale_j <= v_ref)
