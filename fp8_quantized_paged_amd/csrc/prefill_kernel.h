@@ -659,12 +659,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 
     PageOffs offs_v = page_offsets(tile_ids(t_first + 2));  // page offsets of tile t + 2
     int4 ids_k_raw = tile_ids_raw(t_first + 3);  // of tile t + 3, read one tile ahead
-    // One tile step.  R = (t - t_first) & 3, the tile's place in the four-slot rings,
-    // is a compile-time constant: the loop below is unrolled by hand over the ring
-    // period (the compiler does not unroll a loop with a barrier in it), so every slot
-    // address is a constant.
+    // One tile step.  R = (t - t_first) & 3, the tile's place in the four-slot rings.
+    // The chained form passes it as a compile-time constant: the loop below is unrolled
+    // by hand over the ring period (the compiler does not unroll a loop with a barrier
+    // in it), so every slot address is a constant.  The explicit-flush form, whose
+    // extra zeroed accumulators leave no registers for four copies, keeps the rolled
+    // loop with R a plain integer.
     auto step = [&](auto r_tag, const int t) {
-      constexpr int R = decltype(r_tag)::value;
+      const int R = static_cast<int>(r_tag);
       const int rel = t - t_first;
       const uint8_t* kb1 = k_lds[(R + 1) & 3];  // K of tile t + 1
       const uint8_t* kb2 = k_lds[(R + 2) & 3];  // K of tile t + 2 (published mid-way)
@@ -855,17 +857,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
-    int t = t_first;
-    for (; t + 3 <= t_last; t += 4) {
-      step(I0{}, t);
-      step(I1{}, t + 1);
-      step(I2{}, t + 2);
-      step(I3{}, t + 3);
+    if constexpr (kValuAdd) {
+      for (int t = t_first; t <= t_last; ++t) step((t - t_first) & 3, t);
+    } else {
+      int t = t_first;
+      for (; t + 3 <= t_last; t += 4) {
+        step(I0{}, t);
+        step(I1{}, t + 1);
+        step(I2{}, t + 2);
+        step(I3{}, t + 3);
+      }
+      // the last (up to three) tiles: t - t_first is a multiple of 4 here
+      if (t <= t_last) step(I0{}, t);
+      if (t + 1 <= t_last) step(I1{}, t + 1);
+      if (t + 2 <= t_last) step(I2{}, t + 2);
     }
-    // the last (up to three) tiles: t - t_first is a multiple of 4 here
-    if (t <= t_last) step(I0{}, t);
-    if (t + 1 <= t_last) step(I1{}, t + 1);
-    if (t + 2 <= t_last) step(I2{}, t + 2);
   };
   static_assert(kIdTiles % 4 == 0, "page-id chunks start at ring position 0");
   if (a.prob_scale < 256.0f / kE4m3Max) {
