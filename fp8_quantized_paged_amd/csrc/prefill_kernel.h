@@ -603,6 +603,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     // read), LPC per chunk: K of tile t + 3, then V of tile t + 2
     constexpr int NLD = PER_K + PER_V;
     constexpr int LPC = NQK > 1 ? (NLD + NQK - 2) / (NQK - 1) : NLD;
+    // The chunk that waits for K of tile t + 2 / V of tile t + 1 and publishes them: the
+    // start of phase 2, or -- head_dim 256 per-token-head, where the loads' latency shows
+    // -- the last chunk before the back-edge queue first reads K of tile t + 2 (1468 ->
+    // 1441 us; per-tensor 1206 -> 1239 us the other way, so it keeps the early one).
+    constexpr int kPublishChunk = kCrossQueue && kPTH ? NCH - QD - 1 : NQK;
+    static_assert(kPublishChunk >= NQK && kPublishChunk + QD <= NCH + (kCrossQueue ? 0 : QD),
+                  "publish before the first read of K of tile t + 2");
     struct Chunk {
       v8i op;
       float4 f2[WV];  // score factors (phase-2 chunks, queued mode)
@@ -769,7 +776,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         }
         if constexpr (kPTH && NQK >= 4)
           if (c == 1) derive(t + 1, fb1, dks, dvs);
-        if (c == NQK) {
+        if (c == kPublishChunk) {
           // K of tile t + 2 and V of tile t + 1 resident: wait for them (the loads of
           // K of tile t + 3 and V of tile t + 2 may stay in flight), publish
           wait_vmcnt<NLD>();
