@@ -407,33 +407,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int NKV = KB / 16;   // 16-byte loads of them
     constexpr int NBLK = D / 16;   // PV accumulator blocks
     // Page inputs reach the operand layout -- which puts 16 token rows in every
-    // 16-lane group -- through LDS: direct-to-LDS loads read the K and V tiles in order
-    // (each lane 16 bytes, a wave 1 KB of contiguous tile per load) into a per-wave ring
-    // of LDS slots, and the operand reads come from LDS.  Slot: K tile [16][D] | V tile
-    // [D][16] | 256 B of scales (lanes 0-15: K, 16-31: V, then repeats).  The loads are
-    // counted by hand (NL per page; wait_vmcnt before a slot is read).  (A register form
-    // for head_dim 64 per-tensor -- K read in order and traded into place with lane
-    // permutes, V one dword per lane and block -- measured 33.2 us against 30.0 us
-    // staged on the gpt-oss-shaped full layer.)
-    constexpr int SLOT = 32 * D + (kPTH ? 256 : 0);
+    // 16-lane group -- in one of two ways (measured per shape):
+    //  * staged (default): direct-to-LDS loads read the K and V tiles in order (each
+    //    lane 16 bytes, a wave 1 KB of contiguous tile per load) into a per-wave ring
+    //    of LDS slots, and the operand reads come from LDS.  Slot: K tile [16][D] |
+    //    V tile [D][16] | 256 B of scales (lanes 0-15: K, 16-31: V, then repeats).
+    //    The loads are counted by hand (NL per page; wait_vmcnt before a slot is read).
+    //  * registers (head_dim 64, per-tensor scales): K is read in order, four lanes to
+    //    a token row, and the lanes trade the pieces into place with lane permutes;
+    //    V is read as one dword (4 tokens of one channel) per lane and block.  With
+    //    every page coming from HBM (8 x 20,000 tokens, 64/8 heads) this runs 34.0 us
+    //    against 36.5 us staged; staged wins only while the cache sits in the 256 MB
+    //    last-level cache.
+    constexpr bool kStage = !(D == 64 && !kPTH);
+    constexpr int SLOT = kStage ? 32 * D + (kPTH ? 256 : 0) : 16;
     constexpr int NL = 2 * (D / 64) + (kPTH ? 1 : 0);
     __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves][kRing][SLOT];
     uint8_t* const stage = stage_all[wave][0];
+    struct RegPage {
+      u32x4_t k;
+      uint32_t v[NBLK];
+    };
+    RegPage regs[kStage ? 1 : kRing];
     auto mload = [&](int i, int slot) {
       const int page = __builtin_amdgcn_readlane(bt_lane, i);
       const int64_t tile = (int64_t)page * a.num_kv_heads + g;
       const uint8_t* kb = a.k_pages + tile * kPage * D;
       const uint8_t* vb = a.v_pages + tile * kPage * D;
-      uint8_t* dst = stage + slot * SLOT;
+      if constexpr (kStage) {
+        uint8_t* dst = stage + slot * SLOT;
 #pragma unroll
-      for (int j = 0; j < D / 64; ++j)
-        lds_load16s(kb, 16 * lane + 1024 * j, lds_offset(dst + 1024 * j));
+        for (int j = 0; j < D / 64; ++j)
+          lds_load16s(kb, 16 * lane + 1024 * j, lds_offset(dst + 1024 * j));
 #pragma unroll
-      for (int j = 0; j < D / 64; ++j)
-        lds_load16s(vb, 16 * lane + 1024 * j, lds_offset(dst + 16 * D + 1024 * j));
-      if constexpr (kPTH)
-        lds_load4((lane < 16 ? a.k_scales : a.v_scales) + tile * kPage + (lane & 15),
-                  lds_offset(dst + 32 * D));
+        for (int j = 0; j < D / 64; ++j)
+          lds_load16s(vb, 16 * lane + 1024 * j, lds_offset(dst + 16 * D + 1024 * j));
+        if constexpr (kPTH)
+          lds_load4((lane < 16 ? a.k_scales : a.v_scales) + tile * kPage + (lane & 15),
+                    lds_offset(dst + 32 * D));
+      } else {
+        RegPage& r = regs[slot];
+        r.k = stream_load(reinterpret_cast<const u32x4_t*>(kb) + lane);
+        // dword 4 d + qg of the tile's channel-d row holds tokens 4 qg .. 4 qg + 3
+        const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(vb) + 4 * n + qg;
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) r.v[blk] = stream_load(vsrc + 64 * blk);
+      }
     };
     // every wave with pages issues kRing - 1 page loads up front (indices clamped to
     // its last page, so the counts below hold for any page count)
@@ -480,13 +499,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       const uint8_t* src = stage + slot * SLOT;
       u32x4_t kq[NKV];  // K row n, bytes qg * KB .. of it
       uint32_t vq[NBLK];  // tokens 4 qg .. 4 qg + 3 of channel 16 blk + n
+      if constexpr (kStage) {
 #pragma unroll
-      for (int j = 0; j < NKV; ++j)
-        kq[j] = *reinterpret_cast<const u32x4_t*>(src + n * D + qg * KB + 16 * j);
+        for (int j = 0; j < NKV; ++j)
+          kq[j] = *reinterpret_cast<const u32x4_t*>(src + n * D + qg * KB + 16 * j);
 #pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk)  // bank-conflict free
-        vq[blk] = *reinterpret_cast<const uint32_t*>(src + 16 * D + (16 * blk + n) * 16 +
-                                                     4 * qg);
+        for (int blk = 0; blk < NBLK; ++blk)  // bank-conflict free
+          vq[blk] = *reinterpret_cast<const uint32_t*>(src + 16 * D + (16 * blk + n) * 16 +
+                                                       4 * qg);
+      } else {  // lane (n, qg) takes its K piece from lane 4 n + qg
+        const RegPage& r = regs[slot];
+        const int from = (4 * n + qg) * 4;
+        kq[0].x = __builtin_amdgcn_ds_bpermute(from, (int)r.k.x);
+        kq[0].y = __builtin_amdgcn_ds_bpermute(from, (int)r.k.y);
+        kq[0].z = __builtin_amdgcn_ds_bpermute(from, (int)r.k.z);
+        kq[0].w = __builtin_amdgcn_ds_bpermute(from, (int)r.k.w);
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) vq[blk] = r.v[blk];
+      }
       float ksc[4], vsc[4];
       if constexpr (kPTH) {
         const float4 k4 = *reinterpret_cast<const float4*>(src + 32 * D + 16 * qg);
@@ -581,9 +611,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     for (; i0 + kRing <= nwp; i0 += kRing) {
 #pragma unroll
       for (int r = 0; r < kRing; ++r) {
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        if constexpr (kStage) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         mload(min(i0 + r + kRing - 1, nwp - 1), (r + kRing - 1) % kRing);
-        wait_vmcnt<(kRing - 1) * NL>();
+        if constexpr (kStage) wait_vmcnt<(kRing - 1) * NL>();
         mcompute(i0 + r, r);
       }
     }
@@ -591,12 +621,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     // page i0 + r number kRing - 2 - r pages
     static_assert(kRing == 2 || kRing == 3, "staging ring of 2 or 3 slots");
     if (i0 < nwp) {
-      wait_vmcnt<(kRing - 2) * NL>();
+      if constexpr (kStage) wait_vmcnt<(kRing - 2) * NL>();
       mcompute(i0, 0);
     }
     if constexpr (kRing == 3) {
       if (i0 + 1 < nwp) {
-        wait_vmcnt<0>();
+        if constexpr (kStage) wait_vmcnt<0>();
         mcompute(i0 + 1, 1);
       }
     }
