@@ -850,8 +850,11 @@ def main():
         B3, L3 = 32, 20000
         lc = workloads.make_logits_case(109, [L3] * B3, [1] * B3, 4, 1, 128, table="perm",
                                         name="paged logits")
+        # at least 8 copies (8 x 84.5 MB): with 4, the three others plus the output
+        # (~264 MB) are about what the 256 MB last-level cache holds, and a launch
+        # measured ~3% fast
         cs = [kvq.PagedCache(lc.num_pages, 1, 128, "fp8", "per_token_head")
-              for _ in range(args.rotate)]
+              for _ in range(max(8, args.rotate))]
         for i in range(0, len(lc.k), 65536):
             sl_ = slice(i, i + 65536)
             kk, vv = to_dev(lc.k[sl_]), to_dev(lc.v[sl_])

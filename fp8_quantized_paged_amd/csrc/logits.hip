@@ -23,6 +23,11 @@
 // contiguous half D/2 hg .. D/2 hg + D/2 - 1 of every key and
 // query row: step s, element e <-> dim D/2 hg + 8 s + e (both operands agree, which
 // is all a contraction needs), so each lane's operands are plain 16-byte loads.
+// The loads of every tile are issued unconditionally and the output stores go through a
+// buffer resource that drops the stores of lanes without output, so no branch hides a
+// memory instruction from the compiler's wait counts: they then keep two tiles in
+// flight (with the loads and stores behind branches each wait also drained the
+// prefetched tiles; indexer shape, 8 cache copies rotated: 22.9 -> 22.0 us).
 #include <algorithm>
 
 #include "kvq_device.h"
@@ -61,6 +66,7 @@ struct LogitsArgs {
   int32_t groups, iters;      // workgroups per (request, head), tiles per workgroup
   float q_scale, k_scale;     // k_scale: per-tensor
   float* out;                 // [rows][Hq][out_stride]
+  int32_t span_bytes;         // bytes a chunk's stores may reach from its first pair's row
   int32_t out_stride;
 };
 
@@ -76,7 +82,7 @@ __device__ __forceinline__ half8_t codes_to_f16(uint32_t lo, uint32_t hi) {
 // kMode: 0 per-tensor, 1 per-token-head, 2 per-KV-head (FP8 only)
 // Two waves per SIMD: a launch's workgroups (two per CU) stay resident at once.  (A
 // three-wave budget spilled the ring at head_dim 128.)
-template <int D, bool kFp8, int kMode>
+template <int D, bool kFp8, int kMode, bool kBuf>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 logits_kernel(const LogitsArgs a) {
   constexpr int ES = kFp8 ? 1 : 2;       // bytes per element
@@ -113,7 +119,7 @@ logits_kernel(const LogitsArgs a) {
   // per-tile loads of this wave: its lane's half row of key key_base + 128 it + col and
   // (per-token-head) the scale of key col of the wave's 32; the scales an output lane
   // needs (keys 8 q + 4 hg + e, register 4 q + e) come from those lanes at the store.
-  // Tiles past the workgroup's range (it >= iters) load nothing.
+  // Tiles past the workgroup's range (it >= iters) are loaded but never computed.
   struct Tile {
     uint4 k[NV];
     float sc;
@@ -125,20 +131,22 @@ logits_kernel(const LogitsArgs a) {
     const int pg[2] = {__builtin_amdgcn_readlane(pid_all, pi),
                        __builtin_amdgcn_readlane(pid_all, pi + 1)};
     const int key = kw + col;
-    t.sc = 0.0f;
-    if constexpr (kFp8 && kMode == 1) {
-      if (tile_ok && key < L)  // slots past L hold unwritten scales: never read
-        t.sc = a.k_scales[((int64_t)pg[col / 16] * H + g) * kPage + key % kPage];
-    }
-    if (tile_ok && key < L) {
-      const int page = col < 16 ? pg[0] : pg[1];
-      const uint8_t* row = a.k_pages + ((((int64_t)page * H + g) * kPage + key % kPage) * D) * ES;
+    // Every lane issues its loads: a lane without a key (past the sequence or the
+    // workgroup's range) reads the call's first query row instead (always there, 16-byte
+    // aligned and at least D * ES bytes), and its garbage only reaches its own output
+    // row, which is -inf or not stored.  A load behind a branch would make the compiler's
+    // wait counts assume it may be missing, and each wait would then drain the
+    // prefetched tiles as well.
+    const bool ok = tile_ok && key < L;
+    const int64_t slot = ((int64_t)(col < 16 ? pg[0] : pg[1]) * H + g) * kPage + key % kPage;
+    if constexpr (kFp8 && kMode == 1)
+      t.sc = *(ok ? a.k_scales + slot : reinterpret_cast<const float*>(a.q));
+    else
+      t.sc = 0.0f;
+    const uint8_t* row =
+        ok ? a.k_pages + slot * D * ES : reinterpret_cast<const uint8_t*>(a.q);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) t.k[v] = *reinterpret_cast<const uint4*>(row + HB * hg + 16 * v);
-    } else {
-#pragma unroll
-      for (int v = 0; v < NV; ++v) t.k[v] = make_uint4(0, 0, 0, 0);
-    }
+    for (int v = 0; v < NV; ++v) t.k[v] = *reinterpret_cast<const uint4*>(row + HB * hg + 16 * v);
   };
   // per-tensor / per-KV-head: one K scale for the head
   float k_scale_h = a.k_scale;
@@ -194,9 +202,34 @@ logits_kernel(const LogitsArgs a) {
     const int pr = r0 + (pair_ok ? p / G : 0), ph = g * G + (pair_ok ? p % G : 0);
     const int vis = pair_ok ? min(a.row_lens[pr], L) : 0;
     float* orow = a.out + ((int64_t)pr * a.num_q_heads + ph) * a.out_stride;
+    // Stores (kBuf): a buffer resource from the chunk's first pair's output row, a.span_bytes
+    // long (the host checked that every pair of a chunk stores inside it); a lane with
+    // nothing to store takes an offset past that range, which the hardware drops.  So
+    // the store needs no branch: every store is issued, and the compiler counts it
+    // exactly in the waits for the key loads (a store behind a branch made it wait
+    // for a prefetched tile too).  Without kBuf (a chunk spanning 2 GB or more of
+    // output) the stores are plain and conditional.
+    const int64_t base_f = ((int64_t)(r0 + p0 / G) * a.num_q_heads + g * G + p0 % G) * a.out_stride;
+    int rel_f = 0;  // this pair's row, in floats from base_f
+    if constexpr (kBuf)
+      rel_f = pair_ok ? (int)(((int64_t)pr * a.num_q_heads + ph) * a.out_stride - base_f) : 0;
+    const __amdgpu_buffer_rsrc_t orsrc =  // gfx9 word 3: 32-bit raw buffer
+        __builtin_amdgcn_make_buffer_rsrc(a.out + base_f, 0, kBuf ? a.span_bytes : 0, 0x00020000);
     __syncthreads();
     // B operand of this lane (pair col): its half row, kept for all tiles
     const uint8_t* qrow = q_lds + col * QS + HB * hg;
+    // converted once per chunk, not per tile
+    half8_t qf[kFp8 ? NS : 1];
+    bf16x8_t qbf[kFp8 ? 1 : NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if constexpr (kFp8) {
+        const uint2 qc = *reinterpret_cast<const uint2*>(qrow + 8 * s);
+        qf[s] = codes_to_f16(qc.x, qc.y);
+      } else {
+        qbf[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + 16 * s));
+      }
+    }
     // this wave's tiles: it < nt (a.iters, fewer where the row ends first)
     const int nt = min(a.iters, max(0, (a.out_stride - key_base + kTileKeys - 1) / kTileKeys));
     auto compute_store = [&](int it, const Tile& t) {
@@ -205,15 +238,12 @@ logits_kernel(const LogitsArgs a) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         if constexpr (kFp8) {
-          const uint2 qc = *reinterpret_cast<const uint2*>(qrow + 8 * s);
           const uint4 kv = t.k[s / 2];  // key bytes 8 s .. 8 s + 7 of the half row
           const half8_t ka = (s & 1) ? codes_to_f16(kv.z, kv.w) : codes_to_f16(kv.x, kv.y);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, codes_to_f16(qc.x, qc.y), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[s], acc, 0, 0, 0);
         } else {
-          const bf16x8_t qb =
-              __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + 16 * s));
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, t.k[s]),
-                                                        qb, acc, 0, 0, 0);
+                                                        qbf[s], acc, 0, 0, 0);
         }
       }
       // ---- scale, mask (keys past the row's visible length -> -inf), store -----------
@@ -228,8 +258,16 @@ logits_kernel(const LogitsArgs a) {
           if constexpr (kFp8 && kMode == 1) sc = __shfl(t.sc, 8 * q4 + 4 * hg + e);
           v[e] = k0 + e < vis ? acc[4 * q4 + e] * (kFp8 ? sc * a.q_scale : 1.0f) : -INFINITY;
         }
-        if (pair_ok && k0 < a.out_stride)  // out_stride % 4 == 0: all 4 or none
+        if constexpr (kBuf) {
+          typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+          const u32x4v bits = {__float_as_uint(v[0]), __float_as_uint(v[1]),
+                               __float_as_uint(v[2]), __float_as_uint(v[3])};
+          // 0x7FFFFFF0: past any span_bytes (< 0x7FF00000), without wrapping
+          const int off = pair_ok && k0 < a.out_stride ? 4 * (rel_f + k0) : 0x7FFFFFF0;
+          __builtin_amdgcn_raw_buffer_store_b128(bits, orsrc, off, 0, 0);
+        } else if (pair_ok && k0 < a.out_stride) {  // out_stride % 4 == 0: all 4 or none
           *reinterpret_cast<float4*>(orow + k0) = make_float4(v[0], v[1], v[2], v[3]);
+        }
       }
     };
     int i0 = 0;
@@ -238,6 +276,9 @@ logits_kernel(const LogitsArgs a) {
       for (int r = 0; r < kRing; ++r) {
         load_tile(i0 + r + kRing - 1, ring[(r + kRing - 1) % kRing]);
         compute_store(i0 + r, ring[r]);
+        // keeps the next step's operand converts (and so the wait for its tile) from
+        // being hoisted into this one
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
@@ -246,16 +287,21 @@ logits_kernel(const LogitsArgs a) {
   }
 }
 
+template <int D, bool kFp8, bool kBuf>
+static void launch_mode_b(int mode, const LogitsArgs& args, unsigned blocks, hipStream_t st) {
+  if (!kFp8)
+    logits_kernel<D, false, 0, kBuf><<<blocks, kThreads, 0, st>>>(args);
+  else if (mode == KVQ_SCALE_PER_TOKEN_HEAD)
+    logits_kernel<D, true, 1, kBuf><<<blocks, kThreads, 0, st>>>(args);
+  else if (mode == KVQ_SCALE_PER_KV_HEAD)
+    logits_kernel<D, true, 2, kBuf><<<blocks, kThreads, 0, st>>>(args);
+  else
+    logits_kernel<D, true, 0, kBuf><<<blocks, kThreads, 0, st>>>(args);
+}
 template <int D, bool kFp8>
 static void launch_mode(int mode, const LogitsArgs& args, unsigned blocks, hipStream_t st) {
-  if (!kFp8)
-    logits_kernel<D, false, 0><<<blocks, kThreads, 0, st>>>(args);
-  else if (mode == KVQ_SCALE_PER_TOKEN_HEAD)
-    logits_kernel<D, true, 1><<<blocks, kThreads, 0, st>>>(args);
-  else if (mode == KVQ_SCALE_PER_KV_HEAD)
-    logits_kernel<D, true, 2><<<blocks, kThreads, 0, st>>>(args);
-  else
-    logits_kernel<D, true, 0><<<blocks, kThreads, 0, st>>>(args);
+  if (args.span_bytes > 0) launch_mode_b<D, kFp8, true>(mode, args, blocks, st);
+  else launch_mode_b<D, kFp8, false>(mode, args, blocks, st);
 }
 
 template <int D>
@@ -326,6 +372,14 @@ extern "C" kvq_status kvq_paged_logits(const kvq_cache_desc* cache, const void* 
   }
   a.out = out;
   a.out_stride = out_stride;
+  {
+    // 32 consecutive (row, head) pairs of one key head lie within 31 / G + 2 output rows
+    // of Hq * out_stride floats from the first; a span that a 32-bit buffer offset cannot
+    // cover takes the plain-store kernel (span_bytes 0)
+    const int64_t G = num_q_heads / cache->num_kv_heads;
+    const int64_t span = (31 / G + 2) * (int64_t)num_q_heads * out_stride * 4;
+    a.span_bytes = span < 0x7FF00000 ? (int32_t)span : 0;
+  }
   const int64_t blocks = (int64_t)num_seqs * cache->num_kv_heads * a.groups;
   if (blocks > 0x7FFFFFFF) return fail(KVQ_ERR_INVALID_ARG, "grid too large");
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -109,6 +109,40 @@ def test_logits_edges(kvq):
     run_case(kvq, case, "fp8", "per_token_head", out_len=512)
 
 
+def test_logits_wide_output_and_empty_cache(kvq):
+    """Output rows so long (8,200,000 entries, one query head per key head) that a
+    32-pair column chunk spans more than 2 GB of output: the kernel then stores without
+    the buffer resource; the first 512 entries of every row against the oracle, the
+    rest -inf.  And a cache with no pages at all: every logit -inf."""
+    case = workloads.make_logits_case(731, [300, 40], [2, 1], 2, 2, 64, table="perm")
+    out_len, head = 8_200_000, 512
+    c = write_cache(kvq, case, "fp8", "per_token_head")
+    log("logits wide output rows (plain stores)")
+    got = kvq.paged_logits(c, dev_bf16(case.q), dev(case.cu_rows), dev(case.row_lens),
+                           dev(case.block_table), dev(case.seq_lens), out_len,
+                           kvq.Scales(1.0, 1.0, 1.0, 1.0))
+    tail_inf = bool(torch.isneginf(got[:, :, head:]).all())
+    got = got[:, :, :head].cpu().numpy().astype(np.float64)
+    assert tail_inf, "entries past the visible keys must be -inf"
+    kp = ocache.dequantized(oracle_pools(case, "per_token_head", 1.0, 1.0), "k")
+    _, qh = ocache.quantize_q(case.q, 1.0)
+    want = ologits.paged_logits(qh, case.cu_rows, case.row_lens, kp, case.block_table, head)
+    mag = ologits.paged_logits(np.abs(qh), case.cu_rows, case.row_lens, np.abs(kp),
+                               case.block_table, head)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isneginf(got), ~fin), "-inf pattern differs"
+    assert (np.abs(got[fin] - want[fin]) <= REL * mag[fin] + 1e-30).all()
+
+    log("logits empty cache")
+    c0 = kvq.PagedCache(0, 2, 64, "fp8", "per_token_head")
+    q = dev_bf16(case.q)
+    cu = dev(np.array([0, 1, 3], dtype=np.int32))
+    zeros = dev(np.zeros(3, dtype=np.int32))
+    bt = dev(np.zeros((2, 1), dtype=np.int32))
+    got0 = kvq.paged_logits(c0, q, cu, zeros, bt, zeros[:2], 64, kvq.Scales(1.0, 1.0, 1.0, 1.0))
+    assert bool(torch.isneginf(got0).all())
+
+
 def test_logits_sampled_at_full_size(kvq):
     """The bench's workload (32 requests x 20,000 cached tokens, 4 query heads on one
     key head, D 128, one query row each), every logit of 4 sampled requests checked."""
