@@ -906,11 +906,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 
   // Ring of kRing page buffers, fully unrolled so every buffer is a named register
   // set: kRing - 1 pages are in flight while one is computed.  The first loads go
-  // out before the query is quantised.
+  // out before the query is quantised, under one branch and with the index clamped (a
+  // wave with one page loads it twice): with a branch around each load, the second
+  // load's wait for its block-table entry also waited for the first page (8 x 20,000
+  // Llama-shaped step 59.8 -> 59.4 us, window-128 layer 7.9 -> 7.5 us).
   PageRegs ring[kRing];
+  if (nwp > 0) {
 #pragma unroll
-  for (int r = 0; r < kRing - 1; ++r)
-    if (r < nwp) load_page(r, ring[r]);
+    for (int r = 0; r < kRing - 1; ++r) load_page(min(r, nwp - 1), ring[r]);
+  }
   if (app_late) append();
 
   // ---- query of the group: fused e4m3 quantisation (fp8) or plain bf16 ----------
