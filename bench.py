@@ -520,8 +520,20 @@ def main():
             fused(i)
         k1.record()
         torch.cuda.synchronize()
+        # warm: the same burst on one cache copy, which the 256 MB last-level cache
+        # partly holds from one launch to the next (the cold figure above is the one used)
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        for i in range(warmup):
+            fused(0)
+        w0.record()
+        for i in range(steps):
+            fused(0)
+        w1.record()
+        torch.cuda.synchronize()
         return {"wall_us": fused_wall, "span_us": fused_span,
                 "kernel_us": k0.elapsed_time(k1) * 1e3 / steps,
+                "warm_kernel_us": w0.elapsed_time(w1) * 1e3 / steps,
                 "unfused_wall_us": unfused_wall, "unfused_span_us": unfused_span}
 
     if "decode" in legs:
@@ -530,6 +542,22 @@ def main():
         legs_t = decode_step_legs(caches, args.steps, args.warmup)
         step_us, span_us, dk_us = legs_t["wall_us"], legs_t["span_us"], legs_t["kernel_us"]
         del caches
+        torch.cuda.empty_cache()
+        # a second denominator: what a plain 1 GiB device-to-device copy streams here
+        # (bytes read + written per second), and the same burst timed warm
+        csrc = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        cdst = torch.empty_like(csrc)
+        for _ in range(3):
+            cdst.copy_(csrc)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(10):
+            cdst.copy_(csrc)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 2 * COPY_BYTES / (c0.elapsed_time(c1) * 1e-3 / 10) / 1e9
+        del csrc, cdst
         torch.cuda.empty_cache()
         dec_b = decode_bytes(B, L, Hkv, Hq, D, 1, 8)
         wr_b = write_bytes(B, Hkv, D, 1, 8)
@@ -568,6 +596,14 @@ def main():
                          "kernel_timing": "HIP events around a burst of back-to-back "
                                           "fused decode-step launches after the timed "
                                           "steps; achieved counts decode + write bytes"},
+            "ceilings": {
+                "device_copy_GB_s": round(copy_gbs, 1),
+                "decode_frac_of_device_copy": round(achieved / copy_gbs, 4),
+                "warm_kernel_us": round(legs_t["warm_kernel_us"], 2),
+                "warm_GB_s": round((dec_b + wr_b) / (legs_t["warm_kernel_us"] * 1e-6) / 1e9, 1),
+                "note": "device copy: torch copy_ of 1 GiB, read + written bytes per second; "
+                        "warm: the same burst on one cache copy (338 MB, partly held by the "
+                        "256 MB last-level cache between launches)"},
         })
 
     if "bf16" in legs:
