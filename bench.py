@@ -368,6 +368,45 @@ def itl_sweep(contexts):
 
 # ---- GPU legs -------------------------------------------------------------------------------
 
+def mfma_ceiling(torch, dev):
+    """Sustained rate of the prefill's FP8 matrix instruction (32x32x64, 131,072 flops per
+    wave and instruction) from the measurement probe libkvq_probe.so: four independent
+    accumulator chains per wave, 1, 2 and 4 waves per SIMD; the best rate is reported.
+    None when the probe library was not built."""
+    import ctypes
+    path = os.path.join(ROOT, "fp8_quantized_paged_amd", "libkvq_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.kvq_probe_mfma_rate
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    iters = 4000
+    best = (0.0, 0)
+    rates = {}
+    for blocks in (256, 512, 1024):
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        st = torch.cuda.current_stream().cuda_stream
+        for _ in range(3):
+            assert fn(blocks, iters, out.data_ptr(), st) == 0
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            assert fn(blocks, iters, out.data_ptr(), st) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / 5
+        tfl = blocks * 4 * iters * 4 * 131072 / sec / 1e12
+        rates[f"{blocks // 256}_waves_per_simd"] = round(tfl, 1)
+        if tfl > best[0]:
+            best = (tfl, blocks)
+    return {"TFLOP_s": round(best[0], 1), "frac_of_published": round(best[0] / FP8_PEAK_TFLOPS, 4),
+            "waves_per_simd": best[1] // 256, "by_waves_per_simd": rates,
+            "probe": "back-to-back v_mfma_f32_32x32x64_f8f6f4, four independent chains per "
+                     "wave, 256 workgroups of 4 waves per wave-per-SIMD step"}
+
+
 class Timer:
     """HIP events on torch's current stream, which is the stream libkvq launches on."""
 
@@ -773,6 +812,10 @@ def main():
             "time_vs_mfma_chain": round(float(np.mean(us_v)) / float(np.mean(us)), 3)}
         del c
         torch.cuda.empty_cache()
+        mr = mfma_ceiling(torch, dev)
+        if mr is not None:
+            result["prefill_hd256"]["mfma_ceiling"] = {
+                **mr, "prefill_frac_of_measured": round(tf / mr["TFLOP_s"], 4)}
 
     for leg, (Hq_, Hkv_, D_) in (("prefill_d128", (32, 8, 128)), ("prefill_d64", (64, 8, 64))):
         if leg not in legs:

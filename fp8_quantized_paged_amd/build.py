@@ -17,6 +17,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvq.so")
+# measurement probe (bench.py only; not part of the library or its source hash)
+PROBE_SRC = os.path.join(HERE, "probe", "mfma_rate.hip")
+PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["host.cpp", "cache_write.hip", "decode.hip", "decode_noalloc.hip", "prefill.hip", "prefill_d64.hip",
@@ -95,6 +98,14 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    if os.path.exists(PROBE_SRC):
+        cmd = [cc, "-shared", PROBE_SRC, "-o", PROBE_LIB + ".tmp", *COMMON_FLAGS, *extra_flags]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if p.returncode != 0:
+            raise RuntimeError(f"hipcc failed on the probe:\n{p.stdout}")
+        os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return LIB
 
 
