@@ -27,7 +27,7 @@
 // buffer resource that drops the stores of lanes without output, so no branch hides a
 // memory instruction from the compiler's wait counts: they then keep two tiles in
 // flight (with the loads and stores behind branches each wait also drained the
-// prefetched tiles; indexer shape, 8 cache copies rotated: 22.9 -> 22.0 us).
+// prefetched tiles; indexer shape, 8 cache copies rotated: 22.9 -> 21.8 us).
 #include <algorithm>
 
 #include "kvq_device.h"
@@ -50,7 +50,10 @@ constexpr int kMaxIters = 12;           // tiles per workgroup, at most (2 page 
 // loads it has in flight, so the CU holding the most tiles sets the time).  Indexer
 // shape (32 x 20,000 keys, D 128, 5,024 tiles), round-robin A/B: 512 workgroups of 10
 // tiles, tile ring of three 22.2 us; one tile in flight: 736 workgroups of 7 tiles 26.2
-// us, 640 of 8 28.5 us; the ring at three workgroups per CU 28.4 us.
+// us, 640 of 8 28.5 us; the ring at three workgroups per CU 28.4 us.  Re-measured once
+// the ring really kept two tiles in flight (see the header): 768 workgroups at three
+// waves per SIMD 21.5 against 21.9 us, 1,024 23.2 us -- within the spread of the
+// method for 768, so the target stays.
 constexpr int kTargetGroups = 512;
 
 struct LogitsArgs {
