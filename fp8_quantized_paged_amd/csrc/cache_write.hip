@@ -17,13 +17,19 @@
 // dim-major: when the 16 tokens fill one page in order (slots 16 p .. 16 p + 15, the
 // usual bulk fill; every wave checks the block's 16 slots itself with scalar loads) the
 // codes are transposed through LDS and every channel row of the page tile is written
-// with one 16-byte store (32 bytes for bf16); otherwise each lane stores its bytes
-// where they belong (one byte per channel row).  The transpose stages the block
+// with one 16-byte store (32 bytes for bf16).  When the 16 tokens instead end one page
+// and start another, each run in order (a chunk that begins mid-page, any page table),
+// the same staging feeds each channel row's two parts in aligned pieces of 1, 2, 4 and
+// 8 elements (mid-page fill 486 -> 232 us, head_dim-256 8,192 tokens 27.1 -> 15.9 us);
+// otherwise each lane stores its bytes where they belong (one byte per channel row).
+// The transpose stages the block
 // token-major (each lane one 8- or 16-byte LDS write) and each channel's thread gathers
 // its 16 values with byte (bf16: 16-bit) reads, which neighbouring lanes share per
 // dword; staging channel-major instead took one-byte LDS writes that the 32 (head_dim
 // 256) or 16 lanes of a row aimed at one bank (head_dim-256 8,192-token write 20.2 ->
 // 10.5 us, 131,072 tokens 265 -> 146 us; Llama-shaped whole-cache fill 188 -> 176 us).
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_host.h"
 
@@ -57,17 +63,40 @@ __global__ __launch_bounds__(2 * D) void cache_write_kernel(
     kw = *reinterpret_cast<const uint4*>(k + src + c * 8);
     vw = *reinterpret_cast<const uint4*>(v + src + c * 8);
   }
-  // whole-page fast path: 16 tokens present, slots 16 p + j in order.  The block's 16
-  // slots are read at uniform addresses (scalar loads), so every wave reaches the same
-  // decision on its own, without a workgroup vote.
-  int64_t slot0 = -1;
-  bool page_run = false;
+  // Whole-page fast path: 16 tokens present, slots 16 p + j in order.  Split path: the
+  // block starts at offset koff != 0 of a page, its first 16 - koff tokens fill that
+  // page's end in order and its last koff tokens start another page in order (a chunk
+  // that begins mid-page; the two pages need not be neighbours).  The block's slots are
+  // read at uniform addresses (scalar loads), so every wave reaches the same decision
+  // on its own, without a workgroup vote.
+  int64_t slot0 = -1, slotB = 0;
+  int koff = 0;
+  bool page_run = false, split_run = false;
   if (t0 + kWriteTokens <= num_tokens) {
-    slot0 = slots[t0];
+    // all 16 loads in one batch, and the whole-page test first: a split test that
+    // fetched the second run's first slot on its own put a second scalar round trip on
+    // every block (head_dim-256 8,192-token write 10.8 -> 12.3 us)
+    int64_t sj[kWriteTokens];
+#pragma unroll
+    for (int j = 0; j < kWriteTokens; ++j) sj[j] = slots[t0 + j];
+    slot0 = sj[0];
     bool in_order = slot0 >= 0 && (slot0 & 15) == 0;
 #pragma unroll
-    for (int j = 1; j < kWriteTokens; ++j) in_order &= slots[t0 + j] == slot0 + j;
+    for (int j = 1; j < kWriteTokens; ++j) in_order &= sj[j] == slot0 + j;
     page_run = in_order;
+    if (!page_run && slot0 >= 0) {
+      // the split check, off the whole-page path: consecutive slots, a page starting
+      // only at token 16 - koff
+      koff = (int)(slot0 & 15);
+      bool run = koff != 0;
+#pragma unroll
+      for (int j = 1; j < kWriteTokens; ++j) {
+        const bool start = (sj[j] & 15) == 0;
+        run &= start ? (sj[j] >= 0) & (j == kWriteTokens - koff) : sj[j] == sj[j - 1] + 1;
+        slotB = j == kWriteTokens - koff ? sj[j] : slotB;
+      }
+      split_run = run;
+    }
   }
   // per-KV-head mode: k_scales / v_scales hold one scale per head (per-tensor: null)
   float ks = k_scale, vs = v_scale;
@@ -79,7 +108,7 @@ __global__ __launch_bounds__(2 * D) void cache_write_kernel(
       vs = v_scales[h];
     }
   }
-  if (!page_run) {
+  if (!page_run && !split_run) {
     // any slot pattern: every (token, head) row on its own (rows of skipped tokens
     // simply do nothing; whole rows of lanes agree)
     if (slot >= 0) {
@@ -89,68 +118,120 @@ __global__ __launch_bounds__(2 * D) void cache_write_kernel(
     }
     return;
   }
-  const int64_t tile = (slot0 >> 4) * num_heads + h;  // the page's (page, head) tile
-  if constexpr (!kFp8) {
-    // bf16 cache: K row copied, V values staged in LDS
-    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(k_pages) + (tile * kPage + i) * D +
-                              c * 8) = kw;
-    *reinterpret_cast<uint4*>(vt + (i * D + c * 8) * 2) = vw;
-  } else {
-    const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
-    const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
-    float kf[8], vf[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kf[2 * j] = bf16_bits_to_float(kk[j] & 0xFFFFu);
-      kf[2 * j + 1] = bf16_bits_to_float(kk[j] >> 16);
-      vf[2 * j] = bf16_bits_to_float(vv[j] & 0xFFFFu);
-      vf[2 * j + 1] = bf16_bits_to_float(vv[j] >> 16);
-    }
-    if constexpr (kPerTokenHead) {
-      const uint32_t kv = row_amax_bf16_kv<kLanesPerRow>(kw, vw);
-      const uint32_t ka = kv << 16, va = kv & 0xFFFF0000u;  // float32 magnitude bits
-      const RowScale krs = row_scale(ka), vrs = row_scale(va);
-      ks = krs.s;
-      vs = vrs.s;
-      kr = krs.r;
-      vr = vrs.r;
-      kfast = krs.fast;
-      vfast = vrs.fast;
-      if (c == 0) {
-        k_scales[tile * kPage + i] = ks;
-        v_scales[tile * kPage + i] = vs;
-      }
-    }
-    *reinterpret_cast<uint2*>(k_pages + (tile * kPage + i) * D + c * 8) =
-        make_uint2(e4m3_quantize4_row(kf, ks, kr, kfast), e4m3_quantize4_row(kf + 4, ks, kr, kfast));
-    const uint32_t vlo = e4m3_quantize4_row(vf, vs, vr, vfast);
-    const uint32_t vhi = e4m3_quantize4_row(vf + 4, vs, vr, vfast);
-    *reinterpret_cast<uint2*>(vt + i * D + c * 8) = make_uint2(vlo, vhi);
-  }
-  __syncthreads();
-  // one channel row of the V tile per thread: 16 codes (16 bytes) or 16 bf16 (32 bytes),
-  // gathered from the 16 staged tokens
-  if (threadIdx.x < D) {
-    const int d = threadIdx.x;
-    uint32_t wd[4 * EB];
-    if constexpr (kFp8) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t x = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x |= (uint32_t)vt[(4 * q + e) * D + d] << (8 * e);
-        wd[q] = x;
-      }
+  // the staged path: K rows and scales to their slots, V through LDS to the page tiles
+  auto staged = [&](auto split_tag) {
+    constexpr bool kSplit = decltype(split_tag)::value;
+    const int64_t tile = (slot0 >> 4) * num_heads + h;  // the page's (page, head) tile
+    // K rows and scales: each token's own slot (for a whole page: the page's tile, offset i)
+    const int64_t rt = kSplit ? (slot >> 4) * num_heads + h : tile;
+    const int ro = kSplit ? (int)(slot & 15) : i;
+    if constexpr (!kFp8) {
+      // bf16 cache: K row copied, V values staged in LDS
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(k_pages) + (rt * kPage + ro) * D +
+                                c * 8) = kw;
+      *reinterpret_cast<uint4*>(vt + (i * D + c * 8) * 2) = vw;
     } else {
-      const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        wd[q] = (uint32_t)vt16[(2 * q) * D + d] | ((uint32_t)vt16[(2 * q + 1) * D + d] << 16);
+      const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
+      const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
+      float kf[8], vf[8];
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kf[2 * j] = bf16_bits_to_float(kk[j] & 0xFFFFu);
+        kf[2 * j + 1] = bf16_bits_to_float(kk[j] >> 16);
+        vf[2 * j] = bf16_bits_to_float(vv[j] & 0xFFFFu);
+        vf[2 * j + 1] = bf16_bits_to_float(vv[j] >> 16);
+      }
+      if constexpr (kPerTokenHead) {
+        const uint32_t kv = row_amax_bf16_kv<kLanesPerRow>(kw, vw);
+        const uint32_t ka = kv << 16, va = kv & 0xFFFF0000u;  // float32 magnitude bits
+        const RowScale krs = row_scale(ka), vrs = row_scale(va);
+        ks = krs.s;
+        vs = vrs.s;
+        kr = krs.r;
+        vr = vrs.r;
+        kfast = krs.fast;
+        vfast = vrs.fast;
+        if (c == 0) {
+          k_scales[rt * kPage + ro] = ks;
+          v_scales[rt * kPage + ro] = vs;
+        }
+      }
+      *reinterpret_cast<uint2*>(k_pages + (rt * kPage + ro) * D + c * 8) =
+          make_uint2(e4m3_quantize4_row(kf, ks, kr, kfast), e4m3_quantize4_row(kf + 4, ks, kr, kfast));
+      const uint32_t vlo = e4m3_quantize4_row(vf, vs, vr, vfast);
+      const uint32_t vhi = e4m3_quantize4_row(vf + 4, vs, vr, vfast);
+      *reinterpret_cast<uint2*>(vt + i * D + c * 8) = make_uint2(vlo, vhi);
     }
-    uint4* dst = reinterpret_cast<uint4*>(v_pages + (tile * D + d) * kPage * EB);
-#pragma unroll
-    for (int w = 0; w < EB; ++w) dst[w] = make_uint4(wd[4 * w], wd[4 * w + 1], wd[4 * w + 2], wd[4 * w + 3]);
-  }
+    __syncthreads();
+    if constexpr (kSplit) {
+      // elements koff .. 15 of page A's channel row d come from tokens 0 .. 15 - koff,
+      // elements 0 .. koff - 1 of page B's from tokens 16 - koff .. 15; each part goes out
+      // in aligned pieces of 1, 2, 4 and 8 elements (the bits of koff), leaving the rows'
+      // other elements -- other tokens' -- untouched
+      if (threadIdx.x < D) {
+        const int d = threadIdx.x;
+        uint8_t* rowA = v_pages + (((slot0 >> 4) * num_heads + h) * D + d) * kPage * EB;
+        uint8_t* rowB = v_pages + (((slotB >> 4) * num_heads + h) * D + d) * kPage * EB;
+        auto put = [&](uint8_t* row, int e0, auto w_tag, int tok0) {
+          constexpr int W = decltype(w_tag)::value;  // elements
+          constexpr int NB = W * EB;                 // bytes
+          uint32_t x[NB >= 4 ? NB / 4 : 1] = {};
+  #pragma unroll
+          for (int u = 0; u < W; ++u) {
+            const uint32_t val = kFp8 ? (uint32_t)vt[(tok0 + u) * D + d]
+                                      : (uint32_t)reinterpret_cast<const uint16_t*>(vt)[(tok0 + u) * D + d];
+            x[(u * EB) / 4] |= val << (8 * ((u * EB) % 4));
+          }
+          uint8_t* dst = row + e0 * EB;
+          if constexpr (NB == 1) *dst = (uint8_t)x[0];
+          else if constexpr (NB == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)x[0];
+          else if constexpr (NB == 4) *reinterpret_cast<uint32_t*>(dst) = x[0];
+          else if constexpr (NB == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(x[0], x[1]);
+          else *reinterpret_cast<uint4*>(dst) = make_uint4(x[0], x[1], x[2], x[3]);
+        };
+        using W1 = std::integral_constant<int, 1>;
+        using W2 = std::integral_constant<int, 2>;
+        using W4 = std::integral_constant<int, 4>;
+        using W8 = std::integral_constant<int, 8>;
+        int e = koff;  // page A: up to the page's end, smallest pieces first
+        if (e & 1) { put(rowA, e, W1{}, e - koff); e += 1; }
+        if (e & 2) { put(rowA, e, W2{}, e - koff); e += 2; }
+        if (e & 4) { put(rowA, e, W4{}, e - koff); e += 4; }
+        if (e & 8) { put(rowA, e, W8{}, e - koff); }
+        int f = 0;     // page B: from the page's start, largest pieces first
+        if (koff & 8) { put(rowB, f, W8{}, kWriteTokens - koff + f); f += 8; }
+        if (koff & 4) { put(rowB, f, W4{}, kWriteTokens - koff + f); f += 4; }
+        if (koff & 2) { put(rowB, f, W2{}, kWriteTokens - koff + f); f += 2; }
+        if (koff & 1) { put(rowB, f, W1{}, kWriteTokens - koff + f); }
+      }
+      return;
+    }
+    // one channel row of the V tile per thread: 16 codes (16 bytes) or 16 bf16 (32 bytes),
+    // gathered from the 16 staged tokens
+    if (threadIdx.x < D) {
+      const int d = threadIdx.x;
+      uint32_t wd[4 * EB];
+      if constexpr (kFp8) {
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t x = 0;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) x |= (uint32_t)vt[(4 * q + e) * D + d] << (8 * e);
+          wd[q] = x;
+        }
+      } else {
+        const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
+  #pragma unroll
+        for (int q = 0; q < 8; ++q)
+          wd[q] = (uint32_t)vt16[(2 * q) * D + d] | ((uint32_t)vt16[(2 * q + 1) * D + d] << 16);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(v_pages + (tile * D + d) * kPage * EB);
+  #pragma unroll
+      for (int w = 0; w < EB; ++w) dst[w] = make_uint4(wd[4 * w], wd[4 * w + 1], wd[4 * w + 2], wd[4 * w + 3]);
+    }
+  };
+  if (split_run) staged(std::true_type{});
+  else staged(std::false_type{});
 }
 
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x,

@@ -295,3 +295,57 @@ def test_cache_write_mixed_page_blocks(kvq, mode):
     vraw = c.v_pages.view(torch.uint8).cpu().numpy().reshape(P, H, D, 16, eb)
     assert (kraw[untouched // 16, :, untouched % 16] == 0x5A).all()
     assert (vraw[untouched // 16, :, :, untouched % 16] == 0x5A).all()
+
+
+def _mid_page_slots(seed, starts_lens, pages_per_seq):
+    """Slots of several sequences' new tokens, each chunk starting at its own position
+    (mostly mid-page) in a permuted page table; the pages of different sequences are
+    distinct, so no slot is written twice."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(len(starts_lens) * pages_per_seq)
+    out = []
+    for i, (start, n) in enumerate(starts_lens):
+        pos = start + np.arange(n)
+        pages = perm[i * pages_per_seq:(i + 1) * pages_per_seq]
+        out.append(pages[pos // 16] * 16 + pos % 16)
+    return np.concatenate(out).astype(np.int64), len(starts_lens) * pages_per_seq
+
+
+@pytest.mark.parametrize("mode", ["per_token_head", "per_tensor", "bf16"])
+@pytest.mark.parametrize("D", [64, 256])
+def test_cache_write_mid_page_chunks(kvq, mode, D):
+    """Chunks that start mid-page: a 16-token block then ends one page in order and starts
+    another (any page of the table) in order -- the two-run store path -- and chunks whose
+    blocks straddle sequences (the single-row path).  Bit-exact to the oracle; every slot no
+    token was written to keeps its marker (the rows of a page's other tokens survive)."""
+    H = 2
+    starts_lens = [(1, 16 * 5 + 3), (2, 40), (7, 16 * 3), (8, 37), (13, 70), (15, 16 * 4 + 1),
+                   (0, 33)]
+    slots, P = _mid_page_slots(77 + D, starts_lens, 8)
+    T = len(slots)
+    rng = np.random.default_rng(6 + D)
+    k = workloads.bf16_round(rng.standard_normal((T, H, D)).astype(np.float32) * 3)
+    v = workloads.bf16_round(rng.standard_normal((T, H, D)).astype(np.float32) * 3)
+    log(f"cache_write mid-page chunks {mode} D={D}: {T} tokens")
+    dtype = "bf16" if mode == "bf16" else "fp8"
+    c = kvq.PagedCache(P, H, D, dtype, "per_tensor" if mode == "bf16" else mode)
+    c.k_pages.view(torch.uint8).fill_(0x5A)
+    c.v_pages.view(torch.uint8).fill_(0x5A)
+    kvq.cache_write(c, dev_bf16(k), dev_bf16(v), dev(slots), 0.5, 0.25)
+    got = read_pools(c)
+    page, off = slots // 16, slots % 16
+    if mode == "bf16":
+        assert np.array_equal(got["k"][page, :, off], k)
+        assert np.array_equal(got["v"][page, :, off], v)
+    else:
+        want = ocache.new_pools(P, H, D)
+        ocache.cache_write(want, k, v, slots, mode, 0.5, 0.25)
+        _check_pools(got, want, slots)
+    written = np.zeros(P * 16, bool)
+    written[slots] = True
+    untouched = np.nonzero(~written)[0]
+    eb = 2 if mode == "bf16" else 1
+    kraw = c.k_pages.view(torch.uint8).cpu().numpy().reshape(P, H, 16, D * eb)
+    vraw = c.v_pages.view(torch.uint8).cpu().numpy().reshape(P, H, D, 16, eb)
+    assert (kraw[untouched // 16, :, untouched % 16] == 0x5A).all()
+    assert (vraw[untouched // 16, :, :, untouched % 16] == 0x5A).all()
