@@ -979,16 +979,20 @@ def main():
         # cache (160,000 tokens x 8 KV heads, D 128, per-token-head scales) and the
         # head_dim-256 prefill chunk's 8,192 new tokens (4 KV heads, per-token-head)
         cw = {}
-        for name, (T, Hkv_, D_) in (("llama8b_fill", (160000, 8, 128)),
-                                     ("hd256_new_tokens", (8192, 4, 256))):
-            P_ = (T + 15) // 16
+        # (the third: the same fill with every 16-token block starting two tokens into a
+        # page, as when a chunk begins mid-page)
+        for name, (T, Hkv_, D_, shift) in (("llama8b_fill", (160000, 8, 128, 0)),
+                                            ("hd256_new_tokens", (8192, 4, 256, 0)),
+                                            ("llama8b_fill_mid_page", (160000, 8, 128, 2))):
+            P_ = (T + shift + 15) // 16
             c = kvq.PagedCache(P_, Hkv_, D_, "fp8", "per_token_head")
             kk = dev_normal((T, Hkv_, D_), 1.0, 7000 + D_)
             vv = dev_normal((T, Hkv_, D_), 1.0, 7100 + D_)
-            sl_ = torch.arange(T, dtype=torch.int64, device=dev)
+            sl_ = torch.arange(shift, shift + T, dtype=torch.int64, device=dev)
             us = timer.run(lambda i: kvq.cache_write(c, kk, vv, sl_), 20, 3, warm_ms=100.0)
             nb = write_bytes(T, Hkv_, D_, 1, 8) + T * 8   # + the slot mapping
-            cw[name] = {"tokens": T, "kv_heads": Hkv_, "head_dim": D_, **stats(us),
+            cw[name] = {"tokens": T, "kv_heads": Hkv_, "head_dim": D_, "slot_shift": shift,
+                        **stats(us),
                         "bytes": nb, "GB_s": round(nb / (float(np.mean(us)) * 1e-6) / 1e9, 1),
                         "frac_hbm": round(nb / (float(np.mean(us)) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
             del c, kk, vv
