@@ -208,3 +208,18 @@ def test_single_hip_runtime_in_process():
                              __import__("os").path.abspath(__file__))))
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "1"
+
+
+def test_mfma_probe_library_loads_and_checks_arguments():
+    """The measurement probe beside the library (bench.py only) is built with it, loads
+    without a GPU, and refuses bad arguments before launching anything."""
+    import os
+    path = os.path.join(os.path.dirname(kvq.__file__), "libkvq_probe.so")
+    assert os.path.exists(path), "build() also builds libkvq_probe.so"
+    lib = ctypes.CDLL(path)
+    fn = lib.kvq_probe_mfma_rate
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert fn(0, 10, None, None) == 1
+    assert fn(256, 0, None, None) == 1
+    assert fn(256, 10, None, None) == 1   # no output buffer
