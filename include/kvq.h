@@ -203,7 +203,10 @@ kvq_status kvq_quantize_fp8(const void* x, int64_t n, float scale, uint8_t* code
  * prefix (KVQ_DECODE_COUNTER_BYTES) followed by the split-K partial results; 0 when
  * every sequence fits in one split (then no workspace is read or written).
  * pages_per_split = 0 selects the library's choice, which depends only on the
- * arguments given here; otherwise 1..256.  bytes [host].
+ * arguments given here (it spreads max_seq_len over about two workgroups per CU);
+ * otherwise 1..256.  A batch whose lengths differ widely runs faster with a smaller
+ * value chosen from its actual lengths, since the library sees only max_seq_len.
+ * bytes [host].
  */
 kvq_status kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t max_seq_len,
