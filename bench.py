@@ -971,7 +971,49 @@ def main():
             "frac_hbm": round(nb3 / (us3 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "timing": "HIP events around a burst of back-to-back launches over rotating "
                       "cache copies"}
-        del cs
+        del cs, lout
+        torch.cuda.empty_cache()
+        # prefill-time selection: one request of 8,192 new rows (causal: row i sees i + 1
+        # keys) over its 8,192 keys, same heads and cache; 1 GB of float32 scores, so
+        # bound by HBM writes -- set beside a plain 1 GB fill on the same output
+        R4 = L4 = 8192
+        pc = workloads.make_logits_case(113, [L4], [R4], 4, 1, 128, table="perm",
+                                        name="paged logits rows")
+        c4 = kvq.PagedCache(pc.num_pages, 1, 128, "fp8", "per_token_head")
+        kvq.cache_write(c4, to_dev(pc.k), to_dev(pc.v),
+                        torch.from_numpy(pc.slots.astype(np.int64)).to(dev))
+        pq = to_dev(pc.q)
+        pcu, prl = torch.from_numpy(pc.cu_rows).to(dev), torch.from_numpy(pc.row_lens).to(dev)
+        pbt, psl = (torch.from_numpy(pc.block_table).to(dev),
+                    torch.from_numpy(pc.seq_lens).to(dev))
+        pout = torch.empty((R4, 4, L4), dtype=torch.float32, device=dev)
+
+        def timed(fn, n):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(n):
+                fn()
+            t1.record()
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) * 1e3 / n
+        n4 = max(5, min(args.steps, 40))
+        us4 = timed(lambda: kvq.paged_logits(c4, pq, pcu, prl, pbt, psl, L4, ones, out=pout), n4)
+        usf = timed(lambda: pout.fill_(0.0), n4)
+        nb4 = R4 * 4 * L4 * 4 + L4 * 132
+        result["paged_logits"]["prefill_rows"] = {
+            "workload": "1 request x 8,192 query rows (causal) x 8,192 cached tokens, 4 "
+                        "query heads / 1 key head, D 128, fp8 per-token-head; float32 "
+                        "[8,192][4][8,192] out",
+            "us_per_launch": round(us4, 2), "bytes": nb4,
+            "GB_s": round(nb4 / (us4 * 1e-6) / 1e9, 1),
+            "frac_hbm": round(nb4 / (us4 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "fill_1GB_GB_s": round(R4 * 4 * L4 * 4 / (usf * 1e-6) / 1e9, 1),
+            "frac_of_fill": round(usf / us4, 4)}
+        del c4, pout
         torch.cuda.empty_cache()
 
     if "cache_write" in legs:

@@ -132,7 +132,7 @@ _SIGS = {
     "kvq_prefill_attention_accum": (ctypes.c_int, [_PD, _p, _p, _i32, _i32, _p, _i32, _p,
                                                    _i32, ctypes.POINTER(Scales), _i32, _i32,
                                                    _f32, _p, ctypes.c_int, ctypes.c_int, _p]),
-    "kvq_paged_logits": (ctypes.c_int, [_PD, _p, _p, _i32, _i32, _p, _p, _i32, _p,
+    "kvq_paged_logits": (ctypes.c_int, [_PD, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _p,
                                         ctypes.POINTER(Scales), _p, _i32, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -415,7 +415,7 @@ def paged_logits(cache: PagedCache, q, cu_rows, row_lens, block_table, seq_lens,
         out = torch.empty((R, Hq, out_len), dtype=torch.float32, device=q.device)
     d = cache.desc()
     _check(_lib.kvq_paged_logits(
-        ctypes.byref(d), _ptr(q), _ptr(cu_rows), int(seq_lens.numel()), Hq, _ptr(row_lens),
+        ctypes.byref(d), _ptr(q), _ptr(cu_rows), int(seq_lens.numel()), R, Hq, _ptr(row_lens),
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), ctypes.byref(scales),
         _ptr(out), out.shape[2], _stream(stream, q.device)), "paged_logits")
     return out

@@ -55,6 +55,16 @@ constexpr int kMaxIters = 12;           // tiles per workgroup, at most (2 page 
 // waves per SIMD 21.5 against 21.9 us, 1,024 23.2 us -- within the spread of the
 // method for 768, so the target stays.
 constexpr int kTargetGroups = 512;
+// Requests with more than 32 (row, head) pairs on average (prefill-time selection:
+// thousands of rows per request, 1 GB of scores and more) are also split over their
+// 32-pair chunks, one per workgroup for the average request (a longer one loops), the
+// tiles per workgroup then chosen for kTargetGroups over tiles x chunks.  A key tile is
+// read once per chunk, from the L2 in practice (the workgroups sharing it run
+// together).  Before, with the grid over tiles only, a request of 8,192 rows and
+// 8,192 keys (4 query heads, 1 GB of scores) ran on 64 workgroups: 2.69 ms; split
+// over chunks 448 us (at 4 and 16 chunks per workgroup 487 and 383 us, but a batch
+// with one long request then waits on a few long workgroups: 404 and 684 us against
+// 480 us at one).
 
 struct LogitsArgs {
   const uint16_t* q;          // bf16 [rows][Hq][D]
@@ -66,7 +76,8 @@ struct LogitsArgs {
   const uint8_t* k_pages;     // [P][Hkv][16][D] codes or bf16
   const float* k_scales;      // per-token-head [P][Hkv][16], per-KV-head [Hkv], or null
   int32_t num_kv_heads, num_q_heads;
-  int32_t groups, iters;      // workgroups per (request, head), tiles per workgroup
+  int32_t groups, iters;      // workgroups per (request, head, chunk set), tiles per workgroup
+  int32_t cgroups;            // chunk sets per request: workgroup c takes chunks c, c + cgroups, ..
   float q_scale, k_scale;     // k_scale: per-tensor
   float* out;                 // [rows][Hq][out_stride]
   int32_t span_bytes;         // bytes a chunk's stores may reach from its first pair's row
@@ -85,7 +96,8 @@ __device__ __forceinline__ half8_t codes_to_f16(uint32_t lo, uint32_t hi) {
 // kMode: 0 per-tensor, 1 per-token-head, 2 per-KV-head (FP8 only)
 // Two waves per SIMD: a launch's workgroups (two per CU) stay resident at once.  (A
 // three-wave budget spilled the ring at head_dim 128.)
-template <int D, bool kFp8, int kMode, bool kBuf>
+// kSt: 0 plain stores, 1 buffer stores, 2 buffer stores after a transpose in lane quads
+template <int D, bool kFp8, int kMode, int kSt>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 logits_kernel(const LogitsArgs a) {
   constexpr int ES = kFp8 ? 1 : 2;       // bytes per element
@@ -93,6 +105,7 @@ logits_kernel(const LogitsArgs a) {
   constexpr int NV = HB / 16;            // 16-byte loads per half row
   constexpr int NS = D / 16;             // MFMA steps over D
   constexpr int QS = D * ES + 16;        // LDS stride of a pair's query row (padded)
+  constexpr bool kBuf = kSt > 0;
   __shared__ __align__(16) uint8_t q_lds[32 * QS];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int lane = (int)threadIdx.x % kWave;
@@ -101,11 +114,12 @@ logits_kernel(const LogitsArgs a) {
   const int g = (int)(blockIdx.x % (unsigned)H);
   const int rest = (int)(blockIdx.x / (unsigned)H);
   const int grp0 = rest % a.groups;
-  const int b = rest / a.groups;
+  const int cset = (rest / a.groups) % a.cgroups;
+  const int b = rest / a.groups / a.cgroups;
   const int G = a.num_q_heads / H;
   const int r0 = a.cu_rows[b];
   const int npairs = (a.cu_rows[b + 1] - r0) * G;
-  if (npairs <= 0) return;               // whole workgroup: no barrier is skipped
+  if (npairs <= 32 * cset) return;       // whole workgroup: no barrier is skipped
   const int L = a.seq_lens[b];
   const int npages = (L + kPage - 1) / kPage;
   const int* bt = a.block_table + (int64_t)b * a.bt_stride;
@@ -157,7 +171,7 @@ logits_kernel(const LogitsArgs a) {
 
   // 16-byte query pieces per thread and chunk (32 pairs x D / 8 pieces)
   constexpr int QI = (32 * (D / 8) + kThreads - 1) / kThreads;
-  for (int p0 = 0; p0 < npairs; p0 += 32) {
+  for (int p0 = 32 * cset; p0 < npairs; p0 += 32 * a.cgroups) {
     // The chunk's query rows are loaded first, then the first tiles' key rows, so the
     // key loads stay in flight while the query is encoded (memory operations complete
     // in order for the wait counter: a query load issued after them would wait for
@@ -205,17 +219,30 @@ logits_kernel(const LogitsArgs a) {
     const int pr = r0 + (pair_ok ? p / G : 0), ph = g * G + (pair_ok ? p % G : 0);
     const int vis = pair_ok ? min(a.row_lens[pr], L) : 0;
     float* orow = a.out + ((int64_t)pr * a.num_q_heads + ph) * a.out_stride;
-    // Stores (kBuf): a buffer resource from the chunk's first pair's output row, a.span_bytes
-    // long (the host checked that every pair of a chunk stores inside it); a lane with
-    // nothing to store takes an offset past that range, which the hardware drops.  So
-    // the store needs no branch: every store is issued, and the compiler counts it
-    // exactly in the waits for the key loads (a store behind a branch made it wait
-    // for a prefetched tile too).  Without kBuf (a chunk spanning 2 GB or more of
+    // Stores (kSt 1, 2): a buffer resource from the chunk's first pair's output row,
+    // a.span_bytes long (the host checked that every pair of a chunk stores inside it);
+    // a lane with nothing to store takes an offset past that range, which the hardware
+    // drops.  So the store needs no branch: every store is issued, and the compiler
+    // counts it exactly in the waits for the key loads (a store behind a branch made it
+    // wait for a prefetched tile too).  With kSt 0 (a chunk spanning 2 GB or more of
     // output) the stores are plain and conditional.
     const int64_t base_f = ((int64_t)(r0 + p0 / G) * a.num_q_heads + g * G + p0 % G) * a.out_stride;
     int rel_f = 0;  // this pair's row, in floats from base_f
-    if constexpr (kBuf)
+    if constexpr (kSt == 1)
       rel_f = pair_ok ? (int)(((int64_t)pr * a.num_q_heads + ph) * a.out_stride - base_f) : 0;
+    // kSt 2: stores go out after a 4 x 4 transpose within each quad of lanes (below):
+    // store t of lane 4 m + j writes pair 4 m + t, so each lane needs the rows of the four
+    // pairs of its quad (offsets in floats from base_f; -1 where the pair does not exist).
+    int rel_q[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int pq = p0 + (col & ~3) + t;
+      rel_q[t] = -1;
+      if constexpr (kSt == 2)
+        if (pq < npairs)
+          rel_q[t] = (int)(((int64_t)(r0 + pq / G) * a.num_q_heads + g * G + pq % G) *
+                               a.out_stride - base_f);
+    }
     const __amdgpu_buffer_rsrc_t orsrc =  // gfx9 word 3: 32-bit raw buffer
         __builtin_amdgcn_make_buffer_rsrc(a.out + base_f, 0, kBuf ? a.span_bytes : 0, 0x00020000);
     __syncthreads();
@@ -251,25 +278,74 @@ logits_kernel(const LogitsArgs a) {
       }
       // ---- scale, mask (keys past the row's visible length -> -inf), store -----------
       // (every lane takes part in the scale permutes; only pair lanes store)
+      // logit of key kw + 8 q4 + 4 hg + e for pair col (register 4 q4 + e)
+      auto scaled = [&](int q4, int e) {
+        float sc = k_scale_h;
+        if constexpr (kFp8 && kMode == 1) sc = __shfl(t.sc, 8 * q4 + 4 * hg + e);
+        return kw + 8 * q4 + 4 * hg + e < vis ? acc[4 * q4 + e] * (kFp8 ? sc * a.q_scale : 1.0f)
+                                              : -INFINITY;
+      };
+      if constexpr (kSt == 2) {
+        float w[4][4];  // [key group q4][e]
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int k0 = kw + 8 * q4 + 4 * hg;
-        float v[4];
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int k0 = kw + 8 * q4 + 4 * hg;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float sc = k_scale_h;
+            if constexpr (kFp8 && kMode == 1) sc = __shfl(t.sc, 8 * q4 + 4 * hg + e);
+            w[q4][e] = k0 + e < vis ? acc[4 * q4 + e] * (kFp8 ? sc * a.q_scale : 1.0f) : -INFINITY;
+          }
+        }
+        // 4 x 4 transpose of the 16-byte groups within each lane quad (lane 4 m + j, slot
+        // t <- lane 4 m + t, slot j), in two exchanges over bit 0 and bit 1 of the lane:
+        // afterwards slot t holds keys kw + 8 j + 4 hg .. + 3 of pair 4 m + t, so store t
+        // writes 128 contiguous bytes (keys kw .. kw + 31) of each of 8 pairs, not 32
+        // bytes of each of 32.
+        const bool b0 = lane & 1, b1 = lane & 2;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float sc = k_scale_h;
-          if constexpr (kFp8 && kMode == 1) sc = __shfl(t.sc, 8 * q4 + 4 * hg + e);
-          v[e] = k0 + e < vis ? acc[4 * q4 + e] * (kFp8 ? sc * a.q_scale : 1.0f) : -INFINITY;
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const float snd = b0 ? w[2 * k][e] : w[2 * k + 1][e];
+            const float rcv = __int_as_float(
+                __builtin_amdgcn_update_dpp(0, __float_as_int(snd), 0xB1, 0xF, 0xF, false));
+            if (b0) w[2 * k][e] = rcv; else w[2 * k + 1][e] = rcv;
+          }
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const float snd = b1 ? w[k][e] : w[k + 2][e];
+            const float rcv = __int_as_float(
+                __builtin_amdgcn_update_dpp(0, __float_as_int(snd), 0x4E, 0xF, 0xF, false));
+            if (b1) w[k][e] = rcv; else w[k + 2][e] = rcv;
+          }
         }
-        if constexpr (kBuf) {
+        const int kq = kw + 8 * (lane & 3) + 4 * hg;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
           typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-          const u32x4v bits = {__float_as_uint(v[0]), __float_as_uint(v[1]),
-                               __float_as_uint(v[2]), __float_as_uint(v[3])};
+          const u32x4v bits = {__float_as_uint(w[t][0]), __float_as_uint(w[t][1]),
+                               __float_as_uint(w[t][2]), __float_as_uint(w[t][3])};
           // 0x7FFFFFF0: past any span_bytes (< 0x7FF00000), without wrapping
-          const int off = pair_ok && k0 < a.out_stride ? 4 * (rel_f + k0) : 0x7FFFFFF0;
+          const int off = rel_q[t] >= 0 && kq < a.out_stride ? 4 * (rel_q[t] + kq) : 0x7FFFFFF0;
           __builtin_amdgcn_raw_buffer_store_b128(bits, orsrc, off, 0, 0);
-        } else if (pair_ok && k0 < a.out_stride) {  // out_stride % 4 == 0: all 4 or none
-          *reinterpret_cast<float4*>(orow + k0) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      } else {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int k0 = kw + 8 * q4 + 4 * hg;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = scaled(q4, e);
+          if constexpr (kSt == 1) {
+            typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+            const u32x4v bits = {__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                 __float_as_uint(v[2]), __float_as_uint(v[3])};
+            const int off = pair_ok && k0 < a.out_stride ? 4 * (rel_f + k0) : 0x7FFFFFF0;
+            __builtin_amdgcn_raw_buffer_store_b128(bits, orsrc, off, 0, 0);
+          } else if (pair_ok && k0 < a.out_stride) {  // out_stride % 4 == 0: all 4 or none
+            *reinterpret_cast<float4*>(orow + k0) = make_float4(v[0], v[1], v[2], v[3]);
+          }
         }
       }
     };
@@ -290,28 +366,30 @@ logits_kernel(const LogitsArgs a) {
   }
 }
 
-template <int D, bool kFp8, bool kBuf>
+template <int D, bool kFp8, int kSt>
 static void launch_mode_b(int mode, const LogitsArgs& args, unsigned blocks, hipStream_t st) {
   if (!kFp8)
-    logits_kernel<D, false, 0, kBuf><<<blocks, kThreads, 0, st>>>(args);
+    logits_kernel<D, false, 0, kSt><<<blocks, kThreads, 0, st>>>(args);
   else if (mode == KVQ_SCALE_PER_TOKEN_HEAD)
-    logits_kernel<D, true, 1, kBuf><<<blocks, kThreads, 0, st>>>(args);
+    logits_kernel<D, true, 1, kSt><<<blocks, kThreads, 0, st>>>(args);
   else if (mode == KVQ_SCALE_PER_KV_HEAD)
-    logits_kernel<D, true, 2, kBuf><<<blocks, kThreads, 0, st>>>(args);
+    logits_kernel<D, true, 2, kSt><<<blocks, kThreads, 0, st>>>(args);
   else
-    logits_kernel<D, true, 0, kBuf><<<blocks, kThreads, 0, st>>>(args);
+    logits_kernel<D, true, 0, kSt><<<blocks, kThreads, 0, st>>>(args);
 }
 template <int D, bool kFp8>
-static void launch_mode(int mode, const LogitsArgs& args, unsigned blocks, hipStream_t st) {
-  if (args.span_bytes > 0) launch_mode_b<D, kFp8, true>(mode, args, blocks, st);
-  else launch_mode_b<D, kFp8, false>(mode, args, blocks, st);
+static void launch_mode(int mode, int store, const LogitsArgs& args, unsigned blocks,
+                        hipStream_t st) {
+  if (store == 2) launch_mode_b<D, kFp8, 2>(mode, args, blocks, st);
+  else if (store == 1) launch_mode_b<D, kFp8, 1>(mode, args, blocks, st);
+  else launch_mode_b<D, kFp8, 0>(mode, args, blocks, st);
 }
 
 template <int D>
-static void launch_dtype(const kvq_cache_desc* c, const LogitsArgs& args, unsigned blocks,
-                         hipStream_t st) {
-  if (c->dtype == KVQ_FP8_E4M3) launch_mode<D, true>(c->mode, args, blocks, st);
-  else launch_mode<D, false>(c->mode, args, blocks, st);
+static void launch_dtype(const kvq_cache_desc* c, int store, const LogitsArgs& args,
+                         unsigned blocks, hipStream_t st) {
+  if (c->dtype == KVQ_FP8_E4M3) launch_mode<D, true>(c->mode, store, args, blocks, st);
+  else launch_mode<D, false>(c->mode, store, args, blocks, st);
 }
 
 }  // namespace lg
@@ -321,19 +399,19 @@ using namespace kvq;
 
 extern "C" kvq_status kvq_paged_logits(const kvq_cache_desc* cache, const void* q,
                                        const int32_t* cu_rows, int32_t num_seqs,
-                                       int32_t num_q_heads, const int32_t* row_lens,
+                                       int32_t total_rows, int32_t num_q_heads, const int32_t* row_lens,
                                        const int32_t* block_table, int32_t block_table_stride,
                                        const int32_t* seq_lens, const kvq_scales* scales,
                                        float* out, int32_t out_stride, void* stream) {
   clear_error();
   if (kvq_status s = check_cache(cache)) return s;
-  if (num_seqs < 0 || num_q_heads <= 0 || out_stride < 0)
-    return fail(KVQ_ERR_INVALID_ARG, "num_seqs %d num_q_heads %d out_stride %d", num_seqs,
-                num_q_heads, out_stride);
+  if (num_seqs < 0 || total_rows < 0 || num_q_heads <= 0 || out_stride < 0)
+    return fail(KVQ_ERR_INVALID_ARG, "num_seqs %d total_rows %d num_q_heads %d out_stride %d",
+                num_seqs, total_rows, num_q_heads, out_stride);
   if (num_q_heads % cache->num_kv_heads)
     return fail(KVQ_ERR_INVALID_ARG, "num_q_heads %d not a multiple of num_kv_heads %d",
                 num_q_heads, cache->num_kv_heads);
-  if (num_seqs == 0 || out_stride == 0) return KVQ_OK;
+  if (num_seqs == 0 || total_rows == 0 || out_stride == 0) return KVQ_OK;
   if (out_stride % 4)
     return fail(KVQ_ERR_INVALID_ARG, "out_stride %d is not a multiple of 4", out_stride);
   if (!q || !out || !cu_rows || !row_lens || !seq_lens || !block_table)
@@ -345,6 +423,7 @@ extern "C" kvq_status kvq_paged_logits(const kvq_cache_desc* cache, const void* 
       ((uintptr_t)cache->k_scales & 15u))
     return fail(KVQ_ERR_INVALID_ARG, "k_scales must be 16-byte aligned");
   lg::LogitsArgs a;
+  int64_t pairs = 0;  // (row, head) pairs of the average request, per key head
   a.q = static_cast<const uint16_t*>(q);
   a.cu_rows = cu_rows;
   a.row_lens = row_lens;
@@ -357,10 +436,18 @@ extern "C" kvq_status kvq_paged_logits(const kvq_cache_desc* cache, const void* 
   a.num_q_heads = num_q_heads;
   {
     const int64_t tiles = (out_stride + lg::kTileKeys - 1) / lg::kTileKeys;
-    const int64_t total = (int64_t)num_seqs * cache->num_kv_heads * tiles;
-    a.iters = (int)std::min<int64_t>(lg::kMaxIters, std::max<int64_t>(
+    // 32-pair chunks of the average request (the kernel reads the actual rows from
+    // cu_rows; a request with more chunks than this loops over them)
+    const int64_t G = num_q_heads / cache->num_kv_heads;
+    pairs = (total_rows + num_seqs - 1) / num_seqs * G;
+    const int64_t chunks = (pairs + 31) / 32;
+    a.cgroups = (int)chunks;
+    // tiles per workgroup for about kTargetGroups workgroups, then spread evenly
+    const int64_t total = (int64_t)num_seqs * cache->num_kv_heads * tiles * a.cgroups;
+    const int64_t iters = std::min<int64_t>(lg::kMaxIters, std::max<int64_t>(
         1, (total + lg::kTargetGroups - 1) / lg::kTargetGroups));
-    a.groups = (int)((tiles + a.iters - 1) / a.iters);
+    a.groups = (int)((tiles + iters - 1) / iters);
+    a.iters = (int)((tiles + a.groups - 1) / a.groups);
   }
   a.q_scale = 1.0f;
   a.k_scale = 1.0f;
@@ -383,13 +470,19 @@ extern "C" kvq_status kvq_paged_logits(const kvq_cache_desc* cache, const void* 
     const int64_t span = (31 / G + 2) * (int64_t)num_q_heads * out_stride * 4;
     a.span_bytes = span < 0x7FF00000 ? (int32_t)span : 0;
   }
-  const int64_t blocks = (int64_t)num_seqs * cache->num_kv_heads * a.groups;
+  // store form: plain where a chunk's rows span 2 GB or more; buffer stores otherwise,
+  // through the lane-quad transpose where chunks hold more than 8 pairs (it costs VALU
+  // work per tile, which only pays where a store instruction would otherwise touch
+  // more than 8 rows: indexer shape with one row per request 17.6 us plain buffer
+  // stores, 19.4 us transposed; 8,192 rows 404 -> 243 us)
+  const int store = a.span_bytes == 0 ? 0 : pairs > 8 ? 2 : 1;
+  const int64_t blocks = (int64_t)num_seqs * cache->num_kv_heads * a.groups * a.cgroups;
   if (blocks > 0x7FFFFFFF) return fail(KVQ_ERR_INVALID_ARG, "grid too large");
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (cache->head_dim) {
-    case 64: lg::launch_dtype<64>(cache, a, (unsigned)blocks, st); break;
-    case 128: lg::launch_dtype<128>(cache, a, (unsigned)blocks, st); break;
-    case 256: lg::launch_dtype<256>(cache, a, (unsigned)blocks, st); break;
+    case 64: lg::launch_dtype<64>(cache, store, a, (unsigned)blocks, st); break;
+    case 128: lg::launch_dtype<128>(cache, store, a, (unsigned)blocks, st); break;
+    case 256: lg::launch_dtype<256>(cache, store, a, (unsigned)blocks, st); break;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "logits launch: %s", hipGetErrorString(e));

@@ -398,18 +398,21 @@ kvq_status kvq_prefill_attention_accum(const kvq_cache_desc* cache, const void* 
  * float32 (e4m3 and bf16 values widened for the matrix cores); no softmax scale and
  * no reduction over heads (the selection rule is the caller's).
  * q [device] bf16 [total_rows][num_q_heads][D], 16-byte aligned; cu_rows [device]
- * int32 [num_seqs+1]; row_lens [device] int32 [total_rows]; seq_lens [device] int32
- * [num_seqs]; out [device] float32 [total_rows][num_q_heads][out_stride], 16-byte
- * aligned, out_stride a multiple of 4; every entry is written.  Only the K pool (and
- * K scales) of the cache is read.  Errors: INVALID_ARG for NULL pointers, misaligned
- * q/out (16 bytes) or per-token-head k_scales (16 bytes), out_stride not a multiple of
- * 4, Hq not a multiple of Hkv; HIP for a failed launch.  Supported: fp8 or bf16 cache,
- * D in {64,128,256}, any group size.
+ * int32 [num_seqs+1]; total_rows = cu_rows[num_seqs] (a host value that sizes the
+ * launch: the kernel takes the rows themselves from cu_rows, and 0 writes nothing);
+ * row_lens [device] int32 [total_rows]; seq_lens [device] int32 [num_seqs]; out
+ * [device] float32 [total_rows][num_q_heads][out_stride], 16-byte aligned, out_stride
+ * a multiple of 4; every entry is written.  Only the K pool (and K scales) of the cache
+ * is read.  Errors: INVALID_ARG for NULL pointers, a negative count, misaligned q/out
+ * (16 bytes) or per-token-head k_scales (16 bytes), out_stride not a multiple of 4, Hq
+ * not a multiple of Hkv, a grid past 2^31 - 1 workgroups; HIP for a failed launch.
+ * Supported: fp8 or bf16 cache, D in {64,128,256}, any group size.
  */
 kvq_status kvq_paged_logits(const kvq_cache_desc* cache, const void* q, const int32_t* cu_rows,
-                            int32_t num_seqs, int32_t num_q_heads, const int32_t* row_lens,
-                            const int32_t* block_table, int32_t block_table_stride,
-                            const int32_t* seq_lens, const kvq_scales* scales, float* out,
+                            int32_t num_seqs, int32_t total_rows, int32_t num_q_heads,
+                            const int32_t* row_lens, const int32_t* block_table,
+                            int32_t block_table_stride, const int32_t* seq_lens,
+                            const kvq_scales* scales, float* out,
                             int32_t out_stride, void* stream);
 
 #ifdef __cplusplus

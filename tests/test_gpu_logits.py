@@ -99,6 +99,20 @@ def test_logits_q_scale_and_many_rows(kvq):
     run_case(kvq, case, "fp8", "per_token_head", q_scale=0.5)
 
 
+def test_logits_chunk_sets(kvq):
+    """Requests averaging more than 32 (row, head) pairs per key head: the launch also
+    splits over 32-pair chunks (7 chunk sets here), a request with more chunks loops over
+    them (600 pairs), one has a single chunk and one none; stores through the lane-quad
+    transpose.  FP8 with per-token-head scales and a bf16 cache."""
+    case = workloads.make_logits_case(741, [900, 40, 17, 300], [150, 3, 0, 61], 8, 2, 128,
+                                      table="perm")
+    log("logits chunk sets fp8, 214 rows")
+    run_case(kvq, case, "fp8", "per_token_head", q_scale=0.25)
+    case = workloads.make_logits_case(742, [130, 517], [100, 37], 4, 1, 64, table="perm")
+    log("logits chunk sets bf16, 137 rows")
+    run_case(kvq, case, "bf16", "per_token_head")
+
+
 def test_logits_edges(kvq):
     """Empty requests, rows with no visible key, and an output narrower than the cache
     (keys past out_len are not written) or wider (all -inf past the visible keys)."""
