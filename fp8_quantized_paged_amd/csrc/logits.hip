@@ -11,11 +11,12 @@
 // result is scaled by q_scale * k_scale_j.  bf16 cache: q and k as bf16 on
 // v_mfma_f32_32x32x16_bf16 (exact products, float32 sums), unscaled.
 //
-// Work split.  A workgroup owns one (request, KV head) and `iters` consecutive 128-key
-// tiles (1 to 12, chosen so that the launch has about two workgroups per CU), each of
-// its 4 waves 32 keys of a tile (one 32-key MFMA block); the request's
-// query rows times the group's query heads ("pairs") are the MFMA columns, 32 at a
-// time, staged once per chunk in LDS.  The tiles are software-pipelined: a wave loads
+// Work split.  A workgroup owns one (request, KV head), one set of the request's 32-pair
+// chunks (all of them unless the requests average more than 32 pairs) and `iters`
+// consecutive 128-key tiles (1 to 12, chosen so that the launch has about two
+// workgroups per CU), each of its 4 waves 32 keys of a tile (one 32-key MFMA block);
+// the request's query rows times the group's query heads ("pairs") are the other MFMA
+// operand, 32 at a time, staged once per chunk in LDS.  The tiles are software-pipelined: a wave loads
 // all its page ids at once, then keeps two tiles' key rows in flight (a three-buffer
 // register ring) while one is computed, so the block-table -> key -> store chain of
 // dependent memory round trips is paid once per workgroup rather than once per tile.
@@ -96,7 +97,8 @@ __device__ __forceinline__ half8_t codes_to_f16(uint32_t lo, uint32_t hi) {
 // kMode: 0 per-tensor, 1 per-token-head, 2 per-KV-head (FP8 only)
 // Two waves per SIMD: a launch's workgroups (two per CU) stay resident at once.  (A
 // three-wave budget spilled the ring at head_dim 128.)
-// kSt: 0 plain stores, 1 buffer stores, 2 buffer stores after a transpose in lane quads
+// kSt: 0 plain stores, 1 buffer stores, 2 buffer stores after a transpose in lane quads,
+// 3 swapped operands with one dword store per pair row (group size a power of two)
 template <int D, bool kFp8, int kMode, int kSt>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 logits_kernel(const LogitsArgs a) {
@@ -243,8 +245,39 @@ logits_kernel(const LogitsArgs a) {
           rel_q[t] = (int)(((int64_t)(r0 + pq / G) * a.num_q_heads + g * G + pq % G) *
                                a.out_stride - base_f);
     }
+    // kSt 3: the MFMA computes S = Q . K^T (query rows as the A operand), so register
+    // 4 q4 + e of lane (col, hg) holds pair 8 q4 + 4 hg + e against key kw + col, and
+    // a dword store of one register writes 128 contiguous bytes of each of two pair
+    // rows.  With G a power of two (and p0 a multiple of 32), a pair's row offset from
+    // base_f splits over the disjoint bit fields of 8 q4 + e and 4 hg:
+    // rel(i) = ((i / G) Hq + i % G) out_stride is the per-lane rel(4 hg) plus a
+    // per-register constant rel(8 q4 + e) (wave-uniform).  Pairs past the request's
+    // last are dropped by the buffer's record count, which ends with the last valid
+    // pair's row (rows grow with the pair index).
+    const int lgG = __builtin_ctz((unsigned)G);
+    auto rel_of = [&](int i) {
+      return ((i >> lgG) * a.num_q_heads + (i & (G - 1))) * a.out_stride;
+    };
+    int vis_r[kSt == 3 ? 16 : 1];
+    int minvis = 0, maxvis = 0;  // over the chunk's pairs (wave-uniform)
+    int lane_rel = 0;            // rel(4 hg) + col
+    uint32_t span = kBuf ? (uint32_t)a.span_bytes : 0u;
+    if constexpr (kSt == 3) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) vis_r[r] = __shfl(vis, 8 * (r / 4) + 4 * hg + r % 4);
+      int mn = pair_ok ? vis : 0x7FFFFFFF, mx = pair_ok ? vis : 0;
+#pragma unroll
+      for (int m = 1; m < 32; m <<= 1) {
+        mn = min(mn, __shfl_xor(mn, m));
+        mx = max(mx, __shfl_xor(mx, m));
+      }
+      minvis = __builtin_amdgcn_readfirstlane(mn);
+      maxvis = __builtin_amdgcn_readfirstlane(mx);
+      lane_rel = rel_of(4 * hg) + col;
+      span = 4u * (uint32_t)(rel_of(min(32, npairs - p0) - 1) + a.out_stride);
+    }
     const __amdgpu_buffer_rsrc_t orsrc =  // gfx9 word 3: 32-bit raw buffer
-        __builtin_amdgcn_make_buffer_rsrc(a.out + base_f, 0, kBuf ? a.span_bytes : 0, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(a.out + base_f, 0, (int)span, 0x00020000);
     __syncthreads();
     // B operand of this lane (pair col): its half row, kept for all tiles
     const uint8_t* qrow = q_lds + col * QS + HB * hg;
@@ -265,6 +298,44 @@ logits_kernel(const LogitsArgs a) {
     auto compute_store = [&](int it, const Tile& t) {
       const int kw = key_base + it * kTileKeys;
       v16f acc = (v16f){};
+      if constexpr (kSt == 3) {
+        // tiles no pair of the chunk sees skip the matrix work (acc 0, all -inf below);
+        // tiles every pair sees in full skip the mask (both tests wave-uniform, and only
+        // arithmetic sits under them: every store is issued)
+        if (kw < maxvis) {
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            if constexpr (kFp8) {
+              const uint4 kv = t.k[s / 2];
+              const half8_t ka = (s & 1) ? codes_to_f16(kv.z, kv.w) : codes_to_f16(kv.x, kv.y);
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf[s], ka, acc, 0, 0, 0);
+            } else {
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  qbf[s], __builtin_bit_cast(bf16x8_t, t.k[s]), acc, 0, 0, 0);
+            }
+          }
+        }
+        float sck = 1.0f;
+        if constexpr (kFp8) sck = (kMode == 1 ? t.sc : k_scale_h) * a.q_scale;
+        const int key = kw + col;
+        float v[16];
+        if (kw + 32 <= minvis) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = acc[r] * sck;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = key < vis_r[r] ? acc[r] * sck : -INFINITY;
+        }
+        // keys at or past out_stride: an offset past the record count (no wrap: the
+        // per-register part stays below 0x7FF00000)
+        const uint32_t voff = key < a.out_stride ? 4u * (uint32_t)(lane_rel + kw) : 0x7FFFFFF0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t off = voff + 4u * (uint32_t)rel_of(8 * (r / 4) + r % 4);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[r]), orsrc, (int)off, 0, 0);
+        }
+        return;
+      }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         if constexpr (kFp8) {
@@ -380,7 +451,8 @@ static void launch_mode_b(int mode, const LogitsArgs& args, unsigned blocks, hip
 template <int D, bool kFp8>
 static void launch_mode(int mode, int store, const LogitsArgs& args, unsigned blocks,
                         hipStream_t st) {
-  if (store == 2) launch_mode_b<D, kFp8, 2>(mode, args, blocks, st);
+  if (store == 3) launch_mode_b<D, kFp8, 3>(mode, args, blocks, st);
+  else if (store == 2) launch_mode_b<D, kFp8, 2>(mode, args, blocks, st);
   else if (store == 1) launch_mode_b<D, kFp8, 1>(mode, args, blocks, st);
   else launch_mode_b<D, kFp8, 0>(mode, args, blocks, st);
 }
@@ -470,12 +542,17 @@ extern "C" kvq_status kvq_paged_logits(const kvq_cache_desc* cache, const void* 
     const int64_t span = (31 / G + 2) * (int64_t)num_q_heads * out_stride * 4;
     a.span_bytes = span < 0x7FF00000 ? (int32_t)span : 0;
   }
-  // store form: plain where a chunk's rows span 2 GB or more; buffer stores otherwise,
-  // through the lane-quad transpose where chunks hold more than 8 pairs (it costs VALU
-  // work per tile, which only pays where a store instruction would otherwise touch
-  // more than 8 rows: indexer shape with one row per request 17.6 us plain buffer
-  // stores, 19.4 us transposed; 8,192 rows 404 -> 243 us)
-  const int store = a.span_bytes == 0 ? 0 : pairs > 8 ? 2 : 1;
+  // store form: plain where a chunk's rows span 2 GB or more; else buffer stores, for
+  // chunks of more than 8 pairs written row-contiguously: a store of the plain layout
+  // touches 32 rows at 32 bytes each (8,192 rows x 8,192 keys, 4 heads: 404 us), the
+  // lane-quad transpose makes it 8 rows at 128 bytes (243 us) and the swapped operands
+  // 2 rows at 128 bytes with a fifth of the VALU work per tile (same in short bursts;
+  // in 60-launch bursts 213-215 against 240-243 us, which clock down under the
+  // heavier form).  The swapped form needs a power-of-two group; with 8 pairs or
+  // fewer (one row per request, group 4) the plain layout stays (17.6 us against
+  // 19.4 us transposed: most of the tile's lanes have no pair).
+  const int64_t Gq = num_q_heads / cache->num_kv_heads;
+  const int store = a.span_bytes == 0 ? 0 : pairs <= 8 ? 1 : (Gq & (Gq - 1)) == 0 ? 3 : 2;
   const int64_t blocks = (int64_t)num_seqs * cache->num_kv_heads * a.groups * a.cgroups;
   if (blocks > 0x7FFFFFFF) return fail(KVQ_ERR_INVALID_ARG, "grid too large");
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -113,6 +113,20 @@ def test_logits_chunk_sets(kvq):
     run_case(kvq, case, "bf16", "per_token_head")
 
 
+@pytest.mark.parametrize("Hq,Hkv,rows,mode", [
+    (6, 2, [50, 7], "per_tensor"),        # group 3: lane-quad transposed stores
+    (32, 2, [5, 3], "per_kv_head"),       # group 16: swapped operands, 5 chunks per row
+    (64, 1, [1, 2, 1], "per_token_head"), # group 64: a chunk is 32 heads of one row
+])
+def test_logits_store_forms(kvq, Hq, Hkv, rows, mode):
+    """Every store form the launch picks for requests of more than 8 pairs: a group
+    size that is not a power of two, and power-of-two groups below and above 32."""
+    case = workloads.make_logits_case(750 + Hq, [300, 45, 1000][:len(rows)], rows, Hq, Hkv,
+                                      128, table="perm")
+    log(f"logits store forms Hq={Hq} Hkv={Hkv} rows={rows} {mode}")
+    run_case(kvq, case, "fp8", mode, k_scale=0.05 if mode == "per_tensor" else 1.0)
+
+
 def test_logits_edges(kvq):
     """Empty requests, rows with no visible key, and an output narrower than the cache
     (keys past out_len are not written) or wider (all -inf past the visible keys)."""
