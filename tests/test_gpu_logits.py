@@ -195,3 +195,32 @@ def test_logits_sampled_at_full_size(kvq):
         err = np.abs(got[b:b + 1] - want)
         assert (err <= REL * mag + 1e-30).all(), f"request {b}: worst {err.max():.3e}"
     log("logits full size sampled")
+
+
+def test_logits_many_rows_sampled_at_full_size(kvq):
+    """The bench's many-rows workload (one request of 8,192 causal query rows over its
+    8,192 cached tokens, 4 query heads on one key head, D 128; 1 GiB of logits, the
+    swapped-operand store form over 6,144 workgroups): every logit of 10 sampled rows,
+    chosen across chunk boundaries (8 rows per 32-pair chunk) and the request's ends."""
+    R = L = 8192
+    case = workloads.make_logits_case(761, [L], [R], 4, 1, 128, table="perm")
+    c = write_cache(kvq, case, "fp8", "per_token_head")
+    out = kvq.paged_logits(c, dev_bf16(case.q), dev(case.cu_rows), dev(case.row_lens),
+                           dev(case.block_table), dev(case.seq_lens), L,
+                           kvq.Scales(1.0, 1.0, 1.0, 1.0))
+    rows = np.array([0, 1, 7, 8, 255, 256, 4095, 4100, 8190, 8191])
+    got = out[torch.from_numpy(rows).to(out.device)].cpu().numpy().astype(np.float64)
+    del out
+    _, qh = ocache.quantize_q(case.q[rows], 1.0)
+    pools = ocache.new_pools(case.num_pages, 1, 128)
+    ocache.cache_write(pools, case.k, case.v, case.slots, "per_token_head")
+    kp = ocache.dequantized(pools, "k")
+    cu = np.array([0, len(rows)])
+    want = ologits.paged_logits(qh, cu, case.row_lens[rows], kp, case.block_table, L)
+    mag = ologits.paged_logits(np.abs(qh), cu, case.row_lens[rows], np.abs(kp),
+                               case.block_table, L)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isneginf(got), ~fin), "-inf pattern differs"
+    err = np.abs(got[fin] - want[fin])
+    assert (err <= REL * mag[fin] + 1e-30).all(), f"worst {err.max():.3e}"
+    log("logits many rows full size sampled")
