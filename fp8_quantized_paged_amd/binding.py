@@ -132,6 +132,10 @@ _SIGS = {
     "kvq_prefill_attention_accum": (ctypes.c_int, [_PD, _p, _p, _i32, _i32, _p, _i32, _p,
                                                    _i32, ctypes.POINTER(Scales), _i32, _i32,
                                                    _f32, _p, ctypes.c_int, ctypes.c_int, _p]),
+    "kvq_prefill_workspace_bytes": (ctypes.c_size_t, [_PD, _i32, _i32, _i32]),
+    "kvq_prefill_attention_ws": (ctypes.c_int, [_PD, _p, _p, _i32, _i32, _p, _i32, _p, _i32,
+                                                ctypes.POINTER(Scales), _i32, _i32, _f32, _p,
+                                                ctypes.c_int, _p, ctypes.c_size_t, _p]),
     "kvq_paged_logits": (ctypes.c_int, [_PD, _p, _p, _i32, _i32, _i32, _p, _p, _i32, _p,
                                         ctypes.POINTER(Scales), _p, _i32, _p]),
 }
@@ -375,11 +379,13 @@ def prefill_attention(cache: PagedCache, q, cu_q_lens, block_table, seq_lens,
                       max_q_len: int, scales: Scales | None = None, causal: bool = True,
                       window: int = 0, softmax_scale: float = 0.0, out=None,
                       out_dtype: str = "bf16", accumulation: str | None = None,
-                      stream=None):
+                      split: bool = True, workspace=None, stream=None):
     """q bf16 [Nq][Hq][D]; cu_q_lens int32 [B+1]; seq_lens int32 [B] (incl. new).
 
-    accumulation: None (kvq_prefill_attention) or "mfma_chain" / "valu_add"
-    (kvq_prefill_attention_accum with that level-2 form)."""
+    accumulation: None (kvq_prefill_attention, or kvq_prefill_attention_ws with keys
+    split over workgroups where the library asks for a workspace and `split` is set;
+    `workspace`: a device uint8 tensor to use for it instead of a new one) or
+    "mfma_chain" / "valu_add" (kvq_prefill_attention_accum with that level-2 form)."""
     torch = _torch()
     Nq, Hq, D = q.shape
     if scales is None:
@@ -393,8 +399,19 @@ def prefill_attention(cache: PagedCache, q, cu_q_lens, block_table, seq_lens,
             ctypes.byref(scales), int(causal), window, softmax_scale, _ptr(out),
             _DTYPES[out_dtype])
     if accumulation is None:
-        _check(_lib.kvq_prefill_attention(*args, _stream(stream, q.device)),
-               "prefill_attention")
+        # short query chunks on long contexts: keys split over workgroups through a
+        # workspace (kvq_prefill_attention_ws) where the library asks for one
+        nb = _lib.kvq_prefill_workspace_bytes(ctypes.byref(d), int(seq_lens.numel()), Hq,
+                                              max_q_len) if split else 0
+        if nb:
+            ws = (torch.empty(nb, dtype=torch.uint8, device=q.device) if workspace is None
+                  else workspace)
+            _check(_lib.kvq_prefill_attention_ws(*args, _ptr(ws), ws.numel(),
+                                                 _stream(stream, q.device)),
+                   "prefill_attention_ws")
+        else:
+            _check(_lib.kvq_prefill_attention(*args, _stream(stream, q.device)),
+                   "prefill_attention")
     else:
         _check(_lib.kvq_prefill_attention_accum(*args, ACCUMULATIONS[accumulation],
                                                 _stream(stream, q.device)),

@@ -206,6 +206,13 @@ struct PrefillArgs {
   int32_t causal, window;
   void* out;
   int32_t out_f32;
+  // Key splits (1: none).  With more, workgroup (x, split y) covers its share
+  // [y T / nsplit, (y + 1) T / nsplit) of its sequence's T key tiles and writes the
+  // unnormalised partial result of each of its kWgRows rows to the workspace (row
+  // index (y gridDim.x + x) kWgRows + row); prefill_merge_kernel combines them.
+  int32_t nsplit;
+  float* ws_o;   // per row: O v_ref s, D floats (s = prob_scale per-token-head, else 1)
+  float* ws_ml;  // per row: reference maximum m (log2 units) and row sum, two floats
 };
 
 template <typename T>
@@ -271,8 +278,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // keys the workgroup needs
   const int wg_hi = a.causal ? ctx + pend - 1 : L - 1;
   const int wg_lo = a.window > 0 ? max(0, ctx + p0 - a.window + 1) : 0;
-  const int t_first = wg_lo / kTile;
-  const int t_last = wg_hi / kTile;
+  int t_first = wg_lo / kTile;
+  int t_last = wg_hi / kTile;
+  // this row's partial result in a split launch (computed where used: kept live through
+  // the main loop it cost registers)
+  auto ws_row = [&]() {
+    return ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kWgRows + wg_row;
+  };
+  if (a.nsplit > 1) {
+    const int T = (L + kTile - 1) / kTile;
+    t_first = max(t_first, (int)((int64_t)blockIdx.y * T / a.nsplit));
+    t_last = min(t_last, (int)((int64_t)(blockIdx.y + 1) * T / a.nsplit) - 1);
+    if (t_first > t_last) {  // none of the workgroup's keys in this split (uniform)
+      if (grp == 0)
+        *reinterpret_cast<float2*>(a.ws_ml + 2 * ws_row()) = make_float2(-INFINITY, 0.0f);
+      return;
+    }
+  }
   const int npages = (L + kPage - 1) / kPage;
   const int* bt = a.block_table + (int64_t)b * a.bt_stride;
   // per-wave bounds for the mask decision
@@ -898,6 +920,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // sum_j p_j: out = O * v_ref * prob_scale / lam; per-tensor: P'_j ~ p_j / prob_scale
   // and lam ~ sum_j P'_j, out = O * v_scale / lam
   const float lsum = sum_xor<kRows>(lam);
+  if (a.nsplit > 1) {  // partial result: O and the row sum, both relative to 2^m
+    const float f = vref * (kPTH ? a.prob_scale : 1.0f);
+    const int64_t wr = ws_row();
+    float* wo = a.ws_o + wr * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(wo + 32 * db + 8 * r4 + 4 * grp) =
+            make_float4(o[db][4 * r4] * f, o[db][4 * r4 + 1] * f, o[db][4 * r4 + 2] * f,
+                        o[db][4 * r4 + 3] * f);
+    if (grp == 0) *reinterpret_cast<float2*>(a.ws_ml + 2 * wr) = make_float2(m, lsum);
+    return;
+  }
   const float inv = lsum > 0.0f ? vref * (kPTH ? a.prob_scale : 1.0f) / lsum : 0.0f;
   if (row_ok) {
     const int64_t orow = ((int64_t)(q0 + p_loc) * Hq + g * G + hh) * D;
@@ -924,12 +960,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 // (prefill_d64.hip, prefill_d128.hip, prefill_d256.hip) so they compile in parallel.
 template <int D>
 void launch_prefill_fp8(int G, bool per_token_head, bool valu_add, const PrefillArgs& args,
-                        unsigned blocks, hipStream_t st);
+                        dim3 grid, hipStream_t st);
 
 #define KVQ_DEFINE_PREFILL_LAUNCH(D)                                                   \
   template <>                                                                          \
   void launch_prefill_fp8<D>(int G, bool pth, bool valu, const PrefillArgs& args,      \
-                             unsigned blocks, hipStream_t st) {                        \
+                             dim3 blocks, hipStream_t st) {                            \
     auto go = [&](auto g_tag) {                                                        \
       constexpr int GG = decltype(g_tag)::value;                                       \
       if (pth && valu) prefill_kernel<D, GG, true, true><<<blocks, kThreads, 0, st>>>(args);   \

@@ -382,6 +382,40 @@ kvq_status kvq_prefill_attention_accum(const kvq_cache_desc* cache, const void* 
                                        kvq_accumulation accum, void* stream);
 
 /*
+ * Workspace for kvq_prefill_attention_ws: 0 where the launch needs no key split (it
+ * already has about 1.5 workgroups per CU: roughly num_seqs * num_kv_heads *
+ * ceil(max_q_len * G / 128) >= 384, G = num_q_heads / num_kv_heads) and for bf16
+ * caches or unsupported shapes; else the bytes of the split's partial results
+ * (splits * workgroups * 128 rows * (head_dim + 2) * 4).  Depends only on these
+ * arguments.
+ */
+size_t kvq_prefill_workspace_bytes(const kvq_cache_desc* cache, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_q_len);
+
+/*
+ * kvq_prefill_attention for short query chunks on long contexts: the same result
+ * (same arguments, layouts and errors), computed with each workgroup's keys split over
+ * up to 64 workgroups.  Each split writes unnormalised partial results (O, reference
+ * maximum, row sum) to `workspace` [device], and a second kernel on the same stream
+ * combines them through their maxima and sums, as the prefill combines its key tiles
+ * ("vLLM FP8 KV-Cache and Attention Quantization Update", section "Two-level
+ * accumulation").  Used
+ * where kvq_prefill_workspace_bytes is non-zero: 16 new tokens on 131,072 cached
+ * tokens otherwise run on 8 workgroups.  workspace_bytes must be at least that value
+ * (else INVALID_ARG), workspace 16-byte aligned; with a null workspace the call is
+ * kvq_prefill_attention.  A bf16 cache ignores the workspace.  The workspace is
+ * scratch owned by the caller; calls that share one must not overlap.
+ */
+kvq_status kvq_prefill_attention_ws(const kvq_cache_desc* cache, const void* q,
+                                    const int32_t* cu_q_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, const int32_t* block_table,
+                                    int32_t block_table_stride, const int32_t* seq_lens,
+                                    int32_t max_q_len, const kvq_scales* scales,
+                                    int32_t causal, int32_t window, float softmax_scale,
+                                    void* out, kvq_dtype out_dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * Paged query-key logits for a sparse-attention indexer ("vLLM Qwen3.8-Flash-Next: QSA
  * Indexer ... FP8 support", section on the reference test of the decode/prefill
  * selection: the indexer's top-k selection reads these scores from an FP8 or bf16

@@ -17,6 +17,8 @@ those per-key bounds into the largest move of the renormalised mean (attend_rows
 weight_error), which the tests add to the plain 5e-3 + 2e-2 |O| bar.  The full-size
 head_dim-256 workload and the 131,072-key stress test are held to the plain bar.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -76,13 +78,14 @@ def assert_close_with_p_rounding(got, want, bound, what=""):
 
 
 def run_prefill(kvq, c, case, q_scale=1.0, k_scale=1.0, v_scale=1.0, prob_scale=1.0,
-                causal=True, window=0, out_dtype="f32", accumulation=None):
+                causal=True, window=0, out_dtype="f32", accumulation=None, split=True):
     sc = kvq.Scales(q_scale, k_scale, v_scale, prob_scale)
     q_lens = np.diff(case.cu_q_lens)
     out = kvq.prefill_attention(c, dev_bf16(case.q), dev(case.cu_q_lens),
                                 dev(case.block_table), dev(case.seq_lens),
                                 int(q_lens.max()), sc, causal=causal, window=window,
-                                out_dtype=out_dtype, accumulation=accumulation)
+                                out_dtype=out_dtype, accumulation=accumulation,
+                                split=split)
     return out.float().cpu().numpy()
 
 
@@ -285,3 +288,43 @@ def test_prefill_bf16_cache(kvq, D, Hq, Hkv, window):
     err = np.abs(got - want)
     bound = ATOL + RTOL * np.abs(want) + P_ROUND_BF16 * spread
     assert (err <= bound).all(), f"max excess {np.max(err - bound):.3g}"
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 16, 1), (256, 8, 4)])
+@pytest.mark.parametrize("mode", ["per_token_head", "per_tensor"])
+def test_prefill_key_splits(kvq, D, Hq, Hkv, mode):
+    """Short query chunks on a long context: the launch splits each workgroup's keys
+    (16 new tokens on 20,000 cached beside 3 on 5: 32-64 splits, most of them empty for
+    the short sequence) and merges the partial results; the same call without the
+    split, both against the oracle, f32 and bf16 output."""
+    case = workloads.make_prefill_case(900 + D + Hq, [20000, 5], [16, 3], Hq, Hkv, D,
+                                       table="perm")
+    ks, vs = (1.0, 1.0) if mode == "per_token_head" else (0.5, 0.25)
+    c = write_cache(kvq, case, "fp8", mode, ks, vs)
+    want, bound = oracle_prefill(case, mode, k_scale=ks, v_scale=vs, p_bound=True)
+    nb = kvq.binding._lib.kvq_prefill_workspace_bytes(ctypes.byref(c.desc()), 2, Hq, 16)
+    assert nb > 0, "this shape should split"
+    for split in (True, False):
+        log(f"prefill key splits D={D} Hq={Hq} Hkv={Hkv} {mode} split={split}")
+        got = run_prefill(kvq, c, case, k_scale=ks, v_scale=vs, split=split)
+        assert_close_with_p_rounding(got, want, bound, f"split={split} D={D} {mode}")
+    gotb = run_prefill(kvq, c, case, k_scale=ks, v_scale=vs, out_dtype="bf16")
+    assert_close_with_p_rounding(gotb, want, bound, f"split D={D} {mode} bf16 out")
+
+
+def test_prefill_key_splits_window_and_workspace(kvq):
+    """A sliding window with key splits (most splits hold none of a row's keys), and a
+    workspace one byte short of what the library asks for: INVALID_ARG, nothing run."""
+    case = workloads.make_prefill_case(931, [12000], [40], 32, 8, 128, table="perm")
+    c = write_cache(kvq, case, "fp8", "per_token_head")
+    log("prefill key splits, window 100")
+    got = run_prefill(kvq, c, case, window=100)
+    want, bound = oracle_prefill(case, "per_token_head", window=100, p_bound=True)
+    assert_close_with_p_rounding(got, want, bound, "split window 100")
+    nb = kvq.binding._lib.kvq_prefill_workspace_bytes(ctypes.byref(c.desc()), 1, 32, 40)
+    assert nb > 0
+    short = torch.empty(nb - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(Exception, match="workspace"):
+        kvq.prefill_attention(c, dev_bf16(case.q), dev(case.cu_q_lens),
+                              dev(case.block_table), dev(case.seq_lens), 40,
+                              kvq.Scales(1.0, 1.0, 1.0, 1.0), workspace=short)
