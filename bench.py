@@ -45,7 +45,7 @@ SETTLE_S = 0.1               # untimed steps after the warmup, before each timed
 LEGS = ("decode", "bf16", "tiny", "long", "hybrid", "prefill", "cache_write", "itl")
 ITL_CONTEXTS = (4096, 32768, 131072)   # the default line's compact sweep
 EXTRA_LEGS = ("prefill_d128", "prefill_d64", "per_kv_head", "prefill_bf16_window",
-              "paged_logits")
+              "paged_logits", "prefill_split")
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix throughput, AMD published
 
 
@@ -1018,6 +1018,56 @@ def main():
             "fill_1GB_GB_s": round(R4 * 4 * L4 * 4 / (usf * 1e-6) / 1e9, 1),
             "frac_of_fill": round(usf / us4, 4)}
         del c4, pout
+        torch.cuda.empty_cache()
+
+    if "prefill_split" in legs:
+        # short query chunks on a long context (keys split over workgroups, then merged):
+        # one sequence of 131,072 cached tokens, Llama-shaped heads (32/8, D 128),
+        # fp8 per-token-head; 16 and 256 new tokens, split and unsplit
+        Ls = 131072
+        npg = Ls // 16
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(41)
+        bts = torch.randperm(npg, device=dev, generator=gen).to(torch.int32).reshape(1, -1)
+        cs_ = kvq.PagedCache(npg, 8, 128, "fp8", "per_token_head")
+        pos = torch.arange(Ls, device=dev)
+        sl_all = bts[0][pos // 16].to(torch.int64) * 16 + pos % 16
+        for i in range(0, Ls, 65536):
+            kk = torch.randn(65536, 8, 128, device=dev, generator=gen).to(torch.bfloat16)
+            vv = torch.randn(65536, 8, 128, device=dev, generator=gen).to(torch.bfloat16)
+            kvq.cache_write(cs_, kk, vv, sl_all[i:i + 65536])
+        sls = torch.full((1,), Ls, device=dev, dtype=torch.int32)
+        res_s = {"workload": "1 sequence, 131,072 cached tokens (the new ones last), 32/8 "
+                             "heads, D 128, fp8 per-token-head, causal; keys split over "
+                             "workgroups and merged (kvq_prefill_attention_ws) against "
+                             "the unsplit kernel",
+                 "timing": "HIP events over back-to-back launches after 3 untimed"}
+        for n_new in (16, 256):
+            qs = torch.randn(n_new, 32, 128, device=dev, generator=gen).to(torch.bfloat16)
+            cus = torch.tensor([0, n_new], device=dev, dtype=torch.int32)
+            outs_ = torch.empty_like(qs)
+            row = {}
+            for split in (True, False):
+                def f():
+                    kvq.prefill_attention(cs_, qs, cus, bts, sls, n_new, ones, out=outs_,
+                                          split=split)
+                for _ in range(3):
+                    f()
+                torch.cuda.synchronize()
+                t0 = torch.cuda.Event(enable_timing=True)
+                t1 = torch.cuda.Event(enable_timing=True)
+                nrep = max(5, min(args.steps, 30))
+                t0.record()
+                for _ in range(nrep):
+                    f()
+                t1.record()
+                torch.cuda.synchronize()
+                row["us_split" if split else "us_unsplit"] = round(
+                    t0.elapsed_time(t1) * 1e3 / nrep, 1)
+            row["speedup"] = round(row["us_unsplit"] / row["us_split"], 2)
+            res_s[f"new_{n_new}"] = row
+        result["prefill_split"] = res_s
+        del cs_
         torch.cuda.empty_cache()
 
     if "cache_write" in legs:
