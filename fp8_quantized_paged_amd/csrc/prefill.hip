@@ -15,13 +15,17 @@ namespace kvq {
 namespace pf {
 
 // Key splits for a launch of `blocks` workgroups: none once the launch has about 1.5
-// workgroups per CU, else enough for ~768 workgroups, at most kMaxSplits.  A short
+// workgroups per CU, else enough for ~512 workgroups, at most kMaxSplits.  A short
 // query chunk on a long context otherwise runs on a handful of workgroups (16 new
-// tokens at group 4 on 131,072 cached: 8 workgroups, 2.18 ms).
-constexpr int kMaxSplits = 64;
+// tokens at group 4 on 131,072 cached: 8 workgroups, 2.18 ms).  Fewer splits also mean
+// fewer partial results for the merge: round-robin A/B over four short-chunk shapes,
+// ~512 workgroups / at most 32 splits 4-12% faster than ~768 / 64 and ~1,024 / 64
+// (16 new on 131,072: 110.6 against 118.7 and 119.3 us; 8 x 16 on 32,768: 148 against
+// 168 and 175 us).
+constexpr int kMaxSplits = 32;
 static int plan_splits(int64_t blocks) {
   if (blocks >= 384) return 1;
-  return (int)std::min<int64_t>(kMaxSplits, (768 + blocks - 1) / blocks);
+  return (int)std::min<int64_t>(kMaxSplits, (512 + blocks - 1) / blocks);
 }
 static size_t split_ws_bytes(int nsplit, int64_t blocks, int D) {
   return nsplit <= 1 ? 0 : (size_t)nsplit * blocks * kWgRows * (D + 2) * sizeof(float);

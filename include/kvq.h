@@ -395,7 +395,7 @@ size_t kvq_prefill_workspace_bytes(const kvq_cache_desc* cache, int32_t num_seqs
 /*
  * kvq_prefill_attention for short query chunks on long contexts: the same result
  * (same arguments, layouts and errors), computed with each workgroup's keys split over
- * up to 64 workgroups.  Each split writes unnormalised partial results (O, reference
+ * up to 32 workgroups.  Each split writes unnormalised partial results (O, reference
  * maximum, row sum) to `workspace` [device], and a second kernel on the same stream
  * combines them through their maxima and sums, as the prefill combines its key tiles
  * ("vLLM FP8 KV-Cache and Attention Quantization Update", section "Two-level
